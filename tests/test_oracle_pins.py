@@ -1,0 +1,435 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test anchors one oracle function to something other than itself: a
+value the pages print, a closed form, a brute-force enumeration, an invariant
+or a library routine.  Page citations use the page titles listed in the
+oracle's header.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _rand_weights(rng, kind, E, d, d_ff, d_out, bias=False):
+    w = {}
+    n1 = d_out if kind == "linear" else d_ff
+    w["w1"] = rng.standard_normal((E, n1, d)) / math.sqrt(d)
+    if kind == "swiglu":
+        w["w3"] = rng.standard_normal((E, d_ff, d)) / math.sqrt(d)
+    if kind != "linear":
+        w["w2"] = rng.standard_normal((E, d_out, d_ff)) / math.sqrt(d_ff)
+    if bias:
+        w["b1"] = rng.standard_normal((E, n1)) * 0.3
+        if kind != "linear":
+            w["b2"] = rng.standard_normal((E, d_out)) * 0.3
+    return w
+
+
+# ---------------------------------------------------------------------------
+# P4 一个小算例: logits [1,2,3] -> gates ~[0.09,0.24,0.67], y ~ 25.8
+# ---------------------------------------------------------------------------
+
+def _page_example_layer():
+    ex = _load("p4_worked_example.json")
+    x = np.array([[1.0]])
+    w_g = np.array(ex["logits"]).reshape(3, 1)          # z = W_g x = [1,2,3]
+    weights = {"w1": np.zeros((3, 1, 1)),                # A_i = 0
+               "b1": np.array(ex["expert_outputs"]).reshape(3, 1)}  # b_i = 10,20,30
+    return ex, x, w_g, weights
+
+
+def test_worked_example_gates_match_page():
+    ex = _load("p4_worked_example.json")
+    p = O.softmax(np.array([ex["logits"]]))[0]
+    assert np.round(p, 2).tolist() == ex["gates_printed"]
+    assert round(float(p.sum()), 2) == ex["gate_sum_printed"]
+
+
+def test_worked_example_sparse_layer_matches_page():
+    ex, x, w_g, weights = _page_example_layer()
+    out = O.forward(x, w_g, None, k=3, gate_mode="renorm", C=-1, kind="linear", weights=weights)
+    y = float(out["y"][0, 0])
+    # the page multiplies two-decimal gates: 0.9 + 4.8 + 20.1 = 25.8
+    assert abs(y - ex["y_printed"]) < 0.05
+    assert np.round(out["topk_gate"][0][np.argsort(out["topk_idx"][0])], 2).tolist() == ex["gates_printed"]
+    # the page's own arithmetic on its rounded gates reproduces its printed terms
+    terms = np.array(ex["gates_printed"]) * np.array(ex["expert_outputs"])
+    assert np.allclose(terms, ex["weighted_terms_printed"])
+    assert abs(terms.sum() - ex["y_printed"]) < 1e-9
+
+
+def test_worked_example_dense_layer_matches_page():
+    ex, x, w_g, weights = _page_example_layer()
+    y = O.dense_moe(x, w_g, None, "linear", weights)
+    assert abs(float(y[0, 0]) - ex["y_printed"]) < 0.05
+    # the printed denominator is the sum of the two-decimal exp terms
+    assert abs(sum(ex["exp_terms_printed"]) - ex["denominator_printed"]) < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# gates
+# ---------------------------------------------------------------------------
+
+def test_renorm_gates_sum_to_one_and_equal_softmax_over_selected_logits():
+    """P1 §3.3 renormalises selected probabilities; P2 §2.1 / P3 §3.1 take a
+    softmax over the selected logits.  The two must agree (library softmax)."""
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((200, 7)) * 2
+    for k in (1, 2, 3, 7):
+        idx = O.topk_select(z, k)
+        g = O.gates(O.softmax(z), idx, "renorm")
+        sel = np.take_along_axis(z, idx.astype(np.int64), axis=1)
+        ref = scipy.special.softmax(sel, axis=1)
+        assert np.allclose(g, ref, rtol=1e-13, atol=1e-15)
+        assert np.allclose(g.sum(axis=1), 1.0, atol=1e-14)
+
+
+def test_prob_gate_top1_equals_probs_times_onehot_of_argmax():
+    """P5 代码实战: top-1 route weight = probs * one_hot(argmax(logits))."""
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((300, 8))
+    p = scipy.special.softmax(z, axis=1)
+    onehot = np.eye(8)[np.argmax(z, axis=1)]
+    ref = (p * onehot).sum(axis=1)
+    g = O.gates(O.softmax(z), O.topk_select(z, 1), "prob")[:, 0]
+    assert np.allclose(g, ref, rtol=1e-13)
+
+
+def test_softmax_matches_library_and_is_shift_invariant():
+    rng = np.random.default_rng(7)
+    z = rng.standard_normal((50, 9)) * 5
+    assert np.allclose(O.softmax(z), scipy.special.softmax(z, axis=1), rtol=1e-13)
+    assert np.allclose(O.softmax(z + 100.0), O.softmax(z), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# top-k: brute force over all expert subsets (P5 数学定义 counts C(N,K) subsets)
+# ---------------------------------------------------------------------------
+
+def test_topk_brute_force_over_all_subsets():
+    rng = np.random.default_rng(8)
+    combos = _load("p5_combinations.json")
+    assert len(list(itertools.combinations(range(16), 2))) == combos["n16_k2"]
+    assert abs(math.comb(64, 8) - combos["n64_k8_approx"]) / combos["n64_k8_approx"] < 0.01
+    for E in (3, 5, 8):
+        for k in range(1, E + 1):
+            z = rng.standard_normal((40, E))
+            idx = O.topk_select(z, k)
+            for t in range(z.shape[0]):
+                best = max(itertools.combinations(range(E), k), key=lambda s: sum(z[t, i] for i in s))
+                assert set(idx[t].tolist()) == set(best)
+                vals = z[t, idx[t]]
+                assert np.all(np.diff(vals) <= 0)          # largest first
+
+
+def test_topk_ties_pick_lower_index_first():
+    z = np.array([[1.0, 3.0, 3.0, 0.0], [2.0, 2.0, 2.0, 2.0], [0.0, -1.0, 5.0, 5.0]])
+    assert O.topk_select(z, 2).tolist() == [[1, 2], [0, 1], [2, 3]]
+    assert O.topk_select(z, 1).tolist() == [[1], [0], [2]]
+    assert O.near_tie_mask(z, 1).tolist() == [True, True, True]
+    z2 = np.array([[0.0, 1.0, 2.0, 3.0]])
+    assert O.near_tie_mask(z2, 2).tolist() == [False]
+    assert O.near_tie_mask(np.array([[0.0, 1.0, 1.0 + 5e-6, 3.0]]), 2).tolist() == [True]
+    assert O.near_tie_mask(np.array([[0.0, 1.0, 1.0 + 5e-6, 3.0]]), 1).tolist() == [False]
+
+
+def test_topk_rejects_k_out_of_range():
+    """P1 §3.3 warns about K larger than the number of experts."""
+    with pytest.raises(ValueError):
+        O.topk_select(np.zeros((2, 3)), 4)
+    with pytest.raises(ValueError):
+        O.topk_select(np.zeros((2, 3)), 0)
+
+
+# ---------------------------------------------------------------------------
+# capacity and dispatch
+# ---------------------------------------------------------------------------
+
+def test_capacity_page_example_and_workloads():
+    ex = _load("p1_capacity_example.json")
+    c = O.capacity(ex["tokens"], ex["k"], ex["experts"], ex["capacity_factor"], "floor")
+    assert c == ex["capacity_printed"]
+    assert O.capacity(1000, 1, 8, 1.25, "ceil") == 157
+    assert O.capacity(8192, 1, 8, 1.25) == 1280        # Switch-style workload
+    assert O.capacity(8192, 1, 8, 1.0) == 1024
+    assert O.capacity(32768, 8, 256, 1.0) == 1024      # stress workload
+    assert O.capacity(100, 2, 8, None) == -1
+    assert O.capacity(100, 2, 8, 0.0) == -1
+    # k scales the capacity: top-2 gets twice the slots of top-1 at equal factor
+    assert O.capacity(4096, 2, 8, 1.0) == 2 * O.capacity(4096, 1, 8, 1.0)
+
+
+def _dispatch_by_stable_sort(idx, E, C):
+    """Independent formulation: stable library sort of the token-major
+    assignment list by expert, truncated to C per expert."""
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    dest = np.full(T * k, -1, dtype=np.int64)
+    perm = []
+    pos = 0
+    start = 0
+    for e in range(E):
+        group = order[start:start + counts[e]]
+        start += counts[e]
+        keep = group if C < 0 else group[:C]
+        for i, a in enumerate(keep):
+            dest[a] = pos + i
+        perm.extend((keep // k).tolist())
+        pos += len(keep)
+    return counts, dest.reshape(T, k), np.array(perm, dtype=np.int64)
+
+
+@pytest.mark.parametrize("T,E,k,C", [(50, 4, 2, -1), (50, 4, 2, 10), (97, 8, 1, 9), (64, 5, 5, 30),
+                                     (33, 3, 2, 0), (120, 16, 4, 17), (1, 4, 2, 1), (0, 4, 2, 3)])
+def test_dispatch_matches_stable_sort_and_invariants(T, E, k, C):
+    rng = np.random.default_rng(T * 31 + E)
+    z = rng.standard_normal((T, E)) + np.linspace(0, 2, E)   # skewed loads
+    idx = O.topk_select(z, k) if T else np.zeros((0, k), dtype=np.int32)
+    d = O.dispatch(idx, E, C)
+    counts, dest, perm = _dispatch_by_stable_sort(idx, E, C)
+    assert d["counts_routed"].tolist() == counts.tolist()
+    assert d["dest_pos"].tolist() == dest.tolist()
+    assert d["perm_token"].tolist() == perm.tolist()
+    assert int(d["counts_routed"].sum()) == T * k
+    kept = d["counts_kept"]
+    if C >= 0:
+        assert np.all(kept <= C)
+    assert np.all(kept == (counts if C < 0 else np.minimum(counts, C)))
+    off = d["offsets"]
+    assert off[0] == 0 and np.all(np.diff(off) == kept)
+    for e in range(E):
+        seg = d["perm_token"][off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)                     # token order, stable
+    dropped = d["dest_pos"] < 0
+    if C >= 0:
+        assert np.all(d["rank"][dropped] >= C)
+        assert np.all(d["rank"][~dropped] < C)
+    else:
+        assert not dropped.any()
+
+
+def test_dispatch_large_capacity_equals_no_capacity():
+    rng = np.random.default_rng(9)
+    idx = O.topk_select(rng.standard_normal((80, 6)), 3)
+    a = O.dispatch(idx, 6, -1)
+    b = O.dispatch(idx, 6, 80 * 3)
+    for key in ("counts_routed", "counts_kept", "offsets", "dest_pos", "perm_token"):
+        assert a[key].tolist() == b[key].tolist()
+
+
+def test_dispatch_page_capacity_example_drops_the_later_tokens():
+    """P1 §4.2: 1000 tokens, 8 experts, factor 1.25 -> 156 slots.  200 tokens
+    sent to expert 0: the first 156 in token order stay, the last 44 drop."""
+    C = O.capacity(1000, 1, 8, 1.25, "floor")
+    idx = np.zeros((1000, 1), dtype=np.int32)
+    idx[200:, 0] = 1 + (np.arange(800) % 7)
+    d = O.dispatch(idx, 8, C)
+    assert d["counts_routed"][0] == 200 and d["counts_kept"][0] == 156
+    assert np.all(d["dest_pos"][:156, 0] == np.arange(156))
+    assert np.all(d["dest_pos"][156:200, 0] == -1)
+
+
+# ---------------------------------------------------------------------------
+# experts, dense = sparse, special cases
+# ---------------------------------------------------------------------------
+
+def test_expert_ffn_matches_torch_functional():
+    """Library routine: torch.nn.functional in float64, non-square shapes."""
+    rng = np.random.default_rng(10)
+    d, f, o = 6, 10, 4
+    x = rng.standard_normal((5, d))
+    w = _rand_weights(rng, "swiglu", 1, d, f, o)
+    F = torch.nn.functional
+    tx = torch.from_numpy(x)
+    ref = F.linear(F.silu(F.linear(tx, torch.from_numpy(w["w1"][0]))) * F.linear(tx, torch.from_numpy(w["w3"][0])),
+                   torch.from_numpy(w["w2"][0])).numpy()
+    got = O.expert_ffn("swiglu", x, w["w1"][0], w["w3"][0], w["w2"][0])
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+    wr = _rand_weights(rng, "relu", 1, d, f, o, bias=True)
+    ref = F.linear(F.relu(F.linear(tx, torch.from_numpy(wr["w1"][0]), torch.from_numpy(wr["b1"][0]))),
+                   torch.from_numpy(wr["w2"][0]), torch.from_numpy(wr["b2"][0])).numpy()
+    got = O.expert_ffn("relu", x, wr["w1"][0], None, wr["w2"][0], wr["b1"][0], wr["b2"][0])
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+    wl = _rand_weights(rng, "linear", 1, d, f, o, bias=True)
+    ref = F.linear(tx, torch.from_numpy(wl["w1"][0]), torch.from_numpy(wl["b1"][0])).numpy()
+    assert np.allclose(O.expert_ffn("linear", x, wl["w1"][0], b1=wl["b1"][0]), ref, rtol=1e-12)
+    u = rng.standard_normal(100) * 4
+    assert np.allclose(O.silu(u), F.silu(torch.from_numpy(u)).numpy(), rtol=1e-13)
+
+
+@pytest.mark.parametrize("kind", ["linear", "relu", "swiglu"])
+@pytest.mark.parametrize("mode", ["renorm", "prob"])
+def test_dense_equals_sparse_at_k_equal_E(kind, mode):
+    """P4 稠密 vs 稀疏: the sparse layer only adds a top-k step."""
+    rng = np.random.default_rng(11)
+    T, d, f, E = 37, 8, 12, 5
+    x = rng.standard_normal((T, d))
+    w_g = rng.standard_normal((E, d)) / math.sqrt(d)
+    b_g = rng.standard_normal(E) * 0.5
+    w = _rand_weights(rng, kind, E, d, f, d, bias=(kind != "swiglu"))
+    sparse = O.forward(x, w_g, b_g, k=E, gate_mode=mode, C=-1, kind=kind, weights=w)["y"]
+    dense = O.dense_moe(x, w_g, b_g, kind, w)
+    assert np.allclose(sparse, dense, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_plain_ffn():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((9, 6))
+    w = _rand_weights(rng, "relu", 1, 6, 10, 6)
+    y = O.forward(x, rng.standard_normal((1, 6)), None, 1, "renorm", -1, "relu", w)["y"]
+    ref = np.maximum(x @ w["w1"][0].T, 0) @ w["w2"][0].T
+    assert np.allclose(y, ref, rtol=1e-13)
+
+
+def test_identity_linear_experts_return_input():
+    """A_i = I, b_i = 0, renormalised gates, no drops: y = x exactly-ish."""
+    rng = np.random.default_rng(13)
+    T, d, E = 40, 7, 4
+    x = rng.standard_normal((T, d))
+    w = {"w1": np.stack([np.eye(d)] * E)}
+    for k in (1, 2, 4):
+        y = O.forward(x, rng.standard_normal((E, d)), None, k, "renorm", -1, "linear", w)["y"]
+        assert np.allclose(y, x, rtol=1e-14, atol=1e-15)
+
+
+def test_expert_relabelling_leaves_output_unchanged():
+    rng = np.random.default_rng(14)
+    T, d, f, E, k = 60, 8, 10, 6, 2
+    x = rng.standard_normal((T, d))
+    w_g = rng.standard_normal((E, d))
+    w = _rand_weights(rng, "swiglu", E, d, f, d)
+    perm = rng.permutation(E)
+    wp = {key: v[perm] for key, v in w.items()}
+    for C in (-1, 15):
+        a = O.forward(x, w_g, None, k, "prob", C, "swiglu", w)
+        b = O.forward(x, w_g[perm], None, k, "prob", C, "swiglu", wp)
+        assert np.allclose(a["y"], b["y"], rtol=1e-12, atol=1e-14)
+        assert abs(a["aux_loss"] - b["aux_loss"]) < 1e-14
+
+
+def test_shared_experts_add_with_weight_one():
+    """P5 共享专家隔离: routed experts all zero -> y is the shared experts' sum."""
+    rng = np.random.default_rng(15)
+    T, d, f, E = 20, 6, 9, 4
+    x = rng.standard_normal((T, d))
+    zero = {"w1": np.zeros((E, f, d)), "w3": np.zeros((E, f, d)), "w2": np.zeros((E, d, f))}
+    sh = _rand_weights(rng, "swiglu", 2, d, f, d)
+    y = O.forward(x, rng.standard_normal((E, d)), None, 2, "prob", -1, "swiglu", zero, shared=sh)["y"]
+    F = torch.nn.functional
+    tx = torch.from_numpy(x)
+    ref = 0
+    for s in range(2):
+        ref = ref + F.linear(F.silu(F.linear(tx, torch.from_numpy(sh["w1"][s]))) * F.linear(tx, torch.from_numpy(sh["w3"][s])),
+                             torch.from_numpy(sh["w2"][s])).numpy()
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_dropped_slots_contribute_zero_and_residual_passes_input():
+    """P5 专家容量: a dropped token's expert output is 0 and, with the residual,
+    the layer hands x on unchanged."""
+    rng = np.random.default_rng(16)
+    T, d, E = 10, 5, 2
+    x = rng.standard_normal((T, d))
+    w_g = np.zeros((E, d))
+    w_g[0, 0] = 100.0                                     # everyone prefers expert 0 when x0 > 0
+    x[:, 0] = np.abs(x[:, 0]) + 1
+    w = {"w1": rng.standard_normal((E, d, d))}
+    out = O.forward(x, w_g, None, 1, "prob", 3, "linear", w, residual=x)
+    dropped = out["dest_pos"][:, 0] < 0
+    assert dropped.sum() == T - 3
+    assert np.array_equal(out["y"][dropped], x[dropped])   # exactly the residual
+    out2 = O.forward(x, w_g, None, 1, "prob", 3, "linear", w)
+    assert np.all(out2["y"][dropped] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# aux loss: equals alpha under uniform routing (P1 §3.4, P5 负载均衡损失函数)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_aux_loss_is_alpha_when_probs_uniform(k):
+    rng = np.random.default_rng(17)
+    T, d, E = 64, 5, 8
+    x = rng.standard_normal((T, d))
+    w = {"w1": rng.standard_normal((E, d, d))}
+    out = O.forward(x, np.zeros((E, d)), None, k, "renorm", -1, "linear", w, alpha=0.01)
+    assert abs(out["aux_loss"] - 0.01) < 1e-15
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_aux_loss_is_alpha_when_loads_uniform(k):
+    rng = np.random.default_rng(18)
+    T, E = 64, 8
+    idx = np.array([[(t * k + j) % E for j in range(k)] for t in range(T)])   # round robin
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    assert np.all(counts == T * k // E)
+    p = scipy.special.softmax(rng.standard_normal((T, E)) * 3, axis=1)       # arbitrary probabilities
+    assert abs(O.aux_loss(counts, p.sum(axis=0), T, k, E, 0.01) - 0.01) < 1e-15
+
+
+def test_aux_loss_grows_when_unbalanced():
+    T, E = 32, 4
+    counts = np.array([T, 0, 0, 0])
+    colsum = np.array([T, 0.0, 0.0, 0.0])
+    assert abs(O.aux_loss(counts, colsum, T, 1, E, 1.0) - E) < 1e-12    # collapse gives E
+
+
+# ---------------------------------------------------------------------------
+# stored formats (library routines)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_table_matches_torch_and_format_landmarks():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    t = O.E4M3_TABLE
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(t), nan)
+    assert np.array_equal(t[~nan], ref[~nan])
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6 and t[0x38] == 1.0
+    assert nan.sum() == 2
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(19)
+    bits = rng.integers(0, 2 ** 16, size=5000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]                   # finite only
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_to_f64(bits), ref)
+
+
+def test_fp8_weights_decode_with_row_scales():
+    q = np.array([[0x38, 0x40], [0x7E, 0x01]], dtype=np.uint8)   # [1, 2], [448, 2^-9]
+    s = np.array([0.5, 2.0], dtype=np.float32)
+    assert O.to_f64(q, "fp8", s).tolist() == [[0.5, 1.0], [896.0, 2.0 ** -8]]
+
+
+def test_aux_loss_counts_assignments_before_capacity_drops():
+    """P1 §3.4 takes the selection frequency from the top-k indices
+    themselves, so capacity drops do not change f."""
+    rng = np.random.default_rng(20)
+    T, d, E = 48, 6, 4
+    x = rng.standard_normal((T, d))
+    w_g = rng.standard_normal((E, d)) + np.array([[2.0], [0.0], [0.0], [0.0]])
+    w = {"w1": rng.standard_normal((E, d, d))}
+    a = O.forward(x, w_g, None, 2, "prob", -1, "linear", w, alpha=0.01)
+    b = O.forward(x, w_g, None, 2, "prob", 5, "linear", w, alpha=0.01)
+    assert (b["dest_pos"] < 0).any()
+    assert a["aux_loss"] == b["aux_loss"]
