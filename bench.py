@@ -1,0 +1,211 @@
+"""Benchmark: MoE-layer forward on one MI355X.
+
+A step is one pass of the whole layer (router -> dispatch/permute -> routed
+expert FFN -> shared expert FFN -> combine -> aux loss) over one batch of the
+workload, with inputs already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload mixtral]
+
+The roofline object describes the grouped expert FFN (the only dense
+contraction, and the dominant cost): algorithmic FLOPs of one call over its
+mean duration, measured with HIP events on the stream the kernels run on.
+The CPU baseline times the float64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_traffic_mixtral.json")
+
+
+def ffn_flops_per_row(cfg) -> float:
+    if cfg.ffn == "linear":
+        return 2.0 * cfg.d * cfg.d_out
+    if cfg.ffn == "relu":
+        return 2.0 * cfg.d * cfg.d_ff + 2.0 * cfg.d_ff * cfg.d_out
+    return 4.0 * cfg.d * cfg.d_ff + 2.0 * cfg.d_ff * cfg.d_out
+
+
+def stage_bytes(cfg, a_kept: int) -> dict:
+    """Minimum HBM bytes each memory-bound stage must move."""
+    sx = 4 if cfg.act_dtype == "f32" else 2
+    T, d, E, k, do = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_out
+    router = T * d * sx + E * d * 4 + T * k * 8 + E * 4
+    dispatch = T * k * 4 + T * d * sx + a_kept * d * sx + T * k * 4 * 2
+    combine = a_kept * do * sx + T * k * 8 + T * do * sx + (cfg.n_shared * T * do * sx)
+    return {"router": router, "dispatch": dispatch, "combine": combine}
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "sparse_mixture_experts_atomic_amd", "csrc", "ffn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per FFN call from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("ffn_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_call")
+
+
+def cpu_baseline(cfg, arr, C, n_tokens: int):
+    """The oracle, as it stands, on the first n_tokens tokens (all experts)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    w = O.decode_weights(arr, cfg.w_dtype)
+    sh = O.decode_weights(arr, cfg.w_dtype, prefix="sh_") if cfg.n_shared else None
+    x = O.to_f64(arr["x"][:n_tokens], cfg.act_dtype)
+    b_g = None if arr["b_g"] is None else arr["b_g"].astype(np.float64)
+    O.forward(x, arr["w_g"].astype(np.float64), b_g, cfg.k, cfg.gate,
+              O.capacity(n_tokens, cfg.k, cfg.E, cfg.cf, cfg.cap_round), cfg.ffn, w, sh, cfg.alpha)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tokens} of {cfg.T} tokens of the {cfg.name} workload, float64 numpy oracle "
+                      f"incl. decoding all expert weights to float64; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a 1 GiB device copy (for counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 3}))
+        return
+
+    import workloads as W
+    from sparse_mixture_experts_atomic_amd import MoELayer
+    from workloads.device import layer_kwargs, to_tensor
+    import oracle as O
+
+    cfg = W.CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    arr = W.generate(cfg)
+    C = O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+    print(f"[bench] generated {cfg.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    layer = MoELayer(**layer_kwargs(cfg, arr, C, device="cuda"))
+    x = to_tensor(arr["x"], "cuda")
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+
+    stages = ["router", "dispatch", "experts", "shared", "combine", "aux"]
+    ev = {s: [] for s in stages}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        marks[0].record()
+        layer.router(x)
+        marks[1].record()
+        layer.dispatch(x)
+        marks[2].record()
+        layer.experts()
+        marks[3].record()
+        layer.shared(x)
+        marks[4].record()
+        layer.combine()
+        marks[5].record()
+        layer.aux()
+        marks[6].record()
+        for i, s in enumerate(stages):
+            ev[s].append((marks[i], marks[i + 1]))
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    st_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+
+    a_kept = int(layer.offsets[-1].item())
+    ffn_flops = ffn_flops_per_row(cfg) * a_kept
+    sh_flops = ffn_flops_per_row(cfg) * cfg.T * cfg.n_shared
+    ffn_tflops = ffn_flops / (st_ms["experts"] * 1e-3) / 1e12
+    byts = stage_bytes(cfg, a_kept)
+    traffic = stored_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "n_shared": cfg.n_shared, "d_ff": cfg.d_ff, "ffn": cfg.ffn, "gate": cfg.gate,
+                   "capacity": C, "activations": cfg.act_dtype, "expert_weights": cfg.w_dtype,
+                   "router": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": ffn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ffn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "moe_expert_ffn_grouped (routed experts): gate/up GEMM + down GEMM",
+                     "flops_per_launch": ffn_flops, "mean_ms": st_ms["experts"]},
+        "stages_ms": st_ms,
+        "stages_hbm_frac": {
+            "router": byts["router"] / (st_ms["router"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "dispatch": byts["dispatch"] / (st_ms["dispatch"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "combine": byts["combine"] / (st_ms["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        },
+        "shared_tflops": (sh_flops / (st_ms["shared"] * 1e-3) / 1e12) if cfg.n_shared else None,
+        "kept_rows": a_kept,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, arr, C, min(args.cpu_tokens, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,71 @@
+// Internal helpers shared by the libmoe translation units: status handling
+// on the host, bf16/fp8 conversions and small vector types on the device.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- host side
+
+void record_hip_error(hipError_t e);
+
+// Checks the launch that was just enqueued; records the HIP error if any.
+inline int check_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr size_t kWsAlign = 256;
+
+inline int dtype_bytes(int dt) {
+  switch (dt) {
+    case MOE_F32: return 4;
+    case MOE_BF16: return 2;
+    case MOE_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+// -------------------------------------------------------------- device side
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + expf(-u)); }
+
+}  // namespace moe

@@ -1,0 +1,234 @@
+// (a) Router: logits z = x W_g^T (+ b_g) in fp32, softmax in fp32, top-k,
+// gate weights, and per-block column sums of the probabilities.
+//
+// P4 公式：三步走 (router score W_g x, W_g shaped experts x width); P5
+// 选择性精度 (the router softmax is computed in float32); P1 §3.3, P2 §2.1,
+// P3 §3.1 (keep the k largest, optionally renormalised).
+#include <math.h>
+
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRtTok = 32;       // tokens per block
+constexpr int kRtExp = 64;       // experts per inner group
+constexpr int kRtDc = 32;        // columns of d per LDS chunk
+constexpr int kRtThreads = 256;
+constexpr int kRtMaxE = 256;   // logits of a block stay in LDS
+constexpr int kRtMaxK = 64;    // one selected slot per lane
+
+struct RouterArgs {
+  const void* x;
+  const float* w_g;
+  const float* b_g;
+  int T, d, E, k, mode;
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* colsum_part;   // [gridDim.x, E]
+  float* logits_dbg;
+};
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// One block = 32 tokens x all E experts.  Logits are accumulated in
+// registers (2 tokens x 4 experts per thread per 64-expert group) from LDS
+// tiles of x and W_g, then kept in LDS for the softmax/top-k phase, which
+// runs one wavefront per token.
+template <typename XT>
+__global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a) {
+  extern __shared__ float smem[];
+  float* xs = smem;                          // [kRtDc][kRtTok]
+  float* ws = xs + kRtDc * kRtTok;           // [kRtDc][kRtExp]
+  float* lg = ws + kRtDc * kRtExp;           // [kRtTok][E]
+  float* wcol = lg + kRtTok * a.E;           // [4 waves][E] probability partial sums
+
+  const XT* x = static_cast<const XT*>(a.x);
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRtTok;
+  const int tx = tid & 15;                   // expert quad
+  const int ty = tid >> 4;                   // token pair
+
+  for (int eg = 0; eg < a.E; eg += kRtExp) {
+    float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int c0 = 0; c0 < a.d; c0 += kRtDc) {
+      // x chunk: 32 tokens x 32 columns, 4 per thread, stored column-major
+      {
+        int t = tid >> 3, c = (tid & 7) * 4;
+        int tg = t0 + t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int cg = c0 + c + i;
+          float v = 0.f;
+          if (tg < a.T && cg < a.d) v = Elem<XT>::load(x, static_cast<size_t>(tg) * a.d + cg);
+          xs[(c + i) * kRtTok + t] = v;
+        }
+      }
+      // W_g chunk: 64 experts x 32 columns, 8 per thread
+      {
+        int e = tid >> 2, c = (tid & 3) * 8;
+        int eg2 = eg + e;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          int cg = c0 + c + i;
+          float v = 0.f;
+          if (eg2 < a.E && cg < a.d) v = a.w_g[static_cast<size_t>(eg2) * a.d + cg];
+          ws[(c + i) * kRtExp + e] = v;
+        }
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int c = 0; c < kRtDc; ++c) {
+        float x0 = xs[c * kRtTok + ty * 2];
+        float x1 = xs[c * kRtTok + ty * 2 + 1];
+        float4 w = *reinterpret_cast<const float4*>(&ws[c * kRtExp + tx * 4]);
+        acc[0][0] = fmaf(x0, w.x, acc[0][0]);
+        acc[0][1] = fmaf(x0, w.y, acc[0][1]);
+        acc[0][2] = fmaf(x0, w.z, acc[0][2]);
+        acc[0][3] = fmaf(x0, w.w, acc[0][3]);
+        acc[1][0] = fmaf(x1, w.x, acc[1][0]);
+        acc[1][1] = fmaf(x1, w.y, acc[1][1]);
+        acc[1][2] = fmaf(x1, w.z, acc[1][2]);
+        acc[1][3] = fmaf(x1, w.w, acc[1][3]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int e = eg + tx * 4 + j;
+        if (e < a.E) {
+          float v = acc[i][j];
+          if (a.b_g) v += a.b_g[e];
+          lg[(ty * 2 + i) * a.E + e] = v;
+        }
+      }
+  }
+  __syncthreads();
+
+  // softmax + top-k: one wavefront per token
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int e = lane; e < a.E; e += 64) wcol[wave * a.E + e] = 0.f;
+  for (int tl = wave; tl < kRtTok; tl += kRtThreads / 64) {
+    int t = t0 + tl;
+    if (t >= a.T) break;
+    const float* z = lg + tl * a.E;
+    float m = -INFINITY;
+    for (int e = lane; e < a.E; e += 64) m = fmaxf(m, z[e]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float s = 0.f;
+    for (int e = lane; e < a.E; e += 64) s += expf(z[e] - m);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    const float inv = 1.0f / s;
+    for (int e = lane; e < a.E; e += 64) {
+      if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z[e];
+      wcol[wave * a.E + e] += expf(z[e] - m) * inv;
+    }
+    // top-k: k rounds of a wavefront arg-max; expert e lives on lane e % 64,
+    // slot e / 64, and the winning lane marks that slot as taken.
+    uint32_t taken = 0;
+    float myp = 0.f;
+    int myi = 0;
+    float psum = 0.f;
+    for (int j = 0; j < a.k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int e = lane, i = 0; e < a.E; e += 64, ++i) {
+        if (!((taken >> i) & 1u) && better(z[e], e, bv, bi)) { bv = z[e]; bi = e; }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o);
+        int oi = __shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      const float p = expf(bv - m) * inv;
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == j) { myp = p; myi = bi; }
+      psum += p;
+    }
+    if (lane < a.k) {
+      const size_t o = static_cast<size_t>(t) * a.k + lane;
+      a.topk_idx[o] = myi;
+      a.topk_gate[o] = a.mode == MOE_GATE_RENORM ? myp / psum : myp;
+    }
+  }
+  __syncthreads();
+  // per-block probability column sums, fixed order over the 4 waves
+  for (int e = tid; e < a.E; e += kRtThreads) {
+    float v = wcol[e] + wcol[a.E + e] + wcol[2 * a.E + e] + wcol[3 * a.E + e];
+    a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + e] = v;
+  }
+}
+
+// prob_colsum[e] = sum over blocks of the partial sums, in block order,
+// accumulated in double so the result does not drift with the block count.
+__global__ void colsum_reduce_kernel(const float* part, int nb, int E, float* out) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  double s = 0.0;
+  for (int b = 0; b < nb; ++b) s += static_cast<double>(part[static_cast<size_t>(b) * E + e]);
+  out[e] = static_cast<float>(s);
+}
+
+inline int router_blocks(int T) { return (T + kRtTok - 1) / kRtTok; }
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_router_workspace_size(int T, int d, int E, int x_dt) {
+  (void)d;
+  (void)x_dt;
+  if (T < 0 || E < 1) return 0;
+  return align_up(static_cast<size_t>(router_blocks(T)) * E * sizeof(float), kWsAlign) + kWsAlign;
+}
+
+int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g, int T, int d, int E,
+                    int k, int gate_mode, int32_t* topk_idx, float* topk_gate, float* prob_colsum,
+                    float* logits_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kRtMaxE || k > kRtMaxK) return MOE_ERR_UNSUPPORTED;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (gate_mode != MOE_GATE_PROB && gate_mode != MOE_GATE_RENORM) return MOE_ERR_INVALID_ARG;
+  if (!w_g || !aligned16(w_g) || (b_g && !aligned16(b_g))) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (topk_idx && !aligned16(topk_idx)) || (topk_gate && !aligned16(topk_gate)) ||
+      (prob_colsum && !aligned16(prob_colsum)) || (logits_dbg && !aligned16(logits_dbg)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_router_workspace_size(T, d, E, x_dt);
+  if (prob_colsum && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
+  if (T > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
+
+  const int nb = router_blocks(T);
+  float* part = static_cast<float*>(workspace);
+  if (T > 0) {
+    RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
+    size_t lds = (static_cast<size_t>(kRtDc) * kRtTok + static_cast<size_t>(kRtDc) * kRtExp +
+                  static_cast<size_t>(kRtTok) * E + 4 * static_cast<size_t>(E)) * sizeof(float);
+    if (x_dt == MOE_F32)
+      hipLaunchKernelGGL(router_generic_kernel<float>, dim3(nb), dim3(kRtThreads), lds, stream, a);
+    else
+      hipLaunchKernelGGL(router_generic_kernel<uint16_t>, dim3(nb), dim3(kRtThreads), lds, stream, a);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+  }
+  if (prob_colsum) {
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3((E + 255) / 256), dim3(256), 0, stream,
+                       static_cast<const float*>(part), nb, E, prob_colsum);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"
