@@ -325,8 +325,7 @@ def combine(ye: np.ndarray, dest_pos: np.ndarray, g: np.ndarray, ys: Optional[np
     dropped token is 0) and the remaining gates are left as they are.
     """
     T, k = dest_pos.shape
-    n_out = ye.shape[1] if ye.shape[0] else (ys.shape[1] if ys is not None else 0)
-    y = np.zeros((T, n_out), dtype=np.float64)
+    y = np.zeros((T, ye.shape[1]), dtype=np.float64)
     for t in range(T):
         for j in range(k):
             p = int(dest_pos[t, j])

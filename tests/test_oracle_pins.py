@@ -433,3 +433,16 @@ def test_aux_loss_counts_assignments_before_capacity_drops():
     b = O.forward(x, w_g, None, 2, "prob", 5, "linear", w, alpha=0.01)
     assert (b["dest_pos"] < 0).any()
     assert a["aux_loss"] == b["aux_loss"]
+
+
+def test_combine_with_every_slot_dropped_is_zero_with_full_width():
+    """P5 专家容量: with capacity 0 every expert output is 0, so the layer
+    output is all zeros (full width), and exactly x with the residual."""
+    rng = np.random.default_rng(21)
+    T, d, E = 12, 5, 3
+    x = rng.standard_normal((T, d))
+    w = {"w1": rng.standard_normal((E, d, d))}
+    out = O.forward(x, rng.standard_normal((E, d)), None, 2, "renorm", 0, "linear", w)
+    assert out["y"].shape == (T, d) and np.all(out["y"] == 0.0)
+    out = O.forward(x, rng.standard_normal((E, d)), None, 2, "renorm", 0, "linear", w, residual=x)
+    assert np.array_equal(out["y"], x)
