@@ -154,7 +154,7 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
   if (E > kDsMaxE) return MOE_ERR_UNSUPPORTED;
   if (!counts_routed || !counts_kept || !offsets) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_idx || !dest_pos || !perm_token)) return MOE_ERR_INVALID_ARG;
-  const bool copy_rows = x != nullptr || x_perm != nullptr;
+  const bool copy_rows = T > 0 && (x != nullptr || x_perm != nullptr);
   if (copy_rows) {
     if (!x || !x_perm || d < 1) return MOE_ERR_INVALID_ARG;
     if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;

@@ -52,8 +52,11 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
   const int ty = tid >> 4;                   // token pair
 
   for (int eg = 0; eg < a.E; eg += kRtExp) {
-    float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // each 32-column chunk is summed in fp32, the running total in fp64, so
+    // the rounding error does not grow with d the way one long fp32 chain does
+    double tot[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
     for (int c0 = 0; c0 < a.d; c0 += kRtDc) {
+      float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       // x chunk: 32 tokens x 32 columns, 4 per thread, stored column-major
       {
         int t = tid >> 3, c = (tid & 7) * 4;
@@ -93,6 +96,10 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
         acc[1][2] = fmaf(x1, w.z, acc[1][2]);
         acc[1][3] = fmaf(x1, w.w, acc[1][3]);
       }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tot[i][j] += static_cast<double>(acc[i][j]);
       __syncthreads();
     }
 #pragma unroll
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
       for (int j = 0; j < 4; ++j) {
         int e = eg + tx * 4 + j;
         if (e < a.E) {
-          float v = acc[i][j];
+          float v = static_cast<float>(tot[i][j]);
           if (a.b_g) v += a.b_g[e];
           lg[(ty * 2 + i) * a.E + e] = v;
         }

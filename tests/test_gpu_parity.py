@@ -128,7 +128,7 @@ def test_page_worked_example_on_gpu():
     r = Run(cfg, arr)
     y, loss = r.layer.forward(r.x)
     torch.cuda.synchronize()
-    g = r.layer.topk_gate.cpu().numpy()[0]
+    g = r.layer.topk_gate.cpu().numpy()[0].astype(np.float64)
     idx = r.layer.topk_idx.cpu().numpy()[0]
     assert idx.tolist() == [2, 1, 0]
     assert np.round(g[np.argsort(idx)], 2).tolist() == ex["gates_printed"]

@@ -65,6 +65,8 @@ def gen_x(cfg: MoEConfig, rows: Optional[slice] = None) -> np.ndarray:
     chunk = 1024
     T = cfg.T
     start, stop = (0, T) if rows is None else (rows.start or 0, rows.stop if rows.stop is not None else T)
+    if stop <= start:
+        return _store(np.zeros((0, cfg.d), np.float32), cfg.act_dtype)[0]
     c0, c1 = start // chunk, (stop + chunk - 1) // chunk
 
     def one(ci):
