@@ -5,9 +5,9 @@
 // P3 §3.1: the same weighted sum over the k slots; P5 专家容量: a dropped
 // token's expert output is 0.  Aux: P5 负载均衡损失函数, P1 §3.4.
 //
-// Each output row is produced by one block with fp32 accumulation in a fixed
-// order (slots, then shared experts, then residual): no atomics, so the
-// result does not depend on scheduling.
+// Each output element is produced by one thread with fp32 accumulation in a
+// fixed order (slots, then shared experts, then residual): no atomics, so
+// the result does not depend on scheduling.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -43,59 +43,69 @@ template <typename T> struct Vec<T, 1> {
   __device__ __forceinline__ static T pack(const float* f) { T r; Elem<T>::store(&r, 0, f[0]); return r; }
 };
 
+// One thread = one 16-byte output vector of one token (grid y = token).  The gate-weighted
+// rows of the (up to 8 unrolled) slots are loaded together, so a wavefront has
+// k row loads in flight; slot indices and gates are uniform across the
+// wavefront's 64 vectors of the same token.
+constexpr int kCbUnroll = 8;
+
 template <typename T, int VW>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_rows, const int32_t* __restrict__ dest_pos,
-                                                     const float* __restrict__ gate, int T_, int k, int d_out,
+                                                     const float* __restrict__ gate, int T_, int k, int nvec,
                                                      const T* __restrict__ shared_y, int n_shared,
-                                                     const T* __restrict__ residual, T* __restrict__ y, int rows) {
+                                                     const T* __restrict__ residual, T* __restrict__ y) {
   using V = typename Vec<T, VW>::type;
-  const int nvec = d_out / VW;
-  const int t_begin = blockIdx.x * rows;
-  const int t_end = min(T_, t_begin + rows);
+  const int t = blockIdx.y;
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= nvec) return;
   const V* yr = reinterpret_cast<const V*>(y_rows);
-  const V* sy = reinterpret_cast<const V*>(shared_y);
-  const V* rs = reinterpret_cast<const V*>(residual);
-  V* out = reinterpret_cast<V*>(y);
-  for (int t = t_begin; t < t_end; ++t) {
-    for (int v = threadIdx.x; v < nvec; v += 256) {
-      float acc[VW];
+  const int32_t* dp = dest_pos + static_cast<size_t>(t) * k;
+  const float* gp = gate + static_cast<size_t>(t) * k;
+  float acc[VW];
 #pragma unroll
-      for (int i = 0; i < VW; ++i) acc[i] = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int dp = dest_pos[static_cast<size_t>(t) * k + j];
-        if (dp < 0) continue;
-        const float g = gate[static_cast<size_t>(t) * k + j];
-        float f[VW];
-        Vec<T, VW>::unpack(yr[static_cast<size_t>(dp) * nvec + v], f);
+  for (int i = 0; i < VW; ++i) acc[i] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += kCbUnroll) {
+    V rv[kCbUnroll];
+    int d[kCbUnroll];
 #pragma unroll
-        for (int i = 0; i < VW; ++i) acc[i] = fmaf(g, f[i], acc[i]);
-      }
-      for (int s = 0; s < n_shared; ++s) {
-        float f[VW];
-        Vec<T, VW>::unpack(sy[(static_cast<size_t>(s) * T_ + t) * nvec + v], f);
+    for (int u = 0; u < kCbUnroll; ++u) {
+      d[u] = j0 + u < k ? dp[j0 + u] : -1;
+      if (d[u] >= 0) rv[u] = yr[static_cast<size_t>(d[u]) * nvec + v];
+    }
 #pragma unroll
-        for (int i = 0; i < VW; ++i) acc[i] += f[i];
-      }
-      if (rs) {
-        float f[VW];
-        Vec<T, VW>::unpack(rs[static_cast<size_t>(t) * nvec + v], f);
+    for (int u = 0; u < kCbUnroll; ++u) {
+      if (d[u] < 0) continue;
+      const float g = gp[j0 + u];
+      float f[VW];
+      Vec<T, VW>::unpack(rv[u], f);
 #pragma unroll
-        for (int i = 0; i < VW; ++i) acc[i] += f[i];
-      }
-      out[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
+      for (int i = 0; i < VW; ++i) acc[i] = fmaf(g, f[i], acc[i]);
     }
   }
+  const V* sy = reinterpret_cast<const V*>(shared_y);
+  for (int s = 0; s < n_shared; ++s) {
+    float f[VW];
+    Vec<T, VW>::unpack(sy[(static_cast<size_t>(s) * T_ + t) * nvec + v], f);
+#pragma unroll
+    for (int i = 0; i < VW; ++i) acc[i] += f[i];
+  }
+  if (residual) {
+    float f[VW];
+    Vec<T, VW>::unpack(reinterpret_cast<const V*>(residual)[static_cast<size_t>(t) * nvec + v], f);
+#pragma unroll
+    for (int i = 0; i < VW; ++i) acc[i] += f[i];
+  }
+  reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
 }
 
 template <typename T, int VW>
 int launch_combine(const void* y_rows, const int32_t* dest_pos, const float* gate, int T_, int k, int d_out,
                    const void* shared_y, int n_shared, const void* residual, void* y, hipStream_t stream) {
-  int rows = (T_ + 2047) / 2048;
-  if (rows < 1) rows = 1;
-  const int nblk = (T_ + rows - 1) / rows;
-  hipLaunchKernelGGL((combine_kernel<T, VW>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(y_rows),
-                     dest_pos, gate, T_, k, d_out, static_cast<const T*>(shared_y), n_shared,
-                     static_cast<const T*>(residual), static_cast<T*>(y), rows);
+  const int nvec = d_out / VW;
+  // grid: (vector blocks of a row, tokens)
+  hipLaunchKernelGGL((combine_kernel<T, VW>), dim3((nvec + 255) / 256, T_), dim3(256), 0, stream,
+                     static_cast<const T*>(y_rows), dest_pos, gate, T_, k, nvec, static_cast<const T*>(shared_y),
+                     n_shared, static_cast<const T*>(residual), static_cast<T*>(y));
   return check_launch();
 }
 

@@ -35,59 +35,75 @@ __global__ __launch_bounds__(kDsTok) void dispatch_count_kernel(const int32_t* _
   for (int e = threadIdx.x; e < E; e += kDsTok) block_counts[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
-// One block of 1024 threads: per expert, the exclusive scan over blocks of
-// the block counts (in place -> block base), the totals, the kept counts and
-// the exclusive scan over experts of the kept counts (offsets).
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ block_counts, int nb, int E,
-                                                            int C, int32_t* __restrict__ counts_routed,
-                                                            int32_t* __restrict__ counts_kept,
-                                                            int32_t* __restrict__ offsets) {
-  __shared__ int sc[kDsMaxE];
-  const int tid = threadIdx.x;
-  int kept = 0;
-  if (tid < E) {
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      int* p = &block_counts[static_cast<size_t>(b) * E + tid];
-      int c = *p;
-      *p = run;
-      run += c;
-    }
-    kept = C < 0 ? run : min(run, C);
-    counts_routed[tid] = run;
-    counts_kept[tid] = kept;
-  }
-  sc[tid] = kept;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 entries
-  for (int o = 1; o < 1024; o <<= 1) {
-    int v = tid >= o ? sc[tid - o] : 0;
-    __syncthreads();
-    sc[tid] += v;
-    __syncthreads();
-  }
-  if (tid < E) offsets[tid + 1] = sc[tid];
-  if (tid == 0) offsets[0] = 0;
-}
-
-// dest_pos / perm_token.  Within a wavefront lane order is token order; the
-// lanes that chose expert e form the mask M_w[e] (built with LDS atomic OR),
-// so a token's rank inside its wave is popcount(M_w[e] & lanes_below) and
-// the earlier waves of the block add popcount(M_w'[e]).
+// dest_pos / perm_token, plus (block 0) counts_routed, counts_kept and
+// offsets.  Every block first derives from the per-block counts what it
+// needs: the expert totals, their kept counts and the exclusive scan of those
+// (offsets), and its own base = counts of the earlier blocks.  That is a few
+// hundred integer loads per block and saves a separate scan launch.
+// Within the block, lane order is token order: the lanes of a wavefront that
+// chose expert e form the mask M_w[e] (LDS atomic OR), so a token's rank
+// inside its wave is popcount(M_w[e] & lanes_below) and the earlier waves
+// add popcount(M_w'[e]).
 __global__ __launch_bounds__(kDsTok) void dispatch_rank_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
-                                                              int C, const int32_t* __restrict__ block_base,
-                                                              const int32_t* __restrict__ offsets,
+                                                              int C, int nb, const int32_t* __restrict__ block_counts,
+                                                              int32_t* __restrict__ counts_routed,
+                                                              int32_t* __restrict__ counts_kept,
+                                                              int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ dest_pos,
                                                               int32_t* __restrict__ perm_token) {
-  extern __shared__ unsigned long long masks[];   // [kDsWaves][E]
-  for (int i = threadIdx.x; i < kDsWaves * E; i += kDsTok) masks[i] = 0ull;
+  extern __shared__ unsigned long long masks[];   // [kDsWaves][E], then int base[E], int off[E]
+  int* base = reinterpret_cast<int*>(masks + kDsWaves * E);
+  int* off = base + E;
+  __shared__ int wsum[kDsTok / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < kDsWaves * E; i += kDsTok) masks[i] = 0ull;
+  // totals, kept counts and this block's base, per expert
+  for (int e = tid; e < E; e += kDsTok) {
+    int total = 0, before = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int c = block_counts[static_cast<size_t>(b) * E + e];
+      total += c;
+      if (b < static_cast<int>(blockIdx.x)) before += c;
+    }
+    const int kept = C < 0 ? total : min(total, C);
+    base[e] = before;
+    off[e] = kept;
+    if (blockIdx.x == 0) {
+      counts_routed[e] = total;
+      counts_kept[e] = kept;
+    }
+  }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * kDsTok + threadIdx.x;
+  // exclusive scan of off[] (kept counts) over experts: each thread scans a
+  // contiguous run, the run totals are scanned across the block
+  const int per = (E + kDsTok - 1) / kDsTok;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int run = 0;
+  for (int e = e0; e < e1; ++e) run += off[e];
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int prefix = incl - run;
+  for (int w = 0; w < wave; ++w) prefix += wsum[w];
+  for (int e = e0; e < e1; ++e) {
+    const int kept = off[e];
+    off[e] = prefix;
+    if (blockIdx.x == 0) offsets[e] = prefix;
+    prefix += kept;
+  }
+  if (blockIdx.x == 0 && e1 == E && e0 < E) offsets[E] = prefix;
+  if (blockIdx.x == 0 && E == 0 && tid == 0) offsets[0] = 0;
+  const int t = blockIdx.x * kDsTok + tid;
   if (t < T) {
     for (int j = 0; j < k; ++j) {
-      int e = idx[static_cast<size_t>(t) * k + j];
+      const int e = idx[static_cast<size_t>(t) * k + j];
       if (e >= 0 && e < E) atomicOr(&masks[wave * E + e], 1ull << lane);
     }
   }
@@ -96,18 +112,29 @@ __global__ __launch_bounds__(kDsTok) void dispatch_rank_kernel(const int32_t* __
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int j = 0; j < k; ++j) {
     const size_t o = static_cast<size_t>(t) * k + j;
-    int e = idx[o];
+    const int e = idx[o];
     int dest = -1;
     if (e >= 0 && e < E) {
-      int r = block_base[static_cast<size_t>(blockIdx.x) * E + e];
+      int r = base[e];
       for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
       r += __popcll(masks[wave * E + e] & below);
       if (C < 0 || r < C) {
-        dest = offsets[e] + r;
+        dest = off[e] + r;
         perm_token[dest] = t;
       }
     }
     dest_pos[o] = dest;
+  }
+}
+
+// T == 0: the counts are zero and the offsets all zero.
+__global__ void dispatch_empty_kernel(int E, int32_t* counts_routed, int32_t* counts_kept, int32_t* offsets) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    offsets[e] = 0;
+    if (e < E) {
+      counts_routed[e] = 0;
+      counts_kept[e] = 0;
+    }
   }
 }
 
@@ -168,19 +195,16 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
 
   const int nb = disp_blocks(T);
   int32_t* bc = static_cast<int32_t*>(workspace);
-  if (nb > 0) {
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(kDsTok), 0, stream, topk_idx, T, k, E, bc);
-    int st = check_launch();
-    if (st != MOE_OK) return st;
+  if (nb == 0) {
+    hipLaunchKernelGGL(dispatch_empty_kernel, dim3(1), dim3(256), 0, stream, E, counts_routed, counts_kept, offsets);
+    return check_launch();
   }
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, stream, bc, nb, E, capacity, counts_routed,
-                     counts_kept, offsets);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(kDsTok), 0, stream, topk_idx, T, k, E, bc);
   int st = check_launch();
   if (st != MOE_OK) return st;
-  if (nb == 0) return MOE_OK;
-  const size_t lds = static_cast<size_t>(kDsWaves) * E * sizeof(unsigned long long);
-  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nb), dim3(kDsTok), lds, stream, topk_idx, T, k, E, capacity,
-                     static_cast<const int32_t*>(bc), static_cast<const int32_t*>(offsets), dest_pos, perm_token);
+  const size_t lds = static_cast<size_t>(kDsWaves) * E * sizeof(unsigned long long) + 2 * E * sizeof(int);
+  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nb), dim3(kDsTok), lds, stream, topk_idx, T, k, E, capacity, nb,
+                     static_cast<const int32_t*>(bc), counts_routed, counts_kept, offsets, dest_pos, perm_token);
   st = check_launch();
   if (st != MOE_OK) return st;
   if (!copy_rows) return MOE_OK;

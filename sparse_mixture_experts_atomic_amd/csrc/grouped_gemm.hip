@@ -1,0 +1,359 @@
+// Grouped GEMM over variable-size expert segments on gfx950 bf16 MFMA.
+//
+// For each segment e (rows [offsets[e], offsets[e+1]) of A) and each weight
+// matrix B_e [N, K] (stored [out, in], K contiguous):  C = epi(A_e B_e^T).
+// This is the only dense contraction of the layer (the expert FFN matrices
+// of P1 §3.2 / P3 §3.1 / P4 公式：三步走, one batch per expert as P1 §2.4
+// describes).
+//
+// Design (gfx950 / CDNA4):
+//  * block tile BM x BN (weight rows) x 32 (K per stage), 4 wavefronts in a
+//    2x2 grid; each wavefront owns a (BM/2) x (BN/2) accumulator tile made of
+//    v_mfma_f32_32x32x16_bf16 fragments.  On gfx950 this instruction reaches
+//    the bf16 peak with a handful of independent accumulators per wavefront,
+//    and a 128x128 wave tile needs ~64 B of LDS reads per 4096 FLOP, inside
+//    the ~100-150 B/clk a CU's LDS delivers
+//  * global -> registers one stage (64 of K) ahead, registers -> LDS double
+//    buffer, one barrier per stage; LDS rows are 32 bf16 = 4 chunks of 16 B, chunk c of
+//    row r stored at c ^ ((r >> 2) & 3) so 16 fragment rows hit 16 distinct
+//    bank groups
+//  * fp8 e4m3 weights are widened to bf16 on the way into LDS (exact); the
+//    per-output-row scale multiplies the fp32 accumulator in the epilogue
+//  * SwiGLU: each wavefront's weight rows are half gate rows and half up rows
+//    of the same hidden columns, so silu(gate) * up is formed in registers
+//  * tiles are numbered so that the blocks resident on one XCD (blockIdx %
+//    8) take a contiguous range, m-tiles of a group of n-tiles innermost, and
+//    the valid tiles (known only on the device) are spread evenly over the
+//    eight XCDs.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+constexpr int kNGroup = 8;      // n-tiles per ordering group
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// 16 e4m3 codes -> 16 bf16 (exact: every e4m3 value is a bf16 value)
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+    auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+    o[2 * i] = (__float_as_uint(f01[0]) >> 16) | (__float_as_uint(f01[1]) & 0xffff0000u);
+    o[2 * i + 1] = (__float_as_uint(f23[0]) >> 16) | (__float_as_uint(f23[1]) & 0xffff0000u);
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+// Workgroup barrier for LDS hand-off only: release/acquire fences scoped to
+// LDS ("local") around s_barrier.  They order LDS accesses across the barrier
+// and wait for this wave's LDS operations, but not for its global loads, so
+// register prefetches stay in flight.  (__syncthreads also fences global
+// memory, which would drain every outstanding load at each stage.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// largest e in [0, E) with ts[e] <= m  (skips empty segments)
+__device__ __forceinline__ int find_segment(const int32_t* ts, int E, int m) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (ts[mid] <= m) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <int BM, int BN, int NH, int EPI, bool B_FP8>
+__global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2;        // wave tile
+  constexpr int FM = WM / 32, FN = WN / 32;      // 32x32 MFMA fragments per wave
+  constexpr int BK = 32 * NH;                    // K per stage: NH halves of 32
+  constexpr int A_LD = BM * 4 * NH / kThreads;   // 16-byte A loads per thread per stage
+  constexpr int B_LD = B_FP8 ? BN * 2 * NH / kThreads : BN * 4 * NH / kThreads;
+  constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns per block
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the thread count");
+
+  // [buffer][half][row * 4 + swizzled chunk]
+  __shared__ uint4 As[2][NH][BM * 4];
+  __shared__ uint4 Bs[2][NH][BN * 4];
+
+  // ---- tile decode (XCD-aware, grouped over n) ----
+  const int n_tiles = (p.N + HC - 1) / HC;
+  const int m_total = p.ts[p.E];
+  const int V = m_total * n_tiles;
+  const int per = (V + kXcds - 1) / kXcds;
+  const int b = blockIdx.x;
+  const int slot = b / kXcds;
+  if (slot >= per) return;
+  const int L = (b % kXcds) * per + slot;
+  if (L >= V) return;
+  const int grp = L / (m_total * kNGroup);
+  const int gs = min(kNGroup, n_tiles - grp * kNGroup);
+  const int Lr = L - grp * m_total * kNGroup;
+  const int mt_g = Lr / gs;
+  const int nt = grp * kNGroup + Lr % gs;
+
+  const int e = find_segment(p.ts, p.E, mt_g);
+  const int seg0 = p.offsets[e];
+  const int seg1 = p.offsets[e + 1];
+  const int row0 = seg0 + (mt_g - p.ts[e]) * BM;
+  const int rows_valid = min(BM, seg1 - row0);
+  const int K = p.K;
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+
+  // ---- per-thread global sources: a row's BK elements are 4*NH chunks of
+  // 16 bytes (bf16) read by consecutive threads ----
+  const uint16_t* a_src[A_LD];
+  int a_slot[A_LD], a_k[A_LD], a_h[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int q = tid + kThreads * i;
+    const int h = q / (BM * 4);
+    const int r = (q % (BM * 4)) / 4;
+    const int c = q % 4;
+    a_h[i] = h;
+    a_k[i] = h * 32 + c * 8;
+    a_slot[i] = swz(r, c);
+    int rr = row0 + min(r, rows_valid - 1);
+    if (p.a_shared) rr -= seg0;
+    a_src[i] = p.A + static_cast<size_t>(rr) * K;
+  }
+  const uint8_t* b_src[B_LD];
+  int b_r[B_LD], b_k[B_LD], b_h[B_LD], b_c[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int q = tid + kThreads * i;
+    // bf16: a 16-byte chunk is 8 elements, 4 per half row; fp8: 16 elements,
+    // 2 per half row (each widened to two bf16 chunks)
+    const int per_half = B_FP8 ? 2 : 4;
+    const int h = q / (BN * per_half);
+    const int r = (q % (BN * per_half)) / per_half;
+    const int c = q % per_half;
+    b_r[i] = r;
+    b_h[i] = h;
+    b_k[i] = h * 32 + (B_FP8 ? c * 16 : c * 8);
+    b_c[i] = B_FP8 ? c * 2 : c;               // first bf16 chunk within the half
+    int n;
+    const void* base = p.B1;
+    if (EPI == EPI_SWIGLU) {
+      const int w = r / WN, q2 = r % WN;
+      n = nt * HC + w * (WN / 2) + q2 % (WN / 2);
+      if (q2 >= WN / 2) base = p.B3;
+    } else {
+      n = nt * BN + r;
+    }
+    n = min(n, N - 1);
+    const size_t elem = B_FP8 ? 1 : 2;
+    b_src[i] = static_cast<const uint8_t*>(base) + ((static_cast<size_t>(e) * N + n) * K) * elem;
+  }
+
+  uint4 ra[A_LD];
+  uint4 rb[B_LD];
+  // K tails: the address is clamped into the row (always a valid load) and
+  // the chunk is replaced by zeros, so there is no branch per load
+  auto load_stage = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int k = k0 + a_k[i];
+      const uint4 v = *reinterpret_cast<const uint4*>(a_src[i] + min(k, K - 8));
+      ra[i] = k < K ? v : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int k = k0 + b_k[i];
+      const int kc = min(k, K - (B_FP8 ? 16 : 8));
+      const size_t off = B_FP8 ? static_cast<size_t>(kc) : static_cast<size_t>(kc) * 2;
+      const uint4 v = *reinterpret_cast<const uint4*>(b_src[i] + off);
+      rb[i] = k < K ? v : zero4();
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) As[buf][a_h[i]][a_slot[i]] = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      if (B_FP8) {
+        uint4 lo, hi;
+        fp8x16_to_bf16(rb[i], lo, hi);
+        Bs[buf][b_h[i]][swz(b_r[i], b_c[i])] = lo;
+        Bs[buf][b_h[i]][swz(b_r[i], b_c[i] + 1)] = hi;
+      } else {
+        Bs[buf][b_h[i]][swz(b_r[i], b_c[i])] = rb[i];
+      }
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // 32x32x16 operands: lane supplies row (lane % 32), k-chunk (lane / 32) of
+  // the 16-wide k step.  A stage has 2*NH such sub-steps.
+  const int fr = lane & 31;
+  const int fc = lane >> 5;
+  constexpr int NSUB = 2 * NH;
+  auto read_frags = [&](int buf, int sub, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
+    const int h = sub >> 1, ks = sub & 1;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      uint4 v = Bs[buf][h][swz(wn * WN + j * 32 + fr, 2 * ks + fc)];
+      fb[j] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      uint4 v = As[buf][h][swz(wm * WM + i * 32 + fr, 2 * ks + fc)];
+      fa[i] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+  };
+  // a wavefront whose rows all lie past the segment end (the partial last
+  // tile of an expert) skips its MFMAs; it still loads and synchronises
+  const bool wave_rows = wm * WM < rows_valid;
+  auto mma = [&](const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) {
+    if (!wave_rows) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Software pipeline, per stage kt (LDS buffer kt & 1):
+  //   sub-step s: read the fragments of s+1 while the MFMAs of s run;
+  //   after sub-step 0: write stage kt+1 (registers) into the other LDS
+  //   buffer and issue the global loads of stage kt+2;
+  //   before the last sub-step: barrier (stage kt+1 visible, every read of
+  //   stage kt done), then the first fragments of stage kt+1 are read while
+  //   the last MFMAs of stage kt run.
+  const int KT = (K + BK - 1) / BK;
+  load_stage(0);
+  store_stage(0);
+  if (KT > 1) load_stage(BK);
+  lds_barrier();
+  bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  read_frags(0, 0, fa0, fb0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < KT;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      bf16x8_t (&ca)[FM] = (sub & 1) ? fa1 : fa0;
+      bf16x8_t (&cb)[FN] = (sub & 1) ? fb1 : fb0;
+      bf16x8_t (&na)[FM] = (sub & 1) ? fa0 : fa1;
+      bf16x8_t (&nb)[FN] = (sub & 1) ? fb0 : fb1;
+      if (sub + 1 < NSUB) {
+        read_frags(buf, sub + 1, na, nb);
+      } else {
+        lds_barrier();
+        if (more) read_frags(buf ^ 1, 0, na, nb);
+      }
+      mma(ca, cb);
+      if (sub == 0 && more) {
+        store_stage(buf ^ 1);
+        if (kt + 2 < KT) load_stage((kt + 2) * BK);
+      }
+    }
+    // NSUB is even, so the next stage's first fragments sit in fa0/fb0
+  }
+
+  // ---- epilogue: element q of a 32x32 fragment is row 8*(q/4) + 4*(lane/32)
+  // + q%4, column lane%32 ----
+  uint16_t* C = p.C;
+  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < FN / 2; ++j) {
+      const int col = nt * HC + wn * (WN / 2) + j * 32 + fr;
+      if (col >= N) continue;
+      const float sg = p.s1 ? p.s1[static_cast<size_t>(e) * N + col] : 1.f;
+      const float su = p.s3 ? p.s3[static_cast<size_t>(e) * N + col] : 1.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+          if (lr < rows_valid) {
+            const float g = acc[i][j][q] * sg;
+            const float u = acc[i][j + FN / 2][q] * su;
+            C[static_cast<size_t>(row0 + lr) * N + col] = f32_to_bf16(silu_f32(g) * u);
+          }
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = nt * BN + wn * WN + j * 32 + fr;
+      if (col >= N) continue;
+      const float s = p.s1 ? p.s1[static_cast<size_t>(e) * N + col] : 1.f;
+      const float bias = p.bias ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+          if (lr < rows_valid) {
+            float v = acc[i][j][q] * s + bias;
+            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+            C[static_cast<size_t>(row0 + lr) * N + col] = f32_to_bf16(v);
+          }
+        }
+    }
+  }
+}
+
+template <int BM, int BN, int NH, int EPI, bool FP8>
+int launch(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  const long n_tiles = (p.N + HC - 1) / HC;
+  long blocks = n_tiles * m_tiles_max;
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, NH, EPI, FP8>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, stream, p);
+  return check_launch();
+}
+
+template <int BM, int BN, int NH>
+int launch_epi(int epi, bool fp8, const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  if (fp8) {
+    if (epi == EPI_SWIGLU) return launch<BM, BN, NH, EPI_SWIGLU, true>(p, m_tiles_max, stream);
+    if (epi == EPI_RELU) return launch<BM, BN, NH, EPI_RELU, true>(p, m_tiles_max, stream);
+    return launch<BM, BN, NH, EPI_PLAIN, true>(p, m_tiles_max, stream);
+  }
+  if (epi == EPI_SWIGLU) return launch<BM, BN, NH, EPI_SWIGLU, false>(p, m_tiles_max, stream);
+  if (epi == EPI_RELU) return launch<BM, BN, NH, EPI_RELU, false>(p, m_tiles_max, stream);
+  return launch<BM, BN, NH, EPI_PLAIN, false>(p, m_tiles_max, stream);
+}
+
+}  // namespace
+
+// 256-row tiles throughout (one tile map serves both GEMMs of an FFN); the
+// weight-row width is 256 unless that leaves too few tiles to fill 256 CUs
+// a few times over, in which case 128.
+int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream) {
+  const int est_m = (max_rows + kGemmBM - 1) / kGemmBM;
+  const int hc256 = epi == EPI_SWIGLU ? 128 : 256;
+  const long tiles256 = static_cast<long>(est_m) * ((p.N + hc256 - 1) / hc256);
+  (void)tiles256;
+  return launch_epi<kGemmBM, 128, 1>(epi, fp8, p, m_tiles_max, stream);
+}
+
+}  // namespace moe

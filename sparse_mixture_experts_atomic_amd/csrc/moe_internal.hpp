@@ -43,6 +43,7 @@ inline int dtype_bytes(int dt) {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -67,5 +68,30 @@ template <> struct Elem<uint16_t> {
 };
 
 __device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + expf(-u)); }
+
+// ------------------------------------------------- grouped GEMM interface
+
+enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+
+constexpr int kGemmBM = 256;   // rows per m-tile of the grouped GEMM
+
+struct GemmParams {
+  const uint16_t* A;         // bf16 rows [*, K]
+  int a_shared;              // 1: segment e reads A rows from 0 (shared experts)
+  const int32_t* offsets;    // [E+1] segment bounds
+  const int32_t* ts;         // [E+1] m-tile prefix (tiles of kGemmBM rows)
+  int E;
+  const void* B1;            // [E, N, K] bf16 or e4m3 codes
+  const void* B3;            // SwiGLU up projection [E, N, K]
+  const float* s1;           // [E, N] e4m3 row scales (or null)
+  const float* s3;
+  const float* bias;         // [E, N] (or null)
+  uint16_t* C;               // bf16 [*, N]
+  int N;                     // output columns
+  int K;
+};
+
+// Enqueues C = epi(A B^T) per segment.  m_tiles_max bounds ts[E] from above.
+int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream);
 
 }  // namespace moe

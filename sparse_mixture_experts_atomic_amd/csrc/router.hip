@@ -174,17 +174,191 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
   }
 }
 
-// prob_colsum[e] = sum over blocks of the partial sums, in block order,
-// accumulated in double so the result does not drift with the block count.
-__global__ void colsum_reduce_kernel(const float* part, int nb, int E, float* out) {
-  int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= E) return;
+// Streaming router for few experts (E <= 8) and bf16 activations, d <= 4096.
+// The work is bound by reading x once, so each thread keeps the fp32 router
+// weights of its NC column chunks (8 columns each) in registers for the
+// whole block and streams tokens four at a time: one 16-byte load per token
+// and chunk, 8*E FMAs.  Per-token partial dot products are reduced across the
+// wavefront by a reduce-scatter of shuffles and across the 4 wavefronts in
+// LDS, then one thread per token does the fp32 softmax and top-k.
+constexpr int kSmE = 8;
+constexpr int kSmTok = 4;     // tokens per group
+constexpr int kSmThreads = 256;
+
+template <int NC>
+__global__ __launch_bounds__(kSmThreads) void router_small_e_kernel(RouterArgs a, int groups_per_block) {
+  __shared__ float red[kSmThreads / 64][kSmTok * kSmE];
+  __shared__ float lg[kSmTok][kSmE];
+  __shared__ float colsum[kSmE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nchunk = a.d / 8;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  if (tid < kSmE) colsum[tid] = 0.f;
+
+  // router weights of this thread's chunks: w[j][e][c]
+  float w[NC][kSmE][8];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int ch = tid + kSmThreads * j;
+#pragma unroll
+    for (int e = 0; e < kSmE; ++e) {
+      if (ch < nchunk && e < a.E) {
+        const float4 lo = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + ch * 8);
+        const float4 hi = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + ch * 8 + 4);
+        w[j][e][0] = lo.x; w[j][e][1] = lo.y; w[j][e][2] = lo.z; w[j][e][3] = lo.w;
+        w[j][e][4] = hi.x; w[j][e][5] = hi.y; w[j][e][6] = hi.z; w[j][e][7] = hi.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[j][e][c] = 0.f;
+      }
+    }
+  }
+
+  const int g0 = blockIdx.x * groups_per_block;
+  const int g1 = min(g0 + groups_per_block, (a.T + kSmTok - 1) / kSmTok);
+  // x of the next token group is loaded while the current one is reduced
+  uint4 xv[kSmTok][NC], xn[kSmTok][NC];
+  auto load_group = [&](int g, uint4 (&dst)[kSmTok][NC]) {
+#pragma unroll
+    for (int t = 0; t < kSmTok; ++t)
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int ch = tid + kSmThreads * j;
+        const int tt = g * kSmTok + t;
+        dst[t][j] = (ch < nchunk && tt < a.T)
+                        ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(tt) * a.d + ch * 8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+      }
+  };
+  if (g0 < g1) load_group(g0, xv);
+  for (int g = g0; g < g1; ++g) {
+    const int t0 = g * kSmTok;
+    if (g + 1 < g1) load_group(g + 1, xn);
+    float acc[kSmTok * kSmE];
+#pragma unroll
+    for (int i = 0; i < kSmTok * kSmE; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kSmTok; ++t)
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const uint32_t q[4] = {xv[t][j].x, xv[t][j].y, xv[t][j].z, xv[t][j].w};
+        float xf[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          xf[2 * c] = __uint_as_float(q[c] << 16);
+          xf[2 * c + 1] = __uint_as_float(q[c] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < kSmE; ++e)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[t * kSmE + e] = fmaf(xf[c], w[j][e][c], acc[t * kSmE + e]);
+      }
+    // reduce-scatter over the wavefront: after the rounds on lane bits 5..1,
+    // lane l holds entry l >> 1 summed over the 32 lanes that share bit 0
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = acc[i];
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {
+      const int o = 32 >> r;
+      const int n = 16 >> r;
+      const bool upper = (lane & o) != 0;
+#pragma unroll
+      for (int i = 0; i < n; ++i) {
+        const float send = upper ? v[i] : v[i + n];
+        const float keep = upper ? v[i + n] : v[i];
+        v[i] = keep + __shfl_xor(send, o);
+      }
+    }
+    v[0] += __shfl_xor(v[0], 1);
+    if ((lane & 1) == 0) red[wave][lane >> 1] = v[0];
+    __syncthreads();
+    if (tid < kSmTok * kSmE) {
+      const float s = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+      const int t = tid / kSmE, e = tid % kSmE;
+      lg[t][e] = s + ((a.b_g && e < a.E) ? a.b_g[e] : 0.f);
+    }
+    __syncthreads();
+    if (tid < kSmTok && t0 + tid < a.T) {
+      const int t = t0 + tid;
+      const float* z = lg[tid];
+      float m = -INFINITY;
+      for (int e = 0; e < a.E; ++e) m = fmaxf(m, z[e]);
+      float p[kSmE];
+      float s = 0.f;
+      for (int e = 0; e < a.E; ++e) { p[e] = expf(z[e] - m); s += p[e]; }
+      const float inv = 1.0f / s;
+      for (int e = 0; e < a.E; ++e) {
+        p[e] *= inv;
+        if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z[e];
+      }
+      // top-k by repeated selection (largest logit, lower index on ties)
+      uint32_t taken = 0;
+      float psum = 0.f;
+      float ps[kSmE];
+      int is[kSmE];
+      for (int j = 0; j < a.k; ++j) {
+        int bi = -1;
+        float bv = -INFINITY;
+        for (int e = 0; e < a.E; ++e)
+          if (!((taken >> e) & 1u) && (bi < 0 || z[e] > bv)) { bv = z[e]; bi = e; }
+        taken |= 1u << bi;
+        is[j] = bi;
+        ps[j] = p[bi];
+        psum += p[bi];
+      }
+      for (int j = 0; j < a.k; ++j) {
+        a.topk_idx[static_cast<size_t>(t) * a.k + j] = is[j];
+        a.topk_gate[static_cast<size_t>(t) * a.k + j] = a.mode == MOE_GATE_RENORM ? ps[j] / psum : ps[j];
+      }
+      for (int e = 0; e < a.E; ++e) red[0][tid * kSmE + e] = p[e];
+    }
+    __syncthreads();
+    // block column sums in token order (deterministic)
+    if (tid < a.E) {
+      float cs = colsum[tid];
+      for (int t = 0; t < kSmTok; ++t)
+        if (t0 + t < a.T) cs += red[0][t * kSmE + tid];
+      colsum[tid] = cs;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kSmTok; ++t)
+#pragma unroll
+      for (int j = 0; j < NC; ++j) xv[t][j] = xn[t][j];
+  }
+  if (tid < a.E) a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + tid] = colsum[tid];
+}
+
+// prob_colsum[e] = sum over blocks of the partial sums.  One block per
+// expert: strided partial sums in double, then a fixed-order tree, so the
+// result is deterministic and does not drift with the block count.
+__global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* part, int nb, int E, float* out) {
+  __shared__ double red[256];
+  const int e = blockIdx.x;
   double s = 0.0;
-  for (int b = 0; b < nb; ++b) s += static_cast<double>(part[static_cast<size_t>(b) * E + e]);
-  out[e] = static_cast<float>(s);
+  for (int b = threadIdx.x; b < nb; b += 256) s += static_cast<double>(part[static_cast<size_t>(b) * E + e]);
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[e] = static_cast<float>(red[0]);
 }
 
 inline int router_blocks(int T) { return (T + kRtTok - 1) / kRtTok; }
+
+// upper bound of the block count of either router kernel (per-block
+// probability partial sums live in the workspace)
+inline int router_max_blocks(int T) {
+  const int groups = (T + kSmTok - 1) / kSmTok;
+  const int small = groups < 1024 ? groups : 1024;
+  const int generic = router_blocks(T);
+  return small > generic ? small : generic;
+}
 
 }  // namespace
 }  // namespace moe
@@ -197,7 +371,7 @@ size_t moe_router_workspace_size(int T, int d, int E, int x_dt) {
   (void)d;
   (void)x_dt;
   if (T < 0 || E < 1) return 0;
-  return align_up(static_cast<size_t>(router_blocks(T)) * E * sizeof(float), kWsAlign) + kWsAlign;
+  return align_up(static_cast<size_t>(router_max_blocks(T)) * E * sizeof(float), kWsAlign) + kWsAlign;
 }
 
 int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g, int T, int d, int E,
@@ -216,9 +390,24 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
   if (prob_colsum && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
 
-  const int nb = router_blocks(T);
+  const bool small = x_dt == MOE_BF16 && E <= kSmE && d % 8 == 0 && d <= 2 * 8 * kSmThreads;
+  int nb = router_blocks(T);
+  int groups_per_block = 1;
+  if (small && T > 0) {
+    const int groups = (T + kSmTok - 1) / kSmTok;
+    groups_per_block = groups >= 1024 ? 2 * ((groups + 2047) / 2048) : 1;   // about 512-1024 blocks
+    nb = (groups + groups_per_block - 1) / groups_per_block;
+  }
   float* part = static_cast<float*>(workspace);
-  if (T > 0) {
+  if (T > 0 && small) {
+    RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
+    if (d <= 8 * kSmThreads)
+      hipLaunchKernelGGL(router_small_e_kernel<1>, dim3(nb), dim3(kSmThreads), 0, stream, a, groups_per_block);
+    else
+      hipLaunchKernelGGL(router_small_e_kernel<2>, dim3(nb), dim3(kSmThreads), 0, stream, a, groups_per_block);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+  } else if (T > 0) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
     size_t lds = (static_cast<size_t>(kRtDc) * kRtTok + static_cast<size_t>(kRtDc) * kRtExp +
                   static_cast<size_t>(kRtTok) * E + 4 * static_cast<size_t>(E)) * sizeof(float);
@@ -230,7 +419,7 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
     if (st != MOE_OK) return st;
   }
   if (prob_colsum) {
-    hipLaunchKernelGGL(colsum_reduce_kernel, dim3((E + 255) / 256), dim3(256), 0, stream,
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(E), dim3(256), 0, stream,
                        static_cast<const float*>(part), nb, E, prob_colsum);
     int st = check_launch();
     if (st != MOE_OK) return st;
