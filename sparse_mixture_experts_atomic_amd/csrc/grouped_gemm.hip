@@ -25,6 +25,8 @@
 //    8) take a contiguous range, m-tiles of a group of n-tiles innermost, and
 //    the valid tiles (known only on the device) are spread evenly over the
 //    eight XCDs.
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -319,6 +321,237 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 weights, K % 128 == 0: operands go global -> LDS with
+// global_load_lds_dwordx4 (no staging registers, no ds_write), through a ring
+// of four 32-deep stages (4 x 32 KB).  Block tile 256 x 256, four wavefronts
+// of 128 x 128 (one wavefront per SIMD, accumulators in AGPRs).
+//
+// Stage j is loaded while stage j - 2 is consumed: its loads are issued in the
+// middle of stage j - 3, right after the barrier that proves every wavefront
+// has finished reading the ring slot they overwrite, and waited for (vmcnt,
+// then the barrier) in the middle of stage j - 1.  The LDS image of a stage
+// is the same swizzled layout as above: a DMA lane writes slot base + lane, so
+// each lane fetches the global chunk that belongs in its slot.
+constexpr int kDmaStages = 4;
+
+// One global_load_lds_dwordx4: lane l copies 16 bytes from src to LDS byte
+// address m0 + 16 l.  Written as asm so that the compiler does not track it:
+// its own tracking of these loads waits for every one in flight before any
+// LDS read (vmcnt(0)), which would drain the ring at each k-step.  The
+// instruction writes no register (its address operands are read at issue);
+// completion is ordered by the explicit vmcnt waits and barriers below.
+__device__ __forceinline__ void dma16(const void* src, const uint4* lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
+  uint32_t saved;   // m0 is restored, so code around the asm sees it unchanged
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(m0)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, BK = 32;
+  constexpr int WM = 128, WN = 128;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  constexpr int LD = 4;                 // DMA instructions per operand per stage
+  constexpr int D = 2 * LD;             // per thread per stage
+  constexpr int BOFF = BM * 4;          // B image offset inside a ring slot (uint4)
+  __shared__ uint4 S0[(BM + BN) * 4];
+  __shared__ uint4 S1[(BM + BN) * 4];
+  __shared__ uint4 S2[(BM + BN) * 4];
+  __shared__ uint4 S3[(BM + BN) * 4];
+
+  const int n_tiles = (p.N + HC - 1) / HC;
+  const int m_total = p.ts[p.E];
+  const int V = m_total * n_tiles;
+  const int per = (V + kXcds - 1) / kXcds;
+  const int b = blockIdx.x;
+  const int slot = b / kXcds;
+  if (slot >= per) return;
+  const int L = (b % kXcds) * per + slot;
+  if (L >= V) return;
+  const int grp = L / (m_total * kNGroup);
+  const int gs = min(kNGroup, n_tiles - grp * kNGroup);
+  const int Lr = L - grp * m_total * kNGroup;
+  const int mt_g = Lr / gs;
+  const int nt = grp * kNGroup + Lr % gs;
+
+  const int e = find_segment(p.ts, p.E, mt_g);
+  const int seg0 = p.offsets[e];
+  const int seg1 = p.offsets[e + 1];
+  const int row0 = seg0 + (mt_g - p.ts[e]) * BM;
+  const int rows_valid = min(BM, seg1 - row0);
+  const int K = p.K;
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int fr = lane & 31;
+  const int fc = lane >> 5;
+
+  // DMA instruction i of this thread fills slot i * 256 + tid of an operand
+  // image: row i * 64 + tid / 4, stored chunk tid % 4, which holds global
+  // chunk (tid % 4) ^ ((row >> 2) & 3) (the XOR term is the same for all i)
+  const int cq = (tid & 3) ^ ((tid >> 4) & 3);
+  const uint16_t* a_base = p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K;
+  int a_off[LD];
+#pragma unroll
+  for (int i = 0; i < LD; ++i) a_off[i] = min(i * 64 + (tid >> 2), rows_valid - 1) * K + cq * 8;
+  const uint16_t* b_base[LD];
+  int b_off[LD];
+#pragma unroll
+  for (int i = 0; i < LD; ++i) {
+    const int r = i * 64 + (tid >> 2);
+    int n;
+    const void* base = p.B1;
+    if (EPI == EPI_SWIGLU) {
+      // rows [128 w, 128 w + 64) are gate rows of hidden columns
+      // nt * HC + 64 w + (0..63), the next 64 the up rows of the same columns
+      n = nt * HC + (r >> 7) * 64 + (r & 63);
+      if (r & 64) base = p.B3;       // i odd: uniform over the block
+    } else {
+      n = nt * BN + r;
+    }
+    n = min(n, N - 1);
+    b_base[i] = static_cast<const uint16_t*>(base) + static_cast<size_t>(e) * N * K;
+    b_off[i] = n * K + cq * 8;
+  }
+  auto issue = [&](int st, uint4* S) {
+    const int k0 = st * BK;
+#pragma unroll
+    for (int i = 0; i < LD; ++i) dma16(a_base + (a_off[i] + k0), S + i * 256 + wave * 64);
+#pragma unroll
+    for (int i = 0; i < LD; ++i) dma16(b_base[i] + (b_off[i] + k0), S + BOFF + i * 256 + wave * 64);
+  };
+  auto read_frags = [&](const uint4* S, int ks, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      uint4 v = S[BOFF + swz(wn * WN + j * 32 + fr, 2 * ks + fc)];
+      fb[j] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      uint4 v = S[swz(wm * WM + i * 32 + fr, 2 * ks + fc)];
+      fa[i] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  auto mma = [&](const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  const int KT = K / BK;                // multiple of 4, >= 4
+  // one stage: k-step 0 (k-step 1 fragments read meanwhile), wait for the
+  // next stage and barrier, issue the stage three ahead into the slot just
+  // released, k-step 1 (next stage's first fragments read meanwhile).  The
+  // flags are compile-time: LAST = no next stage, MORE = a stage after the
+  // next one is in flight, ISSUE = a stage three ahead exists.
+  auto stage = [&](auto last, auto more, auto iss, int kt, const uint4* Sc, const uint4* Sn, uint4* Sd) {
+    read_frags(Sc, 1, fa1, fb1);
+    mma(fa0, fb0);
+    if constexpr (decltype(more)::value) wait_vmcnt<D>(); else wait_vmcnt<0>();
+    lds_barrier();
+    if constexpr (decltype(iss)::value) issue(kt + 3, Sd);
+    if constexpr (!decltype(last)::value) read_frags(Sn, 0, fa0, fb0);
+    mma(fa1, fb1);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  issue(0, S0);
+  issue(1, S1);
+  issue(2, S2);
+  wait_vmcnt<2 * D>();
+  lds_barrier();
+  read_frags(S0, 0, fa0, fb0);
+  int kt = 0;
+  for (; kt + kDmaStages < KT; kt += kDmaStages) {
+    stage(F_{}, T_{}, T_{}, kt, S0, S1, S3);
+    stage(F_{}, T_{}, T_{}, kt + 1, S1, S2, S0);
+    stage(F_{}, T_{}, T_{}, kt + 2, S2, S3, S1);
+    stage(F_{}, T_{}, T_{}, kt + 3, S3, S0, S2);
+  }
+  // last round: stage KT-1 is issued in its first stage; KT-2 and KT-1 are
+  // the last ones waited for
+  stage(F_{}, T_{}, T_{}, kt, S0, S1, S3);
+  stage(F_{}, T_{}, F_{}, kt + 1, S1, S2, S0);
+  stage(F_{}, F_{}, F_{}, kt + 2, S2, S3, S1);
+  stage(T_{}, F_{}, F_{}, kt + 3, S3, S0, S2);
+
+  uint16_t* C = p.C;
+  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < FN / 2; ++j) {
+      const int col = nt * HC + wn * (WN / 2) + j * 32 + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+          if (lr < rows_valid)
+            C[static_cast<size_t>(row0 + lr) * N + col] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + FN / 2][q]);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = nt * BN + wn * WN + j * 32 + fr;
+      if (col >= N) continue;
+      const float bias = p.bias ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+          if (lr < rows_valid) {
+            float v = acc[i][j][q] + bias;
+            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+            C[static_cast<size_t>(row0 + lr) * N + col] = f32_to_bf16(v);
+          }
+        }
+    }
+  }
+}
+
+template <int EPI>
+int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
+  const long n_tiles = (p.N + HC - 1) / HC;
+  long blocks = n_tiles * m_tiles_max;
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p);
+  return check_launch();
+}
+
 template <int BM, int BN, int NH, int EPI, bool FP8>
 int launch(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
@@ -349,10 +582,15 @@ int launch_epi(int epi, bool fp8, const GemmParams& p, int m_tiles_max, hipStrea
 // weight-row width is 256 unless that leaves too few tiles to fill 256 CUs
 // a few times over, in which case 128.
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream) {
-  const int est_m = (max_rows + kGemmBM - 1) / kGemmBM;
-  const int hc256 = epi == EPI_SWIGLU ? 128 : 256;
-  const long tiles256 = static_cast<long>(est_m) * ((p.N + hc256 - 1) / hc256);
-  (void)tiles256;
+  (void)max_rows;
+  // LDS-DMA kernel: bf16 weights, a whole number of four-stage rounds, and
+  // 32-bit element offsets inside one expert's weight matrix
+  const bool dma_ok = !fp8 && p.K % (32 * kDmaStages) == 0 && static_cast<size_t>(p.N) * p.K < (size_t(1) << 31);
+  if (dma_ok) {
+    if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU>(p, m_tiles_max, stream);
+    if (epi == EPI_RELU) return launch_dma<EPI_RELU>(p, m_tiles_max, stream);
+    return launch_dma<EPI_PLAIN>(p, m_tiles_max, stream);
+  }
   return launch_epi<kGemmBM, 128, 1>(epi, fp8, p, m_tiles_max, stream);
 }
 
