@@ -26,6 +26,7 @@
 //    the valid tiles (known only on the device) are spread evenly over the
 //    eight XCDs.
 #include <type_traits>
+#include <utility>
 
 #include "moe_internal.hpp"
 
@@ -324,34 +325,67 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
 // ---------------------------------------------------------------------------
 // bf16 weights, K % 128 == 0: operands go global -> LDS with
 // global_load_lds_dwordx4 (no staging registers, no ds_write), through a ring
-// of four 32-deep stages (4 x 32 KB).  Block tile 256 x 256, four wavefronts
-// of 128 x 128 (one wavefront per SIMD, accumulators in AGPRs).
+// of R stages of BK columns of K: R = 4 for BK = 32, R = 2 for BK = 64; the
+// ring is 128 KB either way.  Block tile 256 x 256, four wavefronts of
+// 128 x 128 (one wavefront per SIMD, accumulators in AGPRs).
 //
-// Stage j is loaded while stage j - 2 is consumed: its loads are issued in the
-// middle of stage j - 3, right after the barrier that proves every wavefront
-// has finished reading the ring slot they overwrite, and waited for (vmcnt,
-// then the barrier) in the middle of stage j - 1.  The LDS image of a stage
-// is the same swizzled layout as above: a DMA lane writes slot base + lane, so
-// each lane fetches the global chunk that belongs in its slot.
-constexpr int kDmaStages = 4;
+// A stage's slot is free as soon as the barrier in the middle of that stage
+// has passed (every wavefront has read its last k-step by then; the k-step 0
+// of a stage is read during the previous one).  So stage j + R is issued into
+// slot j right after that barrier, and stage j + 1 is waited for (vmcnt, then
+// the barrier) in the middle of stage j: R - 1 stages of load latency are
+// hidden.  The LDS image of a stage is a swizzled row-major layout (see
+// dma_swz); a DMA lane writes slot base + lane, so each lane fetches the
+// global chunk that belongs in its slot.
+constexpr int kDmaKMult = 128;     // K granularity of the DMA kernel
+constexpr int kDmaBK = 64;         // K columns per ring stage (32 or 64)
 
-// One global_load_lds_dwordx4: lane l copies 16 bytes from src to LDS byte
-// address m0 + 16 l.  Written as asm so that the compiler does not track it:
+// a pointer that is the same in every lane, moved to scalar registers
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uintptr_t v = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const T*>((static_cast<uintptr_t>(hi) << 32) | lo);
+}
+
+// One global_load_lds_dwordx4 in its scalar-base form: lane l copies the 16
+// bytes at sbase + voff(l) to LDS byte address m0 + 16 l.  sbase and m0 must
+// be wave-uniform.  Written as asm so that the compiler does not track it:
 // its own tracking of these loads waits for every one in flight before any
 // LDS read (vmcnt(0)), which would drain the ring at each k-step.  The
 // instruction writes no register (its address operands are read at issue);
-// completion is ordered by the explicit vmcnt waits and barriers below.
-__device__ __forceinline__ void dma16(const void* src, const uint4* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
-  uint32_t saved;   // m0 is restored, so code around the asm sees it unchanged
+// completion is ordered by the explicit vmcnt waits and barriers below.  m0
+// is restored, so code around the asm sees it unchanged.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0_value) {
+  // readfirstlane gives the asm its own scalar copies (the compiler may keep
+  // a uniform value in vector registers, which an "s" operand does not take)
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(m0_value);
+  const void* sb = uniform_ptr(sbase);
+  uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(m0)
+      : "v"(voff), "s"(sb), "s"(m0)
       : "memory");
+}
+
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
+template <int N, typename F, int... I>
+__device__ __forceinline__ void template_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void template_for(F&& f) {
+  template_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
@@ -361,19 +395,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-template <int EPI>
+// chunk c (16 bytes) of row r of an LDS operand image with CH chunks per
+// row.  Sixteen consecutive rows read at one chunk hit 16 distinct 16-byte
+// bank groups: for CH = 4 the row sets the low two bits of the group and
+// (r >> 2) & 3 is XORed into the chunk; for CH = 8, r & 1 picks the half and
+// (r >> 1) & 7 is XORed in.
+template <int CH>
+__device__ __forceinline__ int dma_swz(int r, int c) {
+  constexpr int SH = CH == 4 ? 2 : 1;
+  return r * CH + (c ^ ((r >> SH) & (CH - 1)));
+}
+
+template <int EPI, int BK>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256, BK = 32;
+  constexpr int BM = 256, BN = 256;
+  constexpr int R = BK == 32 ? 4 : 2;   // ring stages
+  constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
+  constexpr int NKS = BK / 16;          // MFMA k-steps per stage
   constexpr int WM = 128, WN = 128;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  constexpr int LD = 4;                 // DMA instructions per operand per stage
-  constexpr int D = 2 * LD;             // per thread per stage
-  constexpr int BOFF = BM * 4;          // B image offset inside a ring slot (uint4)
-  __shared__ uint4 S0[(BM + BN) * 4];
-  __shared__ uint4 S1[(BM + BN) * 4];
-  __shared__ uint4 S2[(BM + BN) * 4];
-  __shared__ uint4 S3[(BM + BN) * 4];
+  constexpr int LD = BM * CH / kThreads;  // DMA instructions per operand per stage
+  constexpr int RPI = kThreads / CH;      // rows covered by one DMA instruction
+  constexpr int D = 2 * LD;               // per thread per stage
+  constexpr int BOFF = BM * CH;           // B image offset inside a slot (uint4)
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(NKS % 2 == 0, "k-steps per stage alternate two fragment sets");
+  static_assert(R * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
+  static_assert(D * (R - 1) < 64, "vmcnt range");
+  __shared__ uint4 ring[R][(BM + BN) * CH];
 
   const int n_tiles = (p.N + HC - 1) / HC;
   const int m_total = p.ts[p.E];
@@ -406,50 +456,59 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   const int fc = lane >> 5;
 
   // DMA instruction i of this thread fills slot i * 256 + tid of an operand
-  // image: row i * 64 + tid / 4, stored chunk tid % 4, which holds global
-  // chunk (tid % 4) ^ ((row >> 2) & 3) (the XOR term is the same for all i)
-  const int cq = (tid & 3) ^ ((tid >> 4) & 3);
-  const uint16_t* a_base = p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K;
-  int a_off[LD];
+  // image: row i * RPI + tid / CH, stored chunk tid % CH, which holds the
+  // global chunk (tid % CH) ^ ((tid >> 4) % CH) (the swizzle term of that row,
+  // the same for every i).  Addresses: a uniform base (advanced by 2 BK bytes
+  // per stage) plus a 32-bit per-lane byte offset fixed for the whole loop.
+  const int cq = (tid & (CH - 1)) ^ ((tid >> 4) & (CH - 1));
+  const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K));
+  uint32_t a_vo[LD];
 #pragma unroll
-  for (int i = 0; i < LD; ++i) a_off[i] = min(i * 64 + (tid >> 2), rows_valid - 1) * K + cq * 8;
-  const uint16_t* b_base[LD];
-  int b_off[LD];
+  for (int i = 0; i < LD; ++i)
+    a_vo[i] = static_cast<uint32_t>((min(i * RPI + tid / CH, rows_valid - 1) * K + cq * 8) * 2);
+  const char* b_sb[LD];
+  uint32_t b_vo[LD];
 #pragma unroll
   for (int i = 0; i < LD; ++i) {
-    const int r = i * 64 + (tid >> 2);
+    const int r = i * RPI + tid / CH;
     int n;
     const void* base = p.B1;
     if (EPI == EPI_SWIGLU) {
       // rows [128 w, 128 w + 64) are gate rows of hidden columns
-      // nt * HC + 64 w + (0..63), the next 64 the up rows of the same columns
+      // nt * HC + 64 w + (0..63), the next 64 the up rows of the same columns;
+      // one instruction's RPI rows lie in one such half
       n = nt * HC + (r >> 7) * 64 + (r & 63);
-      if (r & 64) base = p.B3;       // i odd: uniform over the block
+      if ((i * RPI) & 64) base = p.B3;
     } else {
       n = nt * BN + r;
     }
     n = min(n, N - 1);
-    b_base[i] = static_cast<const uint16_t*>(base) + static_cast<size_t>(e) * N * K;
-    b_off[i] = n * K + cq * 8;
+    b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(e) * N * K * 2);
+    b_vo[i] = static_cast<uint32_t>((n * K + cq * 8) * 2);
   }
-  auto issue = [&](int st, uint4* S) {
-    const int k0 = st * BK;
+  const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
+  // single-instruction pieces, so that the stage below can interleave them
+  auto issue_one = [&](int st, uint4* S, int q) __attribute__((always_inline)) {     // q < LD: A, else B
+    const int kb = st * BK * 2;
+    if (q < LD) dma16(a_sb + kb, a_vo[q], lds_addr(S + q * 256) + wave_lds);
+    else dma16(b_sb[q - LD] + kb, b_vo[q - LD], lds_addr(S + BOFF + (q - LD) * 256) + wave_lds);
+  };
+  auto issue = [&](int st, uint4* S) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < LD; ++i) dma16(a_base + (a_off[i] + k0), S + i * 256 + wave * 64);
-#pragma unroll
-    for (int i = 0; i < LD; ++i) dma16(b_base[i] + (b_off[i] + k0), S + BOFF + i * 256 + wave * 64);
+    for (int q = 0; q < D; ++q) issue_one(st, S, q);
+  };
+  auto read_one = [&](const uint4* S, int ks, int r, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
+    if (r < FN) {
+      uint4 v = S[BOFF + dma_swz<CH>(wn * WN + r * 32 + fr, 2 * ks + fc)];
+      fb[r] = *reinterpret_cast<bf16x8_t*>(&v);
+    } else {
+      uint4 v = S[dma_swz<CH>(wm * WM + (r - FN) * 32 + fr, 2 * ks + fc)];
+      fa[r - FN] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
   };
   auto read_frags = [&](const uint4* S, int ks, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      uint4 v = S[BOFF + swz(wn * WN + j * 32 + fr, 2 * ks + fc)];
-      fb[j] = *reinterpret_cast<bf16x8_t*>(&v);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      uint4 v = S[swz(wm * WM + i * 32 + fr, 2 * ks + fc)];
-      fa[i] = *reinterpret_cast<bf16x8_t*>(&v);
-    }
+    for (int r = 0; r < FM + FN; ++r) read_one(S, ks, r, fa, fb);
   };
 
   f32x16_t acc[FM][FN];
@@ -459,51 +518,91 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  auto mma = [&](const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  auto mma_one = [&](int q, const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) {
+    acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / FN], fb[q % FN], acc[q / FN][q % FN], 0, 0, 0);
   };
 
   bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  const int KT = K / BK;                // multiple of 4, >= 4
-  // one stage: k-step 0 (k-step 1 fragments read meanwhile), wait for the
-  // next stage and barrier, issue the stage three ahead into the slot just
-  // released, k-step 1 (next stage's first fragments read meanwhile).  The
-  // flags are compile-time: LAST = no next stage, MORE = a stage after the
-  // next one is in flight, ISSUE = a stage three ahead exists.
-  auto stage = [&](auto last, auto more, auto iss, int kt, const uint4* Sc, const uint4* Sn, uint4* Sd) {
-    read_frags(Sc, 1, fa1, fb1);
-    mma(fa0, fb0);
-    if constexpr (decltype(more)::value) wait_vmcnt<D>(); else wait_vmcnt<0>();
+  const int KT = K / BK;                // multiple of R
+  // One stage, issued in a fixed order (sched_barrier keeps the compiler from
+  // regrouping it): each MFMA is followed by at most about one other memory
+  // instruction, so the matrix pipe is fed while LDS reads and DMAs issue.
+  //   k-steps 0 .. NKS-2: MFMAs, each with one fragment read of the next
+  //   k-step (fragment sets alternate);
+  //   the first kPre MFMAs of the last k-step;
+  //   wait for stage kt + 1 (vmcnt W), barrier;
+  //   the remaining MFMAs of the last k-step, with the next stage's k-step 0
+  //   fragment reads and the DMAs of stage kt + R into this stage's slot.
+  // Compile-time flags: NEXT = a next stage exists, W = vmcnt to wait for,
+  // ISS = stage kt + R exists.
+  constexpr int NQ = FM * FN;           // MFMAs per k-step
+  constexpr int kPre = 2;
+  auto stage = [&](auto next, auto w, auto iss, int kt, uint4* Sc, const uint4* Sn) __attribute__((always_inline)) {
+    // fragment set of k-step s: s even -> fa0/fb0, s odd -> fa1/fb1
+    template_for<NKS - 1>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      auto& ca = (S & 1) ? fa1 : fa0;
+      auto& cb = (S & 1) ? fb1 : fb0;
+      auto& na = (S & 1) ? fa0 : fa1;
+      auto& nb = (S & 1) ? fb0 : fb1;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        mma_one(q, ca, cb);
+        if (q < FM + FN) read_one(Sc, S + 1, q, na, nb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+    // NKS is even: the last k-step uses fa1/fb1
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+      mma_one(q, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<decltype(w)::value>();
     lds_barrier();
-    if constexpr (decltype(iss)::value) issue(kt + 3, Sd);
-    if constexpr (!decltype(last)::value) read_frags(Sn, 0, fa0, fb0);
-    mma(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NR = decltype(next)::value ? FM + FN : 0;
+    constexpr int ND = decltype(iss)::value ? D : 0;
+    constexpr int NC = NR + ND;
+    constexpr int NM = NQ - kPre;
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      mma_one(kPre + q, fa1, fb1);
+      // spread NC companions over NM MFMAs: reads first, then DMAs
+#pragma unroll
+      for (int c = q * NC / NM; c < (q + 1) * NC / NM; ++c) {
+        if (c < NR) read_one(Sn, 0, c, fa0, fb0);
+        else issue_one(kt + R, Sc, c - NR);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  issue(0, S0);
-  issue(1, S1);
-  issue(2, S2);
-  wait_vmcnt<2 * D>();
+  template_for<R>([&](auto s) __attribute__((always_inline)) {
+    constexpr int S = decltype(s)::value;
+    issue(S, ring[S]);
+  });
+  wait_vmcnt<D * (R - 1)>();
   lds_barrier();
-  read_frags(S0, 0, fa0, fb0);
+  read_frags(ring[0], 0, fa0, fb0);
   int kt = 0;
-  for (; kt + kDmaStages < KT; kt += kDmaStages) {
-    stage(F_{}, T_{}, T_{}, kt, S0, S1, S3);
-    stage(F_{}, T_{}, T_{}, kt + 1, S1, S2, S0);
-    stage(F_{}, T_{}, T_{}, kt + 2, S2, S3, S1);
-    stage(F_{}, T_{}, T_{}, kt + 3, S3, S0, S2);
+  // steady rounds: every stage issues stage kt + R and waits with R - 2
+  // stages still in flight
+  for (; kt + R < KT; kt += R) {
+    template_for<R>([&](auto s) __attribute__((always_inline)) {
+      constexpr int S = decltype(s)::value;
+      stage(T_{}, std::integral_constant<int, D * (R - 2)>{}, T_{}, kt + S, ring[S], ring[(S + 1) % R]);
+    });
   }
-  // last round: stage KT-1 is issued in its first stage; KT-2 and KT-1 are
-  // the last ones waited for
-  stage(F_{}, T_{}, T_{}, kt, S0, S1, S3);
-  stage(F_{}, T_{}, F_{}, kt + 1, S1, S2, S0);
-  stage(F_{}, F_{}, F_{}, kt + 2, S2, S3, S1);
-  stage(T_{}, F_{}, F_{}, kt + 3, S3, S0, S2);
+  // last round: nothing more to issue; stage KT - R + s waits with
+  // R - 2 - s stages in flight
+  template_for<R>([&](auto s) __attribute__((always_inline)) {
+    constexpr int S = decltype(s)::value;
+    constexpr int W = S <= R - 2 ? D * (R - 2 - S) : 0;
+    stage(std::integral_constant<bool, (S + 1 < R)>{}, std::integral_constant<int, W>{}, F_{}, kt + S, ring[S],
+          ring[(S + 1) % R]);
+  });
 
   uint16_t* C = p.C;
   if (EPI == EPI_SWIGLU) {
@@ -541,14 +640,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   }
 }
 
-template <int EPI>
+template <int EPI, int BK>
 int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   const long n_tiles = (p.N + HC - 1) / HC;
   long blocks = n_tiles * m_tiles_max;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     p);
   return check_launch();
 }
 
@@ -584,12 +684,13 @@ int launch_epi(int epi, bool fp8, const GemmParams& p, int m_tiles_max, hipStrea
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream) {
   (void)max_rows;
   // LDS-DMA kernel: bf16 weights, a whole number of four-stage rounds, and
-  // 32-bit element offsets inside one expert's weight matrix
-  const bool dma_ok = !fp8 && p.K % (32 * kDmaStages) == 0 && static_cast<size_t>(p.N) * p.K < (size_t(1) << 31);
+  // 31-bit byte offsets inside one expert's weight matrix and one m-tile
+  const bool dma_ok = !fp8 && p.K % kDmaKMult == 0 && static_cast<size_t>(p.N) * p.K * 2 < (size_t(1) << 31) &&
+                      static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31);
   if (dma_ok) {
-    if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU>(p, m_tiles_max, stream);
-    if (epi == EPI_RELU) return launch_dma<EPI_RELU>(p, m_tiles_max, stream);
-    return launch_dma<EPI_PLAIN>(p, m_tiles_max, stream);
+    if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK>(p, m_tiles_max, stream);
+    if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK>(p, m_tiles_max, stream);
+    return launch_dma<EPI_PLAIN, kDmaBK>(p, m_tiles_max, stream);
   }
   return launch_epi<kGemmBM, 128, 1>(epi, fp8, p, m_tiles_max, stream);
 }
