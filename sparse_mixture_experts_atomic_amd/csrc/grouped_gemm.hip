@@ -395,6 +395,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// row pitch (bf16 elements) of the epilogue's 256 x 128 staging block
+constexpr int kEpPitch = 136;
+
+// silu(u) = u / (1 + e^-u) with the hardware exp2 and reciprocal (relative
+// error ~1e-7 each, far below the bf16 rounding of the result)
+__device__ __forceinline__ float silu_fast(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * u));
+}
+
 // chunk c (16 bytes) of row r of an LDS operand image with CH chunks per
 // row.  Sixteen consecutive rows read at one chunk hit 16 distinct 16-byte
 // bank groups: for CH = 4 the row sets the low two bits of the group and
@@ -422,6 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(NKS % 2 == 0, "k-steps per stage alternate two fragment sets");
   static_assert(R * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
+  static_assert(BM * kEpPitch * 2 <= R * (BM + BN) * BK * 2, "epilogue staging fits in the ring");
   static_assert(D * (R - 1) < 64, "vmcnt range");
   __shared__ uint4 ring[R][(BM + BN) * CH];
 
@@ -604,38 +614,55 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
           ring[(S + 1) % R]);
   });
 
-  uint16_t* C = p.C;
-  if (EPI == EPI_SWIGLU) {
+  // ---- epilogue through LDS: the ring is free (the last LDS reads came
+  // before the last barrier and no load is in flight).  Each pass stages a
+  // 256 x 128 bf16 block row-major (pitch kEpPitch, padded so that the two
+  // lane halves of one ds_write land in different banks), then every thread
+  // stores 16-byte pieces of whole rows.
+  //   SwiGLU: one pass, LDS column wn*64 + j*32 + fr <- silu(gate j) * up j.
+  //   Plain/ReLU: pass h takes fragments j = 2h, 2h+1 of both wavefront
+  //   columns; LDS column c maps to tile column (c/64)*128 + 64h + c%64.
+  uint16_t* ep = reinterpret_cast<uint16_t*>(&ring[0][0]);
+  constexpr int NPASS = EPI == EPI_SWIGLU ? 1 : 2;
 #pragma unroll
-    for (int j = 0; j < FN / 2; ++j) {
-      const int col = nt * HC + wn * (WN / 2) + j * 32 + fr;
-      if (col >= N) continue;
+  for (int h = 0; h < NPASS; ++h) {
+    if (h > 0) lds_barrier();              // previous pass fully read
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = EPI == EPI_SWIGLU ? jj : 2 * h + jj;
+      const int lc = wn * 64 + jj * 32 + fr;
+      float bias = 0.f;
+      if (EPI != EPI_SWIGLU && p.bias) {
+        const int col = nt * BN + wn * WN + j * 32 + fr;
+        bias = col < N ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
-          if (lr < rows_valid)
-            C[static_cast<size_t>(row0 + lr) * N + col] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + FN / 2][q]);
+          float v;
+          if (EPI == EPI_SWIGLU) {
+            v = silu_fast(acc[i][j][q]) * acc[i][j + FN / 2][q];
+          } else {
+            v = acc[i][j][q] + bias;
+            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+          }
+          ep[lr * kEpPitch + lc] = f32_to_bf16(v);
         }
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = nt * BN + wn * WN + j * 32 + fr;
-      if (col >= N) continue;
-      const float bias = p.bias ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
-          if (lr < rows_valid) {
-            float v = acc[i][j][q] + bias;
-            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-            C[static_cast<size_t>(row0 + lr) * N + col] = f32_to_bf16(v);
-          }
-        }
+    lds_barrier();
+    // 256 rows x 16 pieces of 8 columns; thread t takes piece t + 256 u
+#pragma unroll 4
+    for (int u = 0; u < 16; ++u) {
+      const int c = tid + kThreads * u;
+      const int lr = c >> 4;
+      const int pc = (c & 15) * 8;          // LDS column of the piece
+      const int col = EPI == EPI_SWIGLU ? nt * HC + pc : nt * BN + (pc >> 6) * 128 + 64 * h + (pc & 63);
+      if (lr < rows_valid && col < N) {
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * kEpPitch + pc);
+        *reinterpret_cast<uint4*>(p.C + static_cast<size_t>(row0 + lr) * N + col) = v;
+      }
     }
   }
 }
@@ -683,9 +710,10 @@ int launch_epi(int epi, bool fp8, const GemmParams& p, int m_tiles_max, hipStrea
 // a few times over, in which case 128.
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream) {
   (void)max_rows;
-  // LDS-DMA kernel: bf16 weights, a whole number of four-stage rounds, and
-  // 31-bit byte offsets inside one expert's weight matrix and one m-tile
-  const bool dma_ok = !fp8 && p.K % kDmaKMult == 0 && static_cast<size_t>(p.N) * p.K * 2 < (size_t(1) << 31) &&
+  // LDS-DMA kernel: bf16 weights, K a multiple of the ring's K per round,
+  // 16-byte output rows (N % 8 == 0), and 31-bit byte offsets inside one
+  // expert's weight matrix and one m-tile
+  const bool dma_ok = !fp8 && p.K % kDmaKMult == 0 && p.N % 8 == 0 && static_cast<size_t>(p.N) * p.K * 2 < (size_t(1) << 31) &&
                       static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31);
   if (dma_ok) {
     if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK>(p, m_tiles_max, stream);
