@@ -94,6 +94,14 @@ int launch_f32(const float* in, int in_shared, const int32_t* offsets, int E, in
 
 inline int m_tiles_max(int max_rows, int E) { return (max_rows + kGemmBM - 1) / kGemmBM + E; }
 
+// compute units of the current device (0 if it cannot be queried)
+int current_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -106,6 +114,7 @@ size_t moe_ffn_workspace_size(int kind, int act_dt, int max_rows, int E, int d, 
   (void)d_out;
   if (max_rows < 0 || E < 1) return 0;
   size_t s = align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), kWsAlign);
+  if (act_dt == MOE_BF16) s += align_up(gemm_partial_bytes(current_cu_count()), kWsAlign);
   if (kind == MOE_FFN_RELU || kind == MOE_FFN_SWIGLU) {
     const size_t esz = act_dt == MOE_F32 ? 4 : 2;
     s += align_up(static_cast<size_t>(max_rows) * static_cast<size_t>(d_ff > 0 ? d_ff : 0) * esz, kWsAlign);
@@ -151,7 +160,14 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
 
   char* ws = static_cast<char*>(workspace);
   int32_t* ts = reinterpret_cast<int32_t*>(ws);
-  void* H = ws + align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), kWsAlign);
+  ws += align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), kWsAlign);
+  const int n_cu = act_dt == MOE_BF16 ? current_cu_count() : 0;
+  float* partial = nullptr;
+  if (act_dt == MOE_BF16) {
+    partial = reinterpret_cast<float*>(ws);
+    ws += align_up(gemm_partial_bytes(n_cu), kWsAlign);
+  }
+  void* H = ws;
   const int shared_in = row_mode == MOE_ROWS_SHARED ? 1 : 0;
   const int n1 = two ? d_ff : d_out;
 
@@ -191,6 +207,9 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
   p1.C = two ? static_cast<uint16_t*>(H) : static_cast<uint16_t*>(y_rows);
   p1.N = n1;
   p1.K = d;
+  p1.partial = partial;
+  p1.n_cu = n_cu;
+  p1.split_max = kGemmSplitMax;
   const int epi1 = kind == MOE_FFN_SWIGLU ? EPI_SWIGLU : (kind == MOE_FFN_RELU ? EPI_RELU : EPI_PLAIN);
   st = launch_grouped_gemm(epi1, fp8, p1, max_rows, mtm, stream);
   if (st != MOE_OK || !two) return st;
@@ -207,6 +226,9 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
   p2.C = static_cast<uint16_t*>(y_rows);
   p2.N = d_out;
   p2.K = d_ff;
+  p2.partial = partial;
+  p2.n_cu = n_cu;
+  p2.split_max = kGemmSplitMax;
   return launch_grouped_gemm(EPI_PLAIN, fp8, p2, max_rows, mtm, stream);
 }
 

@@ -415,6 +415,161 @@ __device__ __forceinline__ int dma_swz(int r, int c) {
   return r * CH + (c ^ ((r >> SH) & (CH - 1)));
 }
 
+// Split tail.  With V tiles and n_cu CUs (one block each), the last round
+// holds rem = V % n_cu tiles and leaves the other CUs idle.  When that round
+// is at most half full, its tiles are split along K into S parts (S <= n_cu /
+// rem, <= split_max, whole stage pairs per part): tiles [0, full) run whole,
+// then rem * S blocks each accumulate one K range of one of the last rem
+// tiles into a partial buffer, and a reduction kernel sums the S parts in
+// order and applies the epilogue.  Everything is derived on the device from
+// the tile count, so no count goes back to the host.
+struct SplitPlan {
+  int full, rem, S, chunk;
+};
+
+__device__ __forceinline__ SplitPlan split_plan(int V, int KT, int R, int n_cu, int split_max) {
+  SplitPlan sp{V, 0, 1, KT};
+  if (split_max <= 1 || n_cu <= 0 || n_cu % kXcds != 0) return sp;
+  const int rem = V % n_cu;
+  if (rem == 0 || 2 * rem > n_cu) return sp;
+  int S = min(split_max, n_cu / rem);
+  S = min(S, KT / R);
+  if (S <= 1) return sp;
+  const int chunk = ((KT + S - 1) / S + R - 1) / R * R;
+  S = (KT + chunk - 1) / chunk;
+  if (S <= 1) return sp;
+  sp.full = V - rem;
+  sp.rem = rem;
+  sp.S = S;
+  sp.chunk = chunk;
+  return sp;
+}
+
+// Epilogue of a 256 x 256 tile held as 4 x 4 32x32 fragments per wavefront
+// (wavefront w owns rows 128 (w / 2) and columns 128 (w % 2); element q of a
+// fragment is row 8 (q / 4) + 4 (lane / 32) + q % 4, column lane % 32),
+// staged through LDS: each pass writes a 256 x 128 bf16 block row-major
+// (pitch kEpPitch, padded so that the two lane halves of one ds_write land in
+// different banks), then every thread stores 16-byte pieces of whole rows.
+//   SwiGLU: one pass, LDS column wn*64 + j*32 + fr <- silu(gate j) * up j.
+//   Plain/ReLU: pass h takes fragments j = 2h, 2h+1 of both wavefront
+//   columns; LDS column c maps to tile column (c/64)*128 + 64h + c%64.
+// ep must hold 256 * kEpPitch bf16 and be free of other use.
+template <int EPI>
+__device__ __forceinline__ void dma_epilogue(const f32x16_t (&acc)[4][4], uint16_t* ep, const GemmParams& p, int e,
+                                             int nt, int row0, int rows_valid) {
+  constexpr int BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
+  constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int fr = lane & 31;
+  const int fc = lane >> 5;
+  constexpr int NPASS = EPI == EPI_SWIGLU ? 1 : 2;
+#pragma unroll
+  for (int h = 0; h < NPASS; ++h) {
+    if (h > 0) lds_barrier();              // previous pass fully read
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = EPI == EPI_SWIGLU ? jj : 2 * h + jj;
+      const int lc = wn * 64 + jj * 32 + fr;
+      float bias = 0.f;
+      if (EPI != EPI_SWIGLU && p.bias) {
+        const int col = nt * BN + wn * WN + j * 32 + fr;
+        bias = col < N ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+          float v;
+          if (EPI == EPI_SWIGLU) {
+            v = silu_fast(acc[i][j][q]) * acc[i][j + FN / 2][q];
+          } else {
+            v = acc[i][j][q] + bias;
+            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+          }
+          ep[lr * kEpPitch + lc] = f32_to_bf16(v);
+        }
+    }
+    lds_barrier();
+    // 256 rows x 16 pieces of 8 columns; thread t takes piece t + 256 u
+#pragma unroll 4
+    for (int u = 0; u < 16; ++u) {
+      const int c = tid + kThreads * u;
+      const int lr = c >> 4;
+      const int pc = (c & 15) * 8;          // LDS column of the piece
+      const int col = EPI == EPI_SWIGLU ? nt * HC + pc : nt * BN + (pc >> 6) * 128 + 64 * h + (pc & 63);
+      if (lr < rows_valid && col < N) {
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * kEpPitch + pc);
+        *reinterpret_cast<uint4*>(p.C + static_cast<size_t>(row0 + lr) * N + col) = v;
+      }
+    }
+  }
+}
+
+// tile L of the grouped grid -> (segment e, n-tile nt, first row, valid rows)
+struct TileCoord {
+  int e, nt, row0, rows_valid, seg0;
+};
+__device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, int L, int m_total, int n_tiles, int BM) {
+  const int grp = L / (m_total * kNGroup);
+  const int gs = min(kNGroup, n_tiles - grp * kNGroup);
+  const int Lr = L - grp * m_total * kNGroup;
+  const int mt_g = Lr / gs;
+  TileCoord t;
+  t.nt = grp * kNGroup + Lr % gs;
+  t.e = find_segment(p.ts, p.E, mt_g);
+  t.seg0 = p.offsets[t.e];
+  t.row0 = t.seg0 + (mt_g - p.ts[t.e]) * BM;
+  t.rows_valid = min(BM, p.offsets[t.e + 1] - t.row0);
+  return t;
+}
+
+// Sum of the S K-parts of each split tile, in part order, then the epilogue.
+// One block per split tile (grid >= rem).
+template <int EPI, int BK>
+__global__ __launch_bounds__(kThreads, 1) void split_reduce_kernel(GemmParams p) {
+  constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
+  constexpr int R = BK == 32 ? 4 : 2;
+  __shared__ uint16_t ep[256 * kEpPitch];
+  const int n_tiles = (p.N + HC - 1) / HC;
+  const int m_total = p.ts[p.E];
+  const SplitPlan sp = split_plan(m_total * n_tiles, p.K / BK, R, p.n_cu, p.split_max);
+  const int r = blockIdx.x;
+  if (r >= sp.rem) return;
+  const TileCoord t = tile_coord(p, sp.full + r, m_total, n_tiles, 256);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+      for (int s = 0; s < sp.S; ++s) {
+        const float4* src = reinterpret_cast<const float4*>(
+            p.partial + static_cast<size_t>(r * sp.S + s) * (256 * 256) +
+            ((static_cast<size_t>(wave) * 16 + i * 4 + j) * 64 + lane) * 16);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 x = src[v];
+          acc[i][j][4 * v] += x.x;
+          acc[i][j][4 * v + 1] += x.y;
+          acc[i][j][4 * v + 2] += x.z;
+          acc[i][j][4 * v + 3] += x.w;
+        }
+      }
+    }
+  dma_epilogue<EPI>(acc, ep, p, t.e, t.nt, t.row0, t.rows_valid);
+}
+
 template <int EPI, int BK>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256;
@@ -438,23 +593,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   const int n_tiles = (p.N + HC - 1) / HC;
   const int m_total = p.ts[p.E];
   const int V = m_total * n_tiles;
-  const int per = (V + kXcds - 1) / kXcds;
+  const int KT = p.K / BK;              // multiple of R
+  const SplitPlan sp = split_plan(V, KT, R, p.n_cu, p.split_max);
+  const int per = (sp.full + kXcds - 1) / kXcds;
   const int b = blockIdx.x;
-  const int slot = b / kXcds;
-  if (slot >= per) return;
-  const int L = (b % kXcds) * per + slot;
-  if (L >= V) return;
-  const int grp = L / (m_total * kNGroup);
-  const int gs = min(kNGroup, n_tiles - grp * kNGroup);
-  const int Lr = L - grp * m_total * kNGroup;
-  const int mt_g = Lr / gs;
-  const int nt = grp * kNGroup + Lr % gs;
-
-  const int e = find_segment(p.ts, p.E, mt_g);
-  const int seg0 = p.offsets[e];
-  const int seg1 = p.offsets[e + 1];
-  const int row0 = seg0 + (mt_g - p.ts[e]) * BM;
-  const int rows_valid = min(BM, seg1 - row0);
+  int L, unit = -1;
+  if (b < kXcds * per) {
+    L = (b % kXcds) * per + b / kXcds;   // blocks of one XCD take a contiguous range
+    if (L >= sp.full) return;
+  } else {
+    unit = b - kXcds * per;              // split unit: tile full + unit / S, part unit % S
+    if (unit >= sp.rem * sp.S) return;
+    L = sp.full + unit / sp.S;
+  }
+  const int ks0 = unit < 0 ? 0 : (unit % sp.S) * sp.chunk;   // first stage of this block
+  const int nks = unit < 0 ? KT : min(sp.chunk, KT - ks0);    // stages (a multiple of R)
+  const TileCoord tc = tile_coord(p, L, m_total, n_tiles, BM);
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
   const int K = p.K;
   const int N = p.N;
   const int tid = threadIdx.x;
@@ -499,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
   // single-instruction pieces, so that the stage below can interleave them
   auto issue_one = [&](int st, uint4* S, int q) __attribute__((always_inline)) {     // q < LD: A, else B
-    const int kb = st * BK * 2;
+    const int kb = (ks0 + st) * BK * 2;
     if (q < LD) dma16(a_sb + kb, a_vo[q], lds_addr(S + q * 256) + wave_lds);
     else dma16(b_sb[q - LD] + kb, b_vo[q - LD], lds_addr(S + BOFF + (q - LD) * 256) + wave_lds);
   };
@@ -533,7 +688,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   };
 
   bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  const int KT = K / BK;                // multiple of R
   // One stage, issued in a fixed order (sched_barrier keeps the compiler from
   // regrouping it): each MFMA is followed by at most about one other memory
   // instruction, so the matrix pipe is fed while LDS reads and DMAs issue.
@@ -599,7 +753,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   int kt = 0;
   // steady rounds: every stage issues stage kt + R and waits with R - 2
   // stages still in flight
-  for (; kt + R < KT; kt += R) {
+  for (; kt + R < nks; kt += R) {
     template_for<R>([&](auto s) __attribute__((always_inline)) {
       constexpr int S = decltype(s)::value;
       stage(T_{}, std::integral_constant<int, D * (R - 2)>{}, T_{}, kt + S, ring[S], ring[(S + 1) % R]);
@@ -614,57 +768,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
           ring[(S + 1) % R]);
   });
 
-  // ---- epilogue through LDS: the ring is free (the last LDS reads came
-  // before the last barrier and no load is in flight).  Each pass stages a
-  // 256 x 128 bf16 block row-major (pitch kEpPitch, padded so that the two
-  // lane halves of one ds_write land in different banks), then every thread
-  // stores 16-byte pieces of whole rows.
-  //   SwiGLU: one pass, LDS column wn*64 + j*32 + fr <- silu(gate j) * up j.
-  //   Plain/ReLU: pass h takes fragments j = 2h, 2h+1 of both wavefront
-  //   columns; LDS column c maps to tile column (c/64)*128 + 64h + c%64.
-  uint16_t* ep = reinterpret_cast<uint16_t*>(&ring[0][0]);
-  constexpr int NPASS = EPI == EPI_SWIGLU ? 1 : 2;
+  if (unit >= 0) {
+    // split unit: raw accumulators to the partial buffer, in the MFMA layout
+    float* pt = p.partial + static_cast<size_t>(unit) * (BM * BN);
 #pragma unroll
-  for (int h = 0; h < NPASS; ++h) {
-    if (h > 0) lds_barrier();              // previous pass fully read
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = EPI == EPI_SWIGLU ? jj : 2 * h + jj;
-      const int lc = wn * 64 + jj * 32 + fr;
-      float bias = 0.f;
-      if (EPI != EPI_SWIGLU && p.bias) {
-        const int col = nt * BN + wn * WN + j * 32 + fr;
-        bias = col < N ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+      for (int j = 0; j < FN; ++j) {
+        float4* dst = reinterpret_cast<float4*>(pt + ((static_cast<size_t>(wave) * (FM * FN) + i * FN + j) * 64 + lane) * 16);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          dst[v] = make_float4(acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]);
       }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
-          float v;
-          if (EPI == EPI_SWIGLU) {
-            v = silu_fast(acc[i][j][q]) * acc[i][j + FN / 2][q];
-          } else {
-            v = acc[i][j][q] + bias;
-            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-          }
-          ep[lr * kEpPitch + lc] = f32_to_bf16(v);
-        }
-    }
-    lds_barrier();
-    // 256 rows x 16 pieces of 8 columns; thread t takes piece t + 256 u
-#pragma unroll 4
-    for (int u = 0; u < 16; ++u) {
-      const int c = tid + kThreads * u;
-      const int lr = c >> 4;
-      const int pc = (c & 15) * 8;          // LDS column of the piece
-      const int col = EPI == EPI_SWIGLU ? nt * HC + pc : nt * BN + (pc >> 6) * 128 + 64 * h + (pc & 63);
-      if (lr < rows_valid && col < N) {
-        const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * kEpPitch + pc);
-        *reinterpret_cast<uint4*>(p.C + static_cast<size_t>(row0 + lr) * N + col) = v;
-      }
-    }
+    return;
   }
+  // the ring is free: the last LDS reads came before the last barrier and no
+  // load is in flight
+  dma_epilogue<EPI>(acc, reinterpret_cast<uint16_t*>(&ring[0][0]), p, e, nt, row0, rows_valid);
 }
 
 template <int EPI, int BK>
@@ -673,9 +793,14 @@ int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   const long n_tiles = (p.N + HC - 1) / HC;
   long blocks = n_tiles * m_tiles_max;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  const bool split = p.split_max > 1 && p.partial && p.n_cu > 0;
+  if (split) blocks += p.n_cu;   // full + rem * S = V + rem * (S - 1) < V + n_cu
   if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                      p);
+  int st = check_launch();
+  if (st != MOE_OK || !split) return st;
+  hipLaunchKernelGGL((split_reduce_kernel<EPI, BK>), dim3(static_cast<unsigned>(p.n_cu)), dim3(kThreads), 0, stream, p);
   return check_launch();
 }
 

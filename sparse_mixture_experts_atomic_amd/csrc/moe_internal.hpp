@@ -89,7 +89,14 @@ struct GemmParams {
   uint16_t* C;               // bf16 [*, N]
   int N;                     // output columns
   int K;
+  float* partial;            // split-tail partial sums: n_cu x 256 x 256 fp32 (or null)
+  int n_cu;                  // compute units (one block of the DMA kernel each)
+  int split_max;             // most K parts of a split tile (1: no split)
 };
+
+// Bytes of the split-tail partial buffer for n_cu compute units.
+inline size_t gemm_partial_bytes(int n_cu) { return static_cast<size_t>(n_cu > 0 ? n_cu : 0) * 256 * 256 * sizeof(float); }
+constexpr int kGemmSplitMax = 4;
 
 // Enqueues C = epi(A B^T) per segment.  m_tiles_max bounds ts[E] from above.
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream);
