@@ -158,6 +158,268 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const V* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// One-launch dispatch for T*k <= kFusedMaxEntries.  Every block reads all
+// T*k expert ids (a few tens of KB, from L2) and derives from them what it
+// needs: the expert totals, their kept counts and exclusive scan (offsets),
+// and the assignments to each expert from tokens before its own range.  No
+// block depends on another, so there is no second launch and no inter-block
+// wait.  The block's rows of x are loaded into registers first, so their HBM
+// latency overlaps the index work; each row is then stored to its kept
+// slots.  Same outputs as the count/rank/permute path, bit for bit.
+// at most 63 int4 loads + 1 tail id = 253 ids per thread, so the packed 8-bit
+// per-thread counts below cannot overflow
+// Sum of v over the 64 lanes of a wavefront, valid in lane 63: quad
+// permutes, row shifts by 4 and 8, then the row-15 and row-31 broadcasts
+// (gfx9 DPP; lanes whose source is outside the row read 0).
+__device__ __forceinline__ uint32_t wave_sum_dpp(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0xb1, 0xf, 0xf, true);    // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x4e, 0xf, 0xf, true);    // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xf, 0xf, true);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xf, 0xf, true);   // row_bcast:31
+  return v;
+}
+
+constexpr int kFusedMaxEntries = 63 * 4 * 256;
+constexpr int kPackedE = 8;                    // register-packed counting for E <= 8
+constexpr int kIdPre = 8;                      // int4 id loads per thread issued before the rows
+constexpr int kFusedThreads = 256;
+
+template <int NQ>
+__global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int C, int tpb, const uint4* __restrict__ x, int nvec,
+    uint4* __restrict__ xp, int32_t* __restrict__ counts_routed, int32_t* __restrict__ counts_kept,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dest_pos, int32_t* __restrict__ perm_token) {
+  __shared__ int before[kDsMaxE];
+  __shared__ int total[kDsMaxE];
+  __shared__ int off[kDsMaxE];
+  __shared__ int ent[kFusedThreads];      // expert of the block's entries
+  __shared__ int dst[kFusedThreads];      // their destination row (-1: none)
+  __shared__ int wsum[kFusedThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t0 = blockIdx.x * tpb;
+  const int t1 = min(T, t0 + tpb);
+  const int nrow_vec = (t1 - t0) * nvec;  // 16-byte vectors of the block's rows
+
+  // 1. the first ids (loads complete in issue order, so the ids are loaded
+  //    before the rows: the counting below then waits only for them)
+  const int n_all = T * k;
+  const int n_before = t0 * k;
+  const int n4 = n_all / 4;
+  // every block reads all ids; starting each block at a different place
+  // spreads the reads of one cache line over time (counting is order-free)
+  const int rot = n4 > 0 ? static_cast<int>((static_cast<long>(blockIdx.x) * 1031) % n4) : 0;
+  int4 iv[kIdPre];
+#pragma unroll
+  for (int u = 0; u < kIdPre; ++u) {
+    const int j = tid + kFusedThreads * u;
+    int i4 = j + rot;
+    if (i4 >= n4) i4 -= n4;
+    iv[u] = j < n4 ? reinterpret_cast<const int4*>(idx)[i4] : make_int4(-1, -1, -1, -1);
+  }
+  const int nb_ent = (t1 - t0) * k;
+  const int my_ent = tid < nb_ent ? idx[static_cast<size_t>(t0) * k + tid] : -1;
+
+  // 2. the block's rows, into registers (vector q = tid + 256 u of the rows)
+  uint4 rv[NQ];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) rv[u] = make_uint4(0u, 0u, 0u, 0u);
+  if (x) {
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = tid + kFusedThreads * u;
+      if (q < nrow_vec) rv[u] = x[static_cast<size_t>(t0) * nvec + q];
+    }
+  }
+
+  // 3. expert totals and counts before t0, from all T*k ids
+  for (int e = tid; e < E; e += kFusedThreads) {
+    before[e] = 0;
+    total[e] = 0;
+  }
+  __syncthreads();
+  if (E <= kPackedE) {
+    // per-thread counts in 8-bit fields of one 64-bit word (at most 255 ids
+    // per thread), widened to 16-bit fields for the wavefront sum
+    unsigned long long tot = 0, bef = 0;
+    auto count = [&](int i, int e) __attribute__((always_inline)) {
+      const unsigned long long one = (e >= 0 && e < E) ? (1ull << (8 * e)) : 0ull;
+      tot += one;
+      bef += i < n_before ? one : 0ull;
+    };
+#pragma unroll
+    for (int u = 0; u < kIdPre; ++u) {
+      const int j = tid + kFusedThreads * u;
+      if (j < n4) {
+        int i4 = j + rot;
+        if (i4 >= n4) i4 -= n4;
+        count(4 * i4, iv[u].x);
+        count(4 * i4 + 1, iv[u].y);
+        count(4 * i4 + 2, iv[u].z);
+        count(4 * i4 + 3, iv[u].w);
+      }
+    }
+    for (int j = tid + kFusedThreads * kIdPre; j < n4; j += kFusedThreads) {
+      int i4 = j + rot;
+      if (i4 >= n4) i4 -= n4;
+      const int4 v = reinterpret_cast<const int4*>(idx)[i4];
+      count(4 * i4, v.x);
+      count(4 * i4 + 1, v.y);
+      count(4 * i4 + 2, v.z);
+      count(4 * i4 + 3, v.w);
+    }
+    for (int i = 4 * n4 + tid; i < n_all; i += kFusedThreads) count(i, idx[i]);
+    // fields 0..3 and 4..7 as 16-bit lanes of two words each
+    constexpr unsigned long long m8 = 0x00ff00ff00ff00ffull;
+    auto widen_lo = [](unsigned long long w) __attribute__((always_inline)) {
+      // bytes 0..3 -> 16-bit fields 0..3
+      unsigned long long x = w & 0xffffffffull;
+      x = (x | (x << 16)) & 0x0000ffff0000ffffull;
+      x = (x | (x << 8)) & m8;
+      return x;
+    };
+    const unsigned long long c64[4] = {widen_lo(tot), widen_lo(tot >> 32), widen_lo(bef), widen_lo(bef >> 32)};
+    // eight 32-bit words of two 16-bit fields each, summed over the wavefront
+    uint32_t c[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      c[2 * r] = wave_sum_dpp(static_cast<uint32_t>(c64[r]));
+      c[2 * r + 1] = wave_sum_dpp(static_cast<uint32_t>(c64[r] >> 32));
+    }
+    if (lane == 63) {
+#pragma unroll
+      for (int e = 0; e < kPackedE; ++e) {
+        if (e < E) {
+          // expert e: word (e >> 1) of the totals (words 4.. of the counts before)
+          atomicAdd(&total[e], static_cast<int>((c[e >> 1] >> (16 * (e & 1))) & 0xffff));
+          atomicAdd(&before[e], static_cast<int>((c[4 + (e >> 1)] >> (16 * (e & 1))) & 0xffff));
+        }
+      }
+    }
+  } else {
+    auto count = [&](int i, int e) __attribute__((always_inline)) {
+      if (e >= 0 && e < E) {
+        atomicAdd(&total[e], 1);
+        if (i < n_before) atomicAdd(&before[e], 1);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kIdPre; ++u) {
+      const int j = tid + kFusedThreads * u;
+      if (j < n4) {
+        int i4 = j + rot;
+        if (i4 >= n4) i4 -= n4;
+        count(4 * i4, iv[u].x);
+        count(4 * i4 + 1, iv[u].y);
+        count(4 * i4 + 2, iv[u].z);
+        count(4 * i4 + 3, iv[u].w);
+      }
+    }
+    for (int j = tid + kFusedThreads * kIdPre; j < n4; j += kFusedThreads) {
+      int i4 = j + rot;
+      if (i4 >= n4) i4 -= n4;
+      const int4 v = reinterpret_cast<const int4*>(idx)[i4];
+      count(4 * i4, v.x);
+      count(4 * i4 + 1, v.y);
+      count(4 * i4 + 2, v.z);
+      count(4 * i4 + 3, v.w);
+    }
+    for (int i = 4 * n4 + tid; i < n_all; i += kFusedThreads) count(i, idx[i]);
+  }
+  if (tid < nb_ent) ent[tid] = my_ent;
+  __syncthreads();
+
+  // 3. kept counts and their exclusive scan over experts (offsets)
+  if (E <= 64) {
+    if (tid == 0) {
+      int prefix = 0;
+      for (int e = 0; e < E; ++e) {
+        const int kept = C < 0 ? total[e] : min(total[e], C);
+        off[e] = prefix;
+        if (blockIdx.x == 0) {
+          counts_routed[e] = total[e];
+          counts_kept[e] = kept;
+          offsets[e] = prefix;
+        }
+        prefix += kept;
+      }
+      if (blockIdx.x == 0) offsets[E] = prefix;
+    }
+  } else {
+  const int per = (E + kFusedThreads - 1) / kFusedThreads;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int run = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int kept = C < 0 ? total[e] : min(total[e], C);
+    off[e] = kept;
+    run += kept;
+    if (blockIdx.x == 0) {
+      counts_routed[e] = total[e];
+      counts_kept[e] = kept;
+    }
+  }
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int prefix = incl - run;
+  for (int w = 0; w < wave; ++w) prefix += wsum[w];
+  for (int e = e0; e < e1; ++e) {
+    const int kept = off[e];
+    off[e] = prefix;
+    if (blockIdx.x == 0) offsets[e] = prefix;
+    prefix += kept;
+  }
+  if (blockIdx.x == 0 && e0 < E && e1 == E) offsets[E] = prefix;
+  }
+  __syncthreads();
+
+  // 4. ranks of the block's entries: assignments to the same expert from
+  //    earlier tokens (before the block, then inside it)
+  if (tid < nb_ent) {
+    const int e = ent[tid];
+    int d = -1;
+    if (e >= 0 && e < E) {
+      int r = before[e];
+      const int first_of_token = (tid / k) * k;
+      for (int i = 0; i < first_of_token; ++i) r += ent[i] == e ? 1 : 0;
+      if (C < 0 || r < C) {
+        d = off[e] + r;
+        // never true when the counts are consistent; keeps any fault out
+        if (d >= n_all) d = -1;
+        else perm_token[d] = t0 + tid / k;
+      }
+    }
+    dest_pos[static_cast<size_t>(t0) * k + tid] = d;
+    dst[tid] = d;
+  }
+  __syncthreads();
+
+  // 5. store each row to its kept slots
+  if (x) {
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = tid + kFusedThreads * u;
+      if (q < nrow_vec) {
+        const int ti = q / nvec;
+        const int v = q - ti * nvec;
+        for (int j = 0; j < k; ++j) {
+          const int d = dst[ti * k + j];
+          if (d >= 0) xp[static_cast<size_t>(d) * nvec + v] = rv[u];
+        }
+      }
+    }
+  }
+}
+
 inline int disp_blocks(int T) { return (T + kDsTok - 1) / kDsTok; }
 
 }  // namespace
@@ -199,6 +461,28 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
     hipLaunchKernelGGL(dispatch_empty_kernel, dim3(1), dim3(256), 0, stream, E, counts_routed, counts_kept, offsets);
     return check_launch();
   }
+  const size_t row_bytes = copy_rows ? static_cast<size_t>(d) * dtype_bytes(x_dt) : 0;
+  if (static_cast<long>(T) * k <= kFusedMaxEntries && row_bytes % 16 == 0) {
+    // tokens per block: at most 16 row vectors per thread, at most 256 entries,
+    // and about 512 blocks when T allows
+    const int nvec = static_cast<int>(row_bytes / 16);
+    int tpb = nvec > 0 ? (16 * kFusedThreads) / nvec : kFusedThreads;
+    tpb = min(tpb, kFusedThreads / k);
+    tpb = min(tpb, max(1, (T + 511) / 512));
+    tpb = max(tpb, 1);
+    const int nq = (tpb * nvec + kFusedThreads - 1) / kFusedThreads;
+    const int nblk = (T + tpb - 1) / tpb;
+    const uint4* xv = copy_rows ? static_cast<const uint4*>(x) : nullptr;
+    uint4* xpv = copy_rows ? static_cast<uint4*>(x_perm) : nullptr;
+#define MOE_FUSED(NQ)                                                                                            \
+  hipLaunchKernelGGL(dispatch_fused_kernel<NQ>, dim3(nblk), dim3(kFusedThreads), 0, stream, topk_idx, T, k, E,  \
+                     capacity, tpb, xv, nvec, xpv, counts_routed, counts_kept, offsets, dest_pos, perm_token)
+    if (nq <= 4) MOE_FUSED(4);
+    else if (nq <= 8) MOE_FUSED(8);
+    else MOE_FUSED(16);
+#undef MOE_FUSED
+    return check_launch();
+  }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(kDsTok), 0, stream, topk_idx, T, k, E, bc);
   int st = check_launch();
   if (st != MOE_OK) return st;
@@ -209,7 +493,6 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
   if (st != MOE_OK) return st;
   if (!copy_rows) return MOE_OK;
 
-  const size_t row_bytes = static_cast<size_t>(d) * dtype_bytes(x_dt);
   // about 2048 blocks, at least one token each
   int rows = (T + 2047) / 2048;
   if (rows < 1) rows = 1;

@@ -531,43 +531,88 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, int L, int 
 }
 
 // Sum of the S K-parts of each split tile, in part order, then the epilogue.
-// One block per split tile (grid >= rem).
+// Four blocks per split tile, one per wavefront quadrant of the GEMM block
+// (rows 128 (w / 2), columns 128 (w % 2)); thread (f, lane) of a block sums
+// fragments (i = f, j = 0..3) of that quadrant and stages its bf16 results
+// through LDS for 16-byte row stores.  Grid >= 4 * rem.
 template <int EPI, int BK>
-__global__ __launch_bounds__(kThreads, 1) void split_reduce_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   constexpr int R = BK == 32 ? 4 : 2;
-  __shared__ uint16_t ep[256 * kEpPitch];
+  constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;   // output columns of a quadrant
+  __shared__ uint16_t ep[128 * kEpPitch];
   const int n_tiles = (p.N + HC - 1) / HC;
   const int m_total = p.ts[p.E];
   const SplitPlan sp = split_plan(m_total * n_tiles, p.K / BK, R, p.n_cu, p.split_max);
-  const int r = blockIdx.x;
+  const int r = blockIdx.x >> 2;
+  const int w = blockIdx.x & 3;
   if (r >= sp.rem) return;
   const TileCoord t = tile_coord(p, sp.full + r, m_total, n_tiles, 256);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  f32x16_t acc[4][4];
+  const int fi = tid >> 6;
+  const int fr = lane & 31;
+  const int fc = lane >> 5;
+  const int wm = w >> 1, wn = w & 1;
+  f32x16_t acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[j][q] = 0.f;
+  for (int s = 0; s < sp.S; ++s) {
+    const float* base = p.partial + static_cast<size_t>(r * sp.S + s) * (256 * 256);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const float4* src = reinterpret_cast<const float4*>(base + ((static_cast<size_t>(w) * 16 + fi * 4 + j) * 64 + lane) * 16);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-      for (int s = 0; s < sp.S; ++s) {
-        const float4* src = reinterpret_cast<const float4*>(
-            p.partial + static_cast<size_t>(r * sp.S + s) * (256 * 256) +
-            ((static_cast<size_t>(wave) * 16 + i * 4 + j) * 64 + lane) * 16);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float4 x = src[v];
-          acc[i][j][4 * v] += x.x;
-          acc[i][j][4 * v + 1] += x.y;
-          acc[i][j][4 * v + 2] += x.z;
-          acc[i][j][4 * v + 3] += x.w;
-        }
+      for (int v = 0; v < 4; ++v) {
+        const float4 x = src[v];
+        acc[j][4 * v] += x.x;
+        acc[j][4 * v + 1] += x.y;
+        acc[j][4 * v + 2] += x.z;
+        acc[j][4 * v + 3] += x.w;
       }
     }
-  dma_epilogue<EPI>(acc, ep, p, t.e, t.nt, t.row0, t.rows_valid);
+  }
+  // quadrant rows fi*32 + 8 (q/4) + 4 fc + q%4; LDS column = output column
+  // of the quadrant
+  const int N = p.N;
+#pragma unroll
+  for (int jj = 0; jj < (EPI == EPI_SWIGLU ? 2 : 4); ++jj) {
+    const int lc = jj * 32 + fr;
+    float bias = 0.f;
+    if (EPI != EPI_SWIGLU && p.bias) {
+      const int col = t.nt * 256 + wn * 128 + lc;
+      bias = col < N ? p.bias[static_cast<size_t>(t.e) * N + col] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int lr = fi * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+      float v;
+      if (EPI == EPI_SWIGLU) {
+        v = silu_fast(acc[jj][q]) * acc[jj + 2][q];
+      } else {
+        v = acc[jj][q] + bias;
+        if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+      }
+      ep[lr * kEpPitch + lc] = f32_to_bf16(v);
+    }
+  }
+  __syncthreads();
+  constexpr int PR = OC / 8;                 // 16-byte pieces per row
+  const int col0 = EPI == EPI_SWIGLU ? t.nt * HC + wn * 64 : t.nt * 256 + wn * 128;
+  const int row_base = wm * 128;
+#pragma unroll
+  for (int u = 0; u < 128 * PR / kThreads; ++u) {
+    const int c = tid + kThreads * u;
+    const int lr = c / PR;
+    const int pc = (c % PR) * 8;
+    const int col = col0 + pc;
+    if (row_base + lr < t.rows_valid && col < N) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * kEpPitch + pc);
+      *reinterpret_cast<uint4*>(p.C + static_cast<size_t>(t.row0 + row_base + lr) * N + col) = v;
+    }
+  }
 }
 
 template <int EPI, int BK>
@@ -793,14 +838,19 @@ int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   const long n_tiles = (p.N + HC - 1) / HC;
   long blocks = n_tiles * m_tiles_max;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-  const bool split = p.split_max > 1 && p.partial && p.n_cu > 0;
+  // the tail can matter only for a grid of a few rounds; otherwise no split
+  // (and no reduction launch)
+  const bool split = p.split_max > 1 && p.partial && p.n_cu > 0 && n_tiles * m_tiles_max <= 4L * p.n_cu;
   if (split) blocks += p.n_cu;   // full + rem * S = V + rem * (S - 1) < V + n_cu
   if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
+  GemmParams q = p;
+  if (!split) q.split_max = 1;
   hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                     p);
+                     q);
   int st = check_launch();
   if (st != MOE_OK || !split) return st;
-  hipLaunchKernelGGL((split_reduce_kernel<EPI, BK>), dim3(static_cast<unsigned>(p.n_cu)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((split_reduce_kernel<EPI, BK>), dim3(static_cast<unsigned>(4 * p.n_cu)), dim3(kThreads), 0, stream,
+                     p);
   return check_launch();
 }
 
