@@ -98,84 +98,74 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_ro
   reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
 }
 
-// k <= 4: each thread handles one vector of kCbTpb consecutive tokens and
-// issues every slot's row load (and the residual loads) before any
-// arithmetic, so many loads are in flight per thread.  Same fixed
-// accumulation order per token as combine_kernel.
-constexpr int kCbTpb = 4;
-template <typename T, int VW>
-__global__ __launch_bounds__(256) void combine_k4_kernel(const T* __restrict__ y_rows, const int32_t* __restrict__ dest_pos,
-                                                        const float* __restrict__ gate, int T_, int k, int nvec,
+// k known at compile time (1, 2, 4 or 8): one thread per 16-byte output
+// vector of one token (grid y = token); the K slot rows are loaded together,
+// then accumulated in slot order (dropped slots skipped), then the shared
+// experts and the residual, as in combine_kernel.
+template <typename T, int VW, int K>
+__global__ __launch_bounds__(256) void combine_kk_kernel(const T* __restrict__ y_rows, const int32_t* __restrict__ dest_pos,
+                                                        const float* __restrict__ gate, int T_, int nvec,
                                                         const T* __restrict__ shared_y, int n_shared,
                                                         const T* __restrict__ residual, T* __restrict__ y) {
   using V = typename Vec<T, VW>::type;
-  const int tb = blockIdx.y * kCbTpb;
+  const int t = blockIdx.y;
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= nvec) return;
   const V* yr = reinterpret_cast<const V*>(y_rows);
-  V rv[kCbTpb][4];
-  int d[kCbTpb][4];
+  int d[K];
+  V rv[K];
 #pragma unroll
-  for (int i = 0; i < kCbTpb; ++i) {
-    const int t = tb + i;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      d[i][u] = (t < T_ && u < k) ? dest_pos[static_cast<size_t>(t) * k + u] : -1;
-      if (d[i][u] >= 0) rv[i][u] = yr[static_cast<size_t>(d[i][u]) * nvec + v];
-    }
+  for (int u = 0; u < K; ++u) {
+    d[u] = dest_pos[static_cast<size_t>(t) * K + u];
+    if (d[u] >= 0) rv[u] = yr[static_cast<size_t>(d[u]) * nvec + v];
   }
-  V rres[kCbTpb];
+  float acc[VW];
+#pragma unroll
+  for (int c = 0; c < VW; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int u = 0; u < K; ++u) {
+    if (d[u] < 0) continue;
+    const float g = gate[static_cast<size_t>(t) * K + u];
+    float f[VW];
+    Vec<T, VW>::unpack(rv[u], f);
+#pragma unroll
+    for (int c = 0; c < VW; ++c) acc[c] = fmaf(g, f[c], acc[c]);
+  }
+  const V* sy = reinterpret_cast<const V*>(shared_y);
+  for (int sI = 0; sI < n_shared; ++sI) {
+    float f[VW];
+    Vec<T, VW>::unpack(sy[(static_cast<size_t>(sI) * T_ + t) * nvec + v], f);
+#pragma unroll
+    for (int c = 0; c < VW; ++c) acc[c] += f[c];
+  }
   if (residual) {
+    float f[VW];
+    Vec<T, VW>::unpack(reinterpret_cast<const V*>(residual)[static_cast<size_t>(t) * nvec + v], f);
 #pragma unroll
-    for (int i = 0; i < kCbTpb; ++i)
-      if (tb + i < T_) rres[i] = reinterpret_cast<const V*>(residual)[static_cast<size_t>(tb + i) * nvec + v];
+    for (int c = 0; c < VW; ++c) acc[c] += f[c];
   }
-#pragma unroll
-  for (int i = 0; i < kCbTpb; ++i) {
-    const int t = tb + i;
-    if (t >= T_) break;
-    float acc[VW];
-#pragma unroll
-    for (int c = 0; c < VW; ++c) acc[c] = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (d[i][u] < 0) continue;
-      const float g = gate[static_cast<size_t>(t) * k + u];
-      float f[VW];
-      Vec<T, VW>::unpack(rv[i][u], f);
-#pragma unroll
-      for (int c = 0; c < VW; ++c) acc[c] = fmaf(g, f[c], acc[c]);
-    }
-    const V* sy = reinterpret_cast<const V*>(shared_y);
-    for (int sI = 0; sI < n_shared; ++sI) {
-      float f[VW];
-      Vec<T, VW>::unpack(sy[(static_cast<size_t>(sI) * T_ + t) * nvec + v], f);
-#pragma unroll
-      for (int c = 0; c < VW; ++c) acc[c] += f[c];
-    }
-    if (residual) {
-      float f[VW];
-      Vec<T, VW>::unpack(rres[i], f);
-#pragma unroll
-      for (int c = 0; c < VW; ++c) acc[c] += f[c];
-    }
-    reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
-  }
+  reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
 }
 
 template <typename T, int VW>
 int launch_combine(const void* y_rows, const int32_t* dest_pos, const float* gate, int T_, int k, int d_out,
                    const void* shared_y, int n_shared, const void* residual, void* y, hipStream_t stream) {
   const int nvec = d_out / VW;
-  if (k <= 4) {
-    // grid: (vector blocks of a row, groups of kCbTpb tokens)
-    hipLaunchKernelGGL((combine_k4_kernel<T, VW>), dim3((nvec + 255) / 256, (T_ + kCbTpb - 1) / kCbTpb), dim3(256), 0,
-                       stream, static_cast<const T*>(y_rows), dest_pos, gate, T_, k, nvec,
-                       static_cast<const T*>(shared_y), n_shared, static_cast<const T*>(residual), static_cast<T*>(y));
-    return check_launch();
+  const dim3 grid((nvec + 255) / 256, T_);   // (vector blocks of a row, tokens)
+#define MOE_CB_K(KK)                                                                                          \
+  hipLaunchKernelGGL((combine_kk_kernel<T, VW, KK>), grid, dim3(256), 0, stream, static_cast<const T*>(y_rows), \
+                     dest_pos, gate, T_, nvec, static_cast<const T*>(shared_y), n_shared,                      \
+                     static_cast<const T*>(residual), static_cast<T*>(y));                                    \
+  return check_launch()
+  switch (k) {
+    case 1: MOE_CB_K(1);
+    case 2: MOE_CB_K(2);
+    case 4: MOE_CB_K(4);
+    case 8: MOE_CB_K(8);
+    default: break;
   }
-  // grid: (vector blocks of a row, tokens)
-  hipLaunchKernelGGL((combine_kernel<T, VW>), dim3((nvec + 255) / 256, T_), dim3(256), 0, stream,
+#undef MOE_CB_K
+  hipLaunchKernelGGL((combine_kernel<T, VW>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(y_rows), dest_pos, gate, T_, k, nvec, static_cast<const T*>(shared_y),
                      n_shared, static_cast<const T*>(residual), static_cast<T*>(y));
   return check_launch();
