@@ -174,96 +174,94 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
   }
 }
 
-// Streaming router for few experts (E <= 8) and bf16 activations, d <= 4096.
-// The work is bound by reading x once, so each thread keeps the fp32 router
-// weights of its NC column chunks (8 columns each) in registers for the
-// whole block and streams tokens four at a time: one 16-byte load per token
-// and chunk, 8*E FMAs.  Per-token partial dot products are reduced across the
-// wavefront by a reduce-scatter of shuffles and across the 4 wavefronts in
-// LDS, then one thread per token does the fp32 softmax and top-k.
+// Streaming router for few experts (E <= 8), bf16 activations, d % 8 == 0,
+// d <= 4096.  The work is bound by reading x once.  A block of 512 threads is
+// split into token lanes of TPR threads; thread c of a lane keeps the fp32
+// router weights of column chunk c (8 columns x 8 experts) in registers and
+// streams the lane's tokens in halves of kSmTph: one 16-byte load and 64 FMAs
+// per token, the next half's loads in flight while the current half is
+// reduced.  The kSmTph x 8 per-thread partial logits of a half are
+// reduce-scattered over the wavefront (each lane ends with one sum), the
+// TPR / 64 wavefronts of a lane are added in LDS in a fixed order, and one
+// thread per token does the fp32 softmax and top-k.  Per-block probability
+// column sums go to the workspace for colsum_reduce_kernel.
 constexpr int kSmE = 8;
-constexpr int kSmTok = 4;     // tokens per group
-constexpr int kSmThreads = 256;
+constexpr int kSmThreads = 512;
+constexpr int kSmTph = 8;                     // tokens per thread and half
+constexpr int kSmHalves = 2;
+constexpr int kSmTpt = kSmTph * kSmHalves;    // tokens per thread
+constexpr int kSmNv = kSmTph * kSmE;          // partial logits per thread and half (64)
 
-template <int NC>
-__global__ __launch_bounds__(kSmThreads) void router_small_e_kernel(RouterArgs a, int groups_per_block) {
-  __shared__ float red[kSmThreads / 64][kSmTok * kSmE];
-  __shared__ float lg[kSmTok][kSmE];
-  __shared__ float colsum[kSmE];
+template <int TPR>
+__global__ __launch_bounds__(kSmThreads) void router_stream_kernel(RouterArgs a) {
+  constexpr int G = kSmThreads / TPR;         // token lanes per block
+  constexpr int WPL = TPR / 64;               // wavefronts per token lane
+  constexpr int TPB = G * kSmTpt;             // tokens per block
+  static_assert(kSmNv == 64, "one reduced value per lane");
+  __shared__ float wred[kSmHalves][kSmThreads / 64][kSmNv];
+  __shared__ float lg[TPB][kSmE];
+  __shared__ float pr[TPB][kSmE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int c = tid % TPR;                    // column chunk
+  const int g = tid / TPR;                    // token lane
   const int nchunk = a.d / 8;
+  const int t0 = blockIdx.x * TPB;
+  const int tl0 = t0 + g * kSmTpt;            // first token of this lane
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  if (tid < kSmE) colsum[tid] = 0.f;
+  const bool cv = c < nchunk;
 
-  // router weights of this thread's chunks: w[j][e][c]
-  float w[NC][kSmE][8];
+  auto load_half = [&](int h, uint4 (&dst)[kSmTph]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int ch = tid + kSmThreads * j;
+    for (int i = 0; i < kSmTph; ++i) {
+      const int t = tl0 + h * kSmTph + i;
+      dst[i] = (cv && t < a.T) ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * a.d + c * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 xa[kSmTph], xb[kSmTph];
+  load_half(0, xa);
+  float w[kSmE][8];
 #pragma unroll
-    for (int e = 0; e < kSmE; ++e) {
-      if (ch < nchunk && e < a.E) {
-        const float4 lo = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + ch * 8);
-        const float4 hi = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + ch * 8 + 4);
-        w[j][e][0] = lo.x; w[j][e][1] = lo.y; w[j][e][2] = lo.z; w[j][e][3] = lo.w;
-        w[j][e][4] = hi.x; w[j][e][5] = hi.y; w[j][e][6] = hi.z; w[j][e][7] = hi.w;
-      } else {
+  for (int e = 0; e < kSmE; ++e) {
+    if (cv && e < a.E) {
+      const float4 lo = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + c * 8);
+      const float4 hi = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + c * 8 + 4);
+      w[e][0] = lo.x; w[e][1] = lo.y; w[e][2] = lo.z; w[e][3] = lo.w;
+      w[e][4] = hi.x; w[e][5] = hi.y; w[e][6] = hi.z; w[e][7] = hi.w;
+    } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) w[j][e][c] = 0.f;
-      }
+      for (int q = 0; q < 8; ++q) w[e][q] = 0.f;
     }
   }
-
-  const int g0 = blockIdx.x * groups_per_block;
-  const int g1 = min(g0 + groups_per_block, (a.T + kSmTok - 1) / kSmTok);
-  // x of the next token group is loaded while the current one is reduced
-  uint4 xv[kSmTok][NC], xn[kSmTok][NC];
-  auto load_group = [&](int g, uint4 (&dst)[kSmTok][NC]) {
+  load_half(1, xb);
+  auto half = [&](int h, const uint4 (&xv)[kSmTph]) __attribute__((always_inline)) {
+    float v[kSmNv];                           // entry i * 8 + e
 #pragma unroll
-    for (int t = 0; t < kSmTok; ++t)
+    for (int i = 0; i < kSmTph; ++i) {
+      const uint32_t q[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+      float xf[8];
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int ch = tid + kSmThreads * j;
-        const int tt = g * kSmTok + t;
-        dst[t][j] = (ch < nchunk && tt < a.T)
-                        ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(tt) * a.d + ch * 8)
-                        : make_uint4(0u, 0u, 0u, 0u);
+      for (int m = 0; m < 4; ++m) {
+        xf[2 * m] = __uint_as_float(q[m] << 16);
+        xf[2 * m + 1] = __uint_as_float(q[m] & 0xffff0000u);
       }
-  };
-  if (g0 < g1) load_group(g0, xv);
-  for (int g = g0; g < g1; ++g) {
-    const int t0 = g * kSmTok;
-    if (g + 1 < g1) load_group(g + 1, xn);
-    float acc[kSmTok * kSmE];
 #pragma unroll
-    for (int i = 0; i < kSmTok * kSmE; ++i) acc[i] = 0.f;
+      for (int e = 0; e < kSmE; ++e) {
+        float s = 0.f;
 #pragma unroll
-    for (int t = 0; t < kSmTok; ++t)
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const uint32_t q[4] = {xv[t][j].x, xv[t][j].y, xv[t][j].z, xv[t][j].w};
-        float xf[8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          xf[2 * c] = __uint_as_float(q[c] << 16);
-          xf[2 * c + 1] = __uint_as_float(q[c] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int e = 0; e < kSmE; ++e)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[t * kSmE + e] = fmaf(xf[c], w[j][e][c], acc[t * kSmE + e]);
+        for (int m = 0; m < 8; ++m) s = fmaf(xf[m], w[e][m], s);
+        v[i * kSmE + e] = s;
       }
-    // reduce-scatter over the wavefront: after the rounds on lane bits 5..1,
-    // lane l holds entry l >> 1 summed over the 32 lanes that share bit 0
-    float v[32];
+    }
+    // reduce-scatter over the wavefront: in the round with partner lane ^ o
+    // the lane keeps the upper half of its entries if (lane & o), so after
+    // the six rounds lane l holds entry l summed over all 64 lanes
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = acc[i];
-#pragma unroll
-    for (int r = 0; r < 5; ++r) {
+    for (int r = 0; r < 6; ++r) {
       const int o = 32 >> r;
-      const int n = 16 >> r;
+      const int n = kSmNv >> (r + 1);
       const bool upper = (lane & o) != 0;
 #pragma unroll
       for (int i = 0; i < n; ++i) {
@@ -272,21 +270,31 @@ __global__ __launch_bounds__(kSmThreads) void router_small_e_kernel(RouterArgs a
         v[i] = keep + __shfl_xor(send, o);
       }
     }
-    v[0] += __shfl_xor(v[0], 1);
-    if ((lane & 1) == 0) red[wave][lane >> 1] = v[0];
-    __syncthreads();
-    if (tid < kSmTok * kSmE) {
-      const float s = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-      const int t = tid / kSmE, e = tid % kSmE;
-      lg[t][e] = s + ((a.b_g && e < a.E) ? a.b_g[e] : 0.f);
-    }
-    __syncthreads();
-    if (tid < kSmTok && t0 + tid < a.T) {
-      const int t = t0 + tid;
-      const float* z = lg[tid];
+    wred[h][wave][lane] = v[0];
+  };
+  half(0, xa);
+  half(1, xb);
+  __syncthreads();
+  // logits: token lane gg, half h, entry en = i * 8 + e, summed over the
+  // lane's wavefronts
+  for (int j = tid; j < kSmHalves * G * kSmNv; j += kSmThreads) {
+    const int h = j / (G * kSmNv);
+    const int gg = (j / kSmNv) % G, en = j % kSmNv;
+    float sum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < WPL; ++ww) sum += wred[h][gg * WPL + ww][en];
+    const int e = en % kSmE;
+    lg[gg * kSmTpt + h * kSmTph + en / kSmE][e] = sum + ((a.b_g && e < a.E) ? a.b_g[e] : 0.f);
+  }
+  __syncthreads();
+  if (tid < TPB) {
+    const int t = t0 + tid;
+    const float* z = lg[tid];
+    float p[kSmE];
+    for (int e = 0; e < kSmE; ++e) p[e] = 0.f;
+    if (t < a.T) {
       float m = -INFINITY;
       for (int e = 0; e < a.E; ++e) m = fmaxf(m, z[e]);
-      float p[kSmE];
       float s = 0.f;
       for (int e = 0; e < a.E; ++e) { p[e] = expf(z[e] - m); s += p[e]; }
       const float inv = 1.0f / s;
@@ -313,23 +321,16 @@ __global__ __launch_bounds__(kSmThreads) void router_small_e_kernel(RouterArgs a
         a.topk_idx[static_cast<size_t>(t) * a.k + j] = is[j];
         a.topk_gate[static_cast<size_t>(t) * a.k + j] = a.mode == MOE_GATE_RENORM ? ps[j] / psum : ps[j];
       }
-      for (int e = 0; e < a.E; ++e) red[0][tid * kSmE + e] = p[e];
     }
-    __syncthreads();
-    // block column sums in token order (deterministic)
-    if (tid < a.E) {
-      float cs = colsum[tid];
-      for (int t = 0; t < kSmTok; ++t)
-        if (t0 + t < a.T) cs += red[0][t * kSmE + tid];
-      colsum[tid] = cs;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < kSmTok; ++t)
-#pragma unroll
-      for (int j = 0; j < NC; ++j) xv[t][j] = xn[t][j];
+    for (int e = 0; e < kSmE; ++e) pr[tid][e] = p[e];
   }
-  if (tid < a.E) a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + tid] = colsum[tid];
+  __syncthreads();
+  // block column sums in token order
+  if (tid < a.E) {
+    float cs = 0.f;
+    for (int i = 0; i < TPB; ++i) cs += pr[i][tid];
+    a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + tid] = cs;
+  }
 }
 
 // prob_colsum[e] = sum over blocks of the partial sums.  One block per
@@ -351,11 +352,22 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* part, i
 
 inline int router_blocks(int T) { return (T + kRtTok - 1) / kRtTok; }
 
+// block count of the streaming kernel for d columns (threads per token
+// lane: a power of two >= 64 covering the d/8 chunks)
+inline int stream_tpr(int d) {
+  int tpr = 64;
+  while (tpr < d / 8) tpr *= 2;
+  return tpr;
+}
+inline int stream_blocks(int T, int d) {
+  const int tpb = (kSmThreads / stream_tpr(d)) * kSmTpt;
+  return (T + tpb - 1) / tpb;
+}
+
 // upper bound of the block count of either router kernel (per-block
 // probability partial sums live in the workspace)
 inline int router_max_blocks(int T) {
-  const int groups = (T + kSmTok - 1) / kSmTok;
-  const int small = groups < 1024 ? groups : 1024;
+  const int small = (T + kSmTpt - 1) / kSmTpt;   // stream kernel: at least kSmTpt tokens per block
   const int generic = router_blocks(T);
   return small > generic ? small : generic;
 }
@@ -371,7 +383,7 @@ size_t moe_router_workspace_size(int T, int d, int E, int x_dt) {
   (void)d;
   (void)x_dt;
   if (T < 0 || E < 1) return 0;
-  return align_up(static_cast<size_t>(router_max_blocks(T)) * E * sizeof(float), kWsAlign) + kWsAlign;
+  return align_up(static_cast<size_t>(router_max_blocks(T)) * E * sizeof(float), kWsAlign);
 }
 
 int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g, int T, int d, int E,
@@ -390,24 +402,24 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
   if (prob_colsum && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
 
-  const bool small = x_dt == MOE_BF16 && E <= kSmE && d % 8 == 0 && d <= 2 * 8 * kSmThreads;
-  int nb = router_blocks(T);
-  int groups_per_block = 1;
-  if (small && T > 0) {
-    const int groups = (T + kSmTok - 1) / kSmTok;
-    groups_per_block = groups >= 1024 ? 2 * ((groups + 2047) / 2048) : 1;   // about 512-1024 blocks
-    nb = (groups + groups_per_block - 1) / groups_per_block;
-  }
+  const bool small = x_dt == MOE_BF16 && E <= kSmE && d % 8 == 0 && d <= 8 * kSmThreads;
   float* part = static_cast<float*>(workspace);
+  const int nb = small ? stream_blocks(T, d) : router_blocks(T);
   if (T > 0 && small) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
-    if (d <= 8 * kSmThreads)
-      hipLaunchKernelGGL(router_small_e_kernel<1>, dim3(nb), dim3(kSmThreads), 0, stream, a, groups_per_block);
+    const int tpr = stream_tpr(d);
+    if (tpr == 64)
+      hipLaunchKernelGGL(router_stream_kernel<64>, dim3(nb), dim3(kSmThreads), 0, stream, a);
+    else if (tpr == 128)
+      hipLaunchKernelGGL(router_stream_kernel<128>, dim3(nb), dim3(kSmThreads), 0, stream, a);
+    else if (tpr == 256)
+      hipLaunchKernelGGL(router_stream_kernel<256>, dim3(nb), dim3(kSmThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(router_small_e_kernel<2>, dim3(nb), dim3(kSmThreads), 0, stream, a, groups_per_block);
+      hipLaunchKernelGGL(router_stream_kernel<512>, dim3(nb), dim3(kSmThreads), 0, stream, a);
     int st = check_launch();
     if (st != MOE_OK) return st;
-  } else if (T > 0) {
+  }
+  if (T > 0 && !small) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
     size_t lds = (static_cast<size_t>(kRtDc) * kRtTok + static_cast<size_t>(kRtDc) * kRtExp +
                   static_cast<size_t>(kRtTok) * E + 4 * static_cast<size_t>(E)) * sizeof(float);

@@ -56,7 +56,7 @@ class MoELayer:
 
     @staticmethod
     def _ws(n: int, dev) -> torch.Tensor:
-        return torch.empty((max(int(n), 256),), dtype=torch.uint8, device=dev)
+        return torch.zeros((max(int(n), 256),), dtype=torch.uint8, device=dev)
 
     # individual stages (the tests drive them one at a time) ----------------
     def router(self, x):
