@@ -733,31 +733,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   };
 
   bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  // One stage, issued in a fixed order (sched_barrier keeps the compiler from
-  // regrouping it): each MFMA is followed by at most about one other memory
-  // instruction, so the matrix pipe is fed while LDS reads and DMAs issue.
-  //   k-steps 0 .. NKS-2: MFMAs, each with one fragment read of the next
-  //   k-step (fragment sets alternate);
-  //   the first kPre MFMAs of the last k-step;
-  //   wait for stage kt + 1 (vmcnt W), barrier;
-  //   the remaining MFMAs of the last k-step, with the next stage's k-step 0
-  //   fragment reads and the DMAs of stage kt + R into this stage's slot.
-  // Compile-time flags: NEXT = a next stage exists, W = vmcnt to wait for,
-  // ISS = stage kt + R exists.
+  // One stage (ring of two 64-deep slots), issued in a fixed order
+  // (sched_barrier keeps the compiler from regrouping it); each MFMA is
+  // followed by about one LDS read or DMA, so the matrix pipe is fed while
+  // they issue:
+  //   k-step 0: MFMAs with the k-step-1 fragment reads and the second half
+  //             of the DMAs of stage kt + 1 (into the other slot);
+  //   k-steps 1, 2: MFMAs with the next k-step's fragment reads;
+  //   the first kPre k-step-3 MFMAs; wait for stage kt + 1 (vmcnt(0): only
+  //   its DMAs are in flight), barrier (this slot is now free);
+  //   k-step 3: the remaining MFMAs with the next stage's k-step-0 fragment
+  //   reads and the first half of the DMAs of stage kt + 2 into this slot.
+  // Splitting a stage's 16 DMAs over two places keeps them from queueing up
+  // behind each other; the later half still has about three k-steps to land.
+  // Compile-time flags: NEXT = stage kt + 1 exists, ISSA = stage kt + 2
+  // exists (first half issued here), ISSB = the second half of stage kt + 1
+  // is issued here (every stage after the first two).
+  static_assert(R == 2 && NKS == 4, "the stage schedule below is written for two 64-deep slots");
   constexpr int NQ = FM * FN;           // MFMAs per k-step
   constexpr int kPre = 2;
-  auto stage = [&](auto next, auto w, auto iss, int kt, uint4* Sc, const uint4* Sn) __attribute__((always_inline)) {
-    // fragment set of k-step s: s even -> fa0/fb0, s odd -> fa1/fb1
+  constexpr int DH = D / 2;             // DMAs per half stage
+  auto stage = [&](auto next, auto issa, auto issb, int kt, uint4* Sc, uint4* Sn) __attribute__((always_inline)) {
     template_for<NKS - 1>([&](auto sc) __attribute__((always_inline)) {
       constexpr int S = decltype(sc)::value;
       auto& ca = (S & 1) ? fa1 : fa0;
       auto& cb = (S & 1) ? fb1 : fb0;
       auto& na = (S & 1) ? fa0 : fa1;
       auto& nb = (S & 1) ? fb0 : fb1;
+      constexpr int NB = (S == 0 && decltype(issb)::value) ? DH : 0;
+      constexpr int NC = FM + FN + NB;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         mma_one(q, ca, cb);
-        if (q < FM + FN) read_one(Sc, S + 1, q, na, nb);
+#pragma unroll
+        for (int c = q * NC / NQ; c < (q + 1) * NC / NQ; ++c) {
+          if (c < FM + FN) read_one(Sc, S + 1, c, na, nb);
+          else issue_one(kt + 1, Sn, DH + (c - FM - FN));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     });
@@ -767,11 +779,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       mma_one(q, fa1, fb1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<decltype(w)::value>();
+    wait_vmcnt<0>();
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
     constexpr int NR = decltype(next)::value ? FM + FN : 0;
-    constexpr int ND = decltype(iss)::value ? D : 0;
+    constexpr int ND = decltype(issa)::value ? DH : 0;
     constexpr int NC = NR + ND;
     constexpr int NM = NQ - kPre;
 #pragma unroll
@@ -781,37 +793,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
 #pragma unroll
       for (int c = q * NC / NM; c < (q + 1) * NC / NM; ++c) {
         if (c < NR) read_one(Sn, 0, c, fa0, fb0);
-        else issue_one(kt + R, Sc, c - NR);
+        else issue_one(kt + 2, Sc, c - NR);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  template_for<R>([&](auto s) __attribute__((always_inline)) {
-    constexpr int S = decltype(s)::value;
-    issue(S, ring[S]);
-  });
-  wait_vmcnt<D * (R - 1)>();
+  // prologue: stages 0 and 1 in full, wait for stage 0
+  issue(0, ring[0]);
+  issue(1, ring[1]);
+  wait_vmcnt<D>();
   lds_barrier();
   read_frags(ring[0], 0, fa0, fb0);
-  int kt = 0;
-  // steady rounds: every stage issues stage kt + R and waits with R - 2
-  // stages still in flight
-  for (; kt + R < nks; kt += R) {
-    template_for<R>([&](auto s) __attribute__((always_inline)) {
-      constexpr int S = decltype(s)::value;
-      stage(T_{}, std::integral_constant<int, D * (R - 2)>{}, T_{}, kt + S, ring[S], ring[(S + 1) % R]);
-    });
+  if (nks == R) {
+    stage(T_{}, F_{}, F_{}, 0, ring[0], ring[1]);
+    stage(F_{}, F_{}, F_{}, 1, ring[1], ring[0]);
+  } else {
+    // first round: stage 1's second half was issued in the prologue
+    stage(T_{}, T_{}, F_{}, 0, ring[0], ring[1]);
+    stage(T_{}, T_{}, T_{}, 1, ring[1], ring[0]);
+    int kt = R;
+    for (; kt + R < nks; kt += R) {
+      stage(T_{}, T_{}, T_{}, kt, ring[0], ring[1]);
+      stage(T_{}, T_{}, T_{}, kt + 1, ring[1], ring[0]);
+    }
+    // last round: nothing left to issue but the second half of the last stage
+    stage(T_{}, F_{}, T_{}, kt, ring[0], ring[1]);
+    stage(F_{}, F_{}, F_{}, kt + 1, ring[1], ring[0]);
   }
-  // last round: nothing more to issue; stage KT - R + s waits with
-  // R - 2 - s stages in flight
-  template_for<R>([&](auto s) __attribute__((always_inline)) {
-    constexpr int S = decltype(s)::value;
-    constexpr int W = S <= R - 2 ? D * (R - 2 - S) : 0;
-    stage(std::integral_constant<bool, (S + 1 < R)>{}, std::integral_constant<int, W>{}, F_{}, kt + S, ring[S],
-          ring[(S + 1) % R]);
-  });
 
   if (unit >= 0) {
     // split unit: raw accumulators to the partial buffer, in the MFMA layout
