@@ -324,21 +324,16 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
 
 // ---------------------------------------------------------------------------
 // bf16 weights, K % 128 == 0: operands go global -> LDS with
-// global_load_lds_dwordx4 (no staging registers, no ds_write), through a ring
-// of R stages of BK columns of K: R = 4 for BK = 32, R = 2 for BK = 64; the
-// ring is 128 KB either way.  Block tile 256 x 256, four wavefronts of
-// 128 x 128 (one wavefront per SIMD, accumulators in AGPRs).
-//
-// A stage's slot is free as soon as the barrier in the middle of that stage
-// has passed (every wavefront has read its last k-step by then; the k-step 0
-// of a stage is read during the previous one).  So stage j + R is issued into
-// slot j right after that barrier, and stage j + 1 is waited for (vmcnt, then
-// the barrier) in the middle of stage j: R - 1 stages of load latency are
-// hidden.  The LDS image of a stage is a swizzled row-major layout (see
-// dma_swz); a DMA lane writes slot base + lane, so each lane fetches the
-// global chunk that belongs in its slot.
+// global_load_lds_dwordx4 (no staging registers, no ds_write) in stages of 64
+// columns of K, so that every DMA lane group reads whole 128-byte rows: the
+// DMA path serves a fixed number of requests per clock, and 64-byte pieces
+// halve its bytes per clock.  Block tile 256 x 256, four wavefronts of
+// 128 x 128 (one wavefront per SIMD, accumulators in AGPRs).  The LDS image
+// of an operand is a swizzled row-major layout (see dma_swz); a DMA lane
+// writes slot base + lane, so each lane fetches the global chunk that belongs
+// in its slot.
 constexpr int kDmaKMult = 128;     // K granularity of the DMA kernel
-constexpr int kDmaBK = 64;         // K columns per ring stage (32 or 64)
+constexpr int kDmaBK = 64;         // K columns per stage
 
 // a pointer that is the same in every lane, moved to scalar registers
 template <typename T>
@@ -538,7 +533,7 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, int L, int 
 template <int EPI, int BK>
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
-  constexpr int R = BK == 32 ? 4 : 2;
+  constexpr int R = 2;                   // split parts are whole stage pairs
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;   // output columns of a quadrant
   __shared__ uint16_t ep[128 * kEpPitch];
   const int n_tiles = (p.N + HC - 1) / HC;
@@ -618,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 template <int EPI, int BK>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256;
-  constexpr int R = BK == 32 ? 4 : 2;   // ring stages
+  constexpr int R = 2;                  // stages per split-part granule (nks is even)
   constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
   constexpr int NKS = BK / 16;          // MFMA k-steps per stage
   constexpr int WM = 128, WN = 128;
@@ -626,14 +621,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
   constexpr int LD = BM * CH / kThreads;  // DMA instructions per operand per stage
   constexpr int RPI = kThreads / CH;      // rows covered by one DMA instruction
-  constexpr int D = 2 * LD;               // per thread per stage
-  constexpr int BOFF = BM * CH;           // B image offset inside a slot (uint4)
-  static_assert(BK == 32 || BK == 64, "stage depth");
-  static_assert(NKS % 2 == 0, "k-steps per stage alternate two fragment sets");
-  static_assert(R * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
-  static_assert(BM * kEpPitch * 2 <= R * (BM + BN) * BK * 2, "epilogue staging fits in the ring");
-  static_assert(D * (R - 1) < 64, "vmcnt range");
-  __shared__ uint4 ring[R][(BM + BN) * CH];
+  constexpr int HALF = BM * CH;           // uint4 per half-slot (one operand of one stage)
+  static_assert(BK == 64 && BM == BN, "the schedule below is written for 64-deep stages of 256 x 256 tiles");
+  static_assert(5 * HALF * 16 <= 160 * 1024, "LDS");
+  static_assert(BM * kEpPitch * 2 <= 5 * HALF * 16, "epilogue staging fits in the ring");
+  __shared__ uint4 ring[5 * HALF];
 
   const int n_tiles = (p.N + HC - 1) / HC;
   const int m_total = p.ts[p.E];
@@ -652,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     L = sp.full + unit / sp.S;
   }
   const int ks0 = unit < 0 ? 0 : (unit % sp.S) * sp.chunk;   // first stage of this block
-  const int nks = unit < 0 ? KT : min(sp.chunk, KT - ks0);    // stages (a multiple of R)
+  const int nks = unit < 0 ? KT : min(sp.chunk, KT - ks0);    // stages (even, >= 2)
   const TileCoord tc = tile_coord(p, L, m_total, n_tiles, BM);
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
   const int K = p.K;
@@ -697,28 +689,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     b_vo[i] = static_cast<uint32_t>((n * K + cq * 8) * 2);
   }
   const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
-  // single-instruction pieces, so that the stage below can interleave them
-  auto issue_one = [&](int st, uint4* S, int q) __attribute__((always_inline)) {     // q < LD: A, else B
-    const int kb = (ks0 + st) * BK * 2;
-    if (q < LD) dma16(a_sb + kb, a_vo[q], lds_addr(S + q * 256) + wave_lds);
-    else dma16(b_sb[q - LD] + kb, b_vo[q - LD], lds_addr(S + BOFF + (q - LD) * 256) + wave_lds);
+  // half-slot index (2 s + c) % 5 from (2 s) % 5 (both < 5)
+  auto hs = [](int c) __attribute__((always_inline)) { return c >= 5 ? c - 5 : c; };
+  // one DMA instruction: instruction q (< LD) of operand A or B of stage st
+  // into half-slot h
+  auto issue_a = [&](int st, int h, int q) __attribute__((always_inline)) {
+    dma16(a_sb + (ks0 + st) * BK * 2, a_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
   };
-  auto issue = [&](int st, uint4* S) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < D; ++q) issue_one(st, S, q);
+  auto issue_b = [&](int st, int h, int q) __attribute__((always_inline)) {
+    dma16(b_sb[q] + (ks0 + st) * BK * 2, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
   };
-  auto read_one = [&](const uint4* S, int ks, int r, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
+  auto read_one = [&](const uint4* SA, const uint4* SB, int ks, int r, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN])
+      __attribute__((always_inline)) {
     if (r < FN) {
-      uint4 v = S[BOFF + dma_swz<CH>(wn * WN + r * 32 + fr, 2 * ks + fc)];
+      uint4 v = SB[dma_swz<CH>(wn * WN + r * 32 + fr, 2 * ks + fc)];
       fb[r] = *reinterpret_cast<bf16x8_t*>(&v);
     } else {
-      uint4 v = S[dma_swz<CH>(wm * WM + (r - FN) * 32 + fr, 2 * ks + fc)];
+      uint4 v = SA[dma_swz<CH>(wm * WM + (r - FN) * 32 + fr, 2 * ks + fc)];
       fa[r - FN] = *reinterpret_cast<bf16x8_t*>(&v);
     }
-  };
-  auto read_frags = [&](const uint4* S, int ks, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
-#pragma unroll
-    for (int r = 0; r < FM + FN; ++r) read_one(S, ks, r, fa, fb);
   };
 
   f32x16_t acc[FM][FN];
@@ -728,99 +717,118 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  auto mma_one = [&](int q, const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) {
+  auto mma_one = [&](int q, const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) __attribute__((always_inline)) {
     acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / FN], fb[q % FN], acc[q / FN][q % FN], 0, 0, 0);
   };
 
   bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  // One stage (ring of two 64-deep slots), issued in a fixed order
-  // (sched_barrier keeps the compiler from regrouping it); each MFMA is
-  // followed by about one LDS read or DMA, so the matrix pipe is fed while
-  // they issue:
-  //   k-step 0: MFMAs with the k-step-1 fragment reads and the second half
-  //             of the DMAs of stage kt + 1 (into the other slot);
-  //   k-steps 1, 2: MFMAs with the next k-step's fragment reads;
-  //   the first kPre k-step-3 MFMAs; wait for stage kt + 1 (vmcnt(0): only
-  //   its DMAs are in flight), barrier (this slot is now free);
-  //   k-step 3: the remaining MFMAs with the next stage's k-step-0 fragment
-  //   reads and the first half of the DMAs of stage kt + 2 into this slot.
-  // Splitting a stage's 16 DMAs over two places keeps them from queueing up
-  // behind each other; the later half still has about three k-steps to land.
-  // Compile-time flags: NEXT = stage kt + 1 exists, ISSA = stage kt + 2
-  // exists (first half issued here), ISSB = the second half of stage kt + 1
-  // is issued here (every stage after the first two).
-  static_assert(R == 2 && NKS == 4, "the stage schedule below is written for two 64-deep slots");
+  // The 160 KB of LDS are five half-slots of 32 KB, each holding one operand
+  // of one stage: stage s keeps A in half-slot (2 s) % 5 and B in (2 s + 1) % 5.
+  // One stage, issued in a fixed order (sched_barrier keeps the compiler from
+  // regrouping it); each MFMA is followed by at most one LDS read and one DMA:
+  //   k-steps 0-2: MFMAs with the next k-step's fragment reads;
+  //   k-step 3: kPre MFMAs; wait for stage s + 1 (vmcnt), barrier s; the
+  //   other MFMAs with the reads of stage s + 1's k-step 0.
+  // Barrier s frees both half-slots of stage s.  The "window" from barrier s
+  // to barrier s + 1 spans 64 MFMAs (the 14 after barrier s, then k-steps 0-2
+  // and the kPre MFMAs of stage s + 1); one DMA goes out every fourth MFMA:
+  // B(s + 2) at positions 0, 4, .., 28 into A(s)'s half-slot, then A(s + 3)
+  // at 32, .., 60 into B(s)'s.  B(s + 2) must land by barrier s + 1, A(s + 3)
+  // only by barrier s + 2.  The DMA path moves ~60 B/clk per CU at 128-byte
+  // rows, so a stage's 64 KB take about half of its 2048 MFMA cycles; issued
+  // in bursts they stall the MFMAs queued behind them, hence the spreading.
+  // Compile-time flags: NEXT = stage s + 1 exists; PREB / PREA = this stage
+  // issues B(s + 1) (second half) / A(s + 2) of window s - 1; POSTB = B(s + 2)
+  // (first half) is issued after barrier s; WAITN = DMAs allowed in flight at
+  // the wait (A(s + 2), issued last).
   constexpr int NQ = FM * FN;           // MFMAs per k-step
   constexpr int kPre = 2;
-  constexpr int DH = D / 2;             // DMAs per half stage
-  auto stage = [&](auto next, auto issa, auto issb, int kt, uint4* Sc, uint4* Sn) __attribute__((always_inline)) {
+  constexpr int NM = NQ - kPre;         // MFMAs after the barrier
+  constexpr int NRD = FM + FN;          // fragment reads per k-step
+  static_assert(NKS == 4 && LD == 8 && NM == 14, "window layout");
+  auto stage = [&](auto next, auto preb, auto prea, auto postb, auto waitn, int s, int cA)
+      __attribute__((always_inline)) {
+    const uint4* Ac = ring + cA * HALF;
+    const uint4* Bc = ring + hs(cA + 1) * HALF;
+    const uint4* An = ring + hs(cA + 2) * HALF;
+    const uint4* Bn = ring + hs(cA + 3) * HALF;
+    const int h_preb = hs(cA + 3);       // B(s + 1) = (2 s + 3) % 5
+    const int h_prea = hs(cA + 4);       // A(s + 2) = (2 s + 4) % 5
     template_for<NKS - 1>([&](auto sc) __attribute__((always_inline)) {
       constexpr int S = decltype(sc)::value;
       auto& ca = (S & 1) ? fa1 : fa0;
       auto& cb = (S & 1) ? fb1 : fb0;
       auto& na = (S & 1) ? fa0 : fa1;
       auto& nb = (S & 1) ? fb0 : fb1;
-      constexpr int NB = (S == 0 && decltype(issb)::value) ? DH : 0;
-      constexpr int NC = FM + FN + NB;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
+      template_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int i = NM + S * NQ + q;      // window position
         mma_one(q, ca, cb);
 #pragma unroll
-        for (int c = q * NC / NQ; c < (q + 1) * NC / NQ; ++c) {
-          if (c < FM + FN) read_one(Sc, S + 1, c, na, nb);
-          else issue_one(kt + 1, Sn, DH + (c - FM - FN));
-        }
+        for (int c = q * NRD / NQ; c < (q + 1) * NRD / NQ; ++c) read_one(Ac, Bc, S + 1, c, na, nb);
+        if constexpr (i % 4 == 0 && i < 32 && decltype(preb)::value) issue_b(s + 1, h_preb, i / 4);
+        if constexpr (i % 4 == 0 && i >= 32 && decltype(prea)::value) issue_a(s + 2, h_prea, (i - 32) / 4);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     });
-    // NKS is even: the last k-step uses fa1/fb1
+    // k-step 3 (fa1/fb1); window positions 62, 63 carry no DMA
 #pragma unroll
     for (int q = 0; q < kPre; ++q) {
       mma_one(q, fa1, fb1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<decltype(waitn)::value>();
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int NR = decltype(next)::value ? FM + FN : 0;
-    constexpr int ND = decltype(issa)::value ? DH : 0;
-    constexpr int NC = NR + ND;
-    constexpr int NM = NQ - kPre;
-#pragma unroll
-    for (int q = 0; q < NM; ++q) {
+    template_for<NM>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
       mma_one(kPre + q, fa1, fb1);
-      // spread NC companions over NM MFMAs: reads first, then DMAs
+      if constexpr (decltype(next)::value) {
 #pragma unroll
-      for (int c = q * NC / NM; c < (q + 1) * NC / NM; ++c) {
-        if (c < NR) read_one(Sn, 0, c, fa0, fb0);
-        else issue_one(kt + 2, Sc, c - NR);
+        for (int c = q * NRD / NM; c < (q + 1) * NRD / NM; ++c) read_one(An, Bn, 0, c, fa0, fb0);
       }
+      if constexpr (q % 4 == 0 && decltype(postb)::value) issue_b(s + 2, cA, q / 4);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  // prologue: stages 0 and 1 in full, wait for stage 0
-  issue(0, ring[0]);
-  issue(1, ring[1]);
-  wait_vmcnt<D>();
-  lds_barrier();
-  read_frags(ring[0], 0, fa0, fb0);
-  if (nks == R) {
-    stage(T_{}, F_{}, F_{}, 0, ring[0], ring[1]);
-    stage(F_{}, F_{}, F_{}, 1, ring[1], ring[0]);
+  using W0 = std::integral_constant<int, 0>;
+  using W8 = std::integral_constant<int, LD>;
+  // prologue: A(0), B(0), A(1), B(1), A(2) into half-slots 0 .. 4; wait for stage 0
+#pragma unroll
+  for (int q = 0; q < LD; ++q) issue_a(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < LD; ++q) issue_b(0, 1, q);
+#pragma unroll
+  for (int q = 0; q < LD; ++q) issue_a(1, 2, q);
+#pragma unroll
+  for (int q = 0; q < LD; ++q) issue_b(1, 3, q);
+  if (nks > 2) {
+#pragma unroll
+    for (int q = 0; q < LD; ++q) issue_a(2, 4, q);
+    wait_vmcnt<3 * LD>();
   } else {
-    // first round: stage 1's second half was issued in the prologue
-    stage(T_{}, T_{}, F_{}, 0, ring[0], ring[1]);
-    stage(T_{}, T_{}, T_{}, 1, ring[1], ring[0]);
-    int kt = R;
-    for (; kt + R < nks; kt += R) {
-      stage(T_{}, T_{}, T_{}, kt, ring[0], ring[1]);
-      stage(T_{}, T_{}, T_{}, kt + 1, ring[1], ring[0]);
+    wait_vmcnt<2 * LD>();
+  }
+  lds_barrier();
+  {
+#pragma unroll
+    for (int r = 0; r < FM + FN; ++r) read_one(ring, ring + HALF, 0, r, fa0, fb0);
+  }
+  if (nks == 2) {
+    stage(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
+    stage(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
+  } else {
+    stage(T_{}, F_{}, F_{}, T_{}, W8{}, 0, 0);
+    int cA = 2;
+    for (int s = 1; s <= nks - 3; ++s) {
+      stage(T_{}, T_{}, T_{}, T_{}, W8{}, s, cA);
+      cA = hs(cA + 2);
     }
-    // last round: nothing left to issue but the second half of the last stage
-    stage(T_{}, F_{}, T_{}, kt, ring[0], ring[1]);
-    stage(F_{}, F_{}, F_{}, kt + 1, ring[1], ring[0]);
+    // s = nks - 2: only B(nks - 1)'s second half left to issue
+    stage(T_{}, T_{}, F_{}, F_{}, W0{}, nks - 2, cA);
+    stage(F_{}, F_{}, F_{}, F_{}, W0{}, nks - 1, hs(cA + 2));
   }
 
   if (unit >= 0) {
@@ -839,7 +847,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   }
   // the ring is free: the last LDS reads came before the last barrier and no
   // load is in flight
-  dma_epilogue<EPI>(acc, reinterpret_cast<uint16_t*>(&ring[0][0]), p, e, nt, row0, rows_valid);
+  dma_epilogue<EPI>(acc, reinterpret_cast<uint16_t*>(ring), p, e, nt, row0, rows_valid);
 }
 
 template <int EPI, int BK>
