@@ -390,7 +390,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// row pitch (bf16 elements) of the epilogue's 256 x 128 staging block
+// row pitch (bf16 elements) of the split reduction's 128 x 128 staging block
 constexpr int kEpPitch = 136;
 
 // silu(u) = u / (1 + e^-u) with the hardware exp2 and reciprocal (relative
@@ -440,69 +440,66 @@ __device__ __forceinline__ SplitPlan split_plan(int V, int KT, int R, int n_cu, 
   return sp;
 }
 
-// Epilogue of a 256 x 256 tile held as 4 x 4 32x32 fragments per wavefront
-// (wavefront w owns rows 128 (w / 2) and columns 128 (w % 2); element q of a
+// Epilogue of one wavefront's FM x 4 fragments of 32 x 32 (element q of a
 // fragment is row 8 (q / 4) + 4 (lane / 32) + q % 4, column lane % 32),
-// staged through LDS: each pass writes a 256 x 128 bf16 block row-major
-// (pitch kEpPitch, padded so that the two lane halves of one ds_write land in
-// different banks), then every thread stores 16-byte pieces of whole rows.
-//   SwiGLU: one pass, LDS column wn*64 + j*32 + fr <- silu(gate j) * up j.
-//   Plain/ReLU: pass h takes fragments j = 2h, 2h+1 of both wavefront
-//   columns; LDS column c maps to tile column (c/64)*128 + 64h + c%64.
-// ep must hold 256 * kEpPitch bf16 and be free of other use.
-template <int EPI>
-__device__ __forceinline__ void dma_epilogue(const f32x16_t (&acc)[4][4], uint16_t* ep, const GemmParams& p, int e,
-                                             int nt, int row0, int rows_valid) {
-  constexpr int BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
-  constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
+// staged through an LDS block private to the wavefront, so that every lane
+// then stores whole 16-byte pieces of output rows and no barrier is needed.
+//   SwiGLU: fragments j and j + 2 hold the gate and up columns of the same
+//   hidden units: 64 output columns, silu(gate) * up.
+//   Plain/ReLU: 128 output columns (+ bias).
+// row0: first output row of the wavefront, rows_valid: valid rows from there
+// (may be <= 0), col0: first output column (pieces at col0 + c >= N are
+// skipped; N % 8 == 0).  st must hold 32 FM x (OC + 8) bf16 of LDS that no
+// other wavefront uses.
+template <int EPI, int FM>
+__device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint16_t* st, const GemmParams& p, int e,
+                                              int row0, int rows_valid, int col0) {
+  constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
+  constexpr int PITCH = OC + 8;           // the two lane halves of a write land 16 banks apart
+  constexpr int PR = OC / 8;              // 16-byte pieces per row
   const int N = p.N;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int lane = threadIdx.x & 63;
   const int fr = lane & 31;
   const int fc = lane >> 5;
-  constexpr int NPASS = EPI == EPI_SWIGLU ? 1 : 2;
 #pragma unroll
-  for (int h = 0; h < NPASS; ++h) {
-    if (h > 0) lds_barrier();              // previous pass fully read
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = EPI == EPI_SWIGLU ? jj : 2 * h + jj;
-      const int lc = wn * 64 + jj * 32 + fr;
-      float bias = 0.f;
-      if (EPI != EPI_SWIGLU && p.bias) {
-        const int col = nt * BN + wn * WN + j * 32 + fr;
-        bias = col < N ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
-          float v;
-          if (EPI == EPI_SWIGLU) {
-            v = silu_fast(acc[i][j][q]) * acc[i][j + FN / 2][q];
-          } else {
-            v = acc[i][j][q] + bias;
-            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
-          }
-          ep[lr * kEpPitch + lc] = f32_to_bf16(v);
-        }
+  for (int j = 0; j < OC / 32; ++j) {
+    float bias = 0.f;
+    if (EPI != EPI_SWIGLU && p.bias) {
+      const int col = col0 + j * 32 + fr;
+      bias = col < N ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
     }
-    lds_barrier();
-    // 256 rows x 16 pieces of 8 columns; thread t takes piece t + 256 u
-#pragma unroll 4
-    for (int u = 0; u < 16; ++u) {
-      const int c = tid + kThreads * u;
-      const int lr = c >> 4;
-      const int pc = (c & 15) * 8;          // LDS column of the piece
-      const int col = EPI == EPI_SWIGLU ? nt * HC + pc : nt * BN + (pc >> 6) * 128 + 64 * h + (pc & 63);
-      if (lr < rows_valid && col < N) {
-        const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * kEpPitch + pc);
-        *reinterpret_cast<uint4*>(p.C + static_cast<size_t>(row0 + lr) * N + col) = v;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; q += 2) {
+        float v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (EPI == EPI_SWIGLU) {
+            v[h] = silu_fast(acc[i][j][q + h]) * acc[i][j + 2][q + h];
+          } else {
+            v[h] = acc[i][j][q + h] + bias;
+            if (EPI == EPI_RELU) v[h] = fmaxf(v[h], 0.f);
+          }
+        }
+        const uint32_t pk = pack_bf16x2(v[0], v[1]);
+        const int r = i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);   // rows r, r + 1
+        st[r * PITCH + j * 32 + fr] = static_cast<uint16_t>(pk);
+        st[(r + 1) * PITCH + j * 32 + fr] = static_cast<uint16_t>(pk >> 16);
       }
+  }
+  // the lanes of one wavefront read back what the others wrote: LDS
+  // operations of a wavefront complete in order, the fence keeps the
+  // compiler from moving the reads above the writes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+#pragma unroll 4
+  for (int u = 0; u < 32 * FM * PR / 64; ++u) {
+    const int c = lane + 64 * u;
+    const int r = c / PR;
+    const int pc = (c % PR) * 8;
+    if (r < rows_valid && col0 + pc < N) {
+      const uint4 v = *reinterpret_cast<const uint4*>(st + r * PITCH + pc);
+      *reinterpret_cast<uint4*>(p.C + static_cast<size_t>(row0 + r) * N + col0 + pc) = v;
     }
   }
 }
@@ -610,27 +607,27 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
   }
 }
 
+// One block per tile.  FM = 4: the 256 x 256 tile (four wavefronts of
+// 128 x 128); FM = 2: a 128 x 256 tile for the last m-tile of a segment with
+// at most 128 rows (four wavefronts of 64 x 128: half the MFMA work, the same
+// weight traffic).  Wavefront w owns rows 32 FM (w / 2) and B rows 128
+// (w % 2).  Split units (unit >= 0) run stages [ks0, ks0 + nks) of a full
+// tile and store raw accumulators.  (The tile body is a generic lambda
+// rather than a function template: written as a function, the register
+// allocator spilled some 200 accumulator registers around the stage loop.)
 template <int EPI, int BK>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256;
-  constexpr int R = 2;                  // stages per split-part granule (nks is even)
-  constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
-  constexpr int NKS = BK / 16;          // MFMA k-steps per stage
-  constexpr int WM = 128, WN = 128;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int HC = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  constexpr int LD = BM * CH / kThreads;  // DMA instructions per operand per stage
-  constexpr int RPI = kThreads / CH;      // rows covered by one DMA instruction
-  constexpr int HALF = BM * CH;           // uint4 per half-slot (one operand of one stage)
-  static_assert(BK == 64 && BM == BN, "the schedule below is written for 64-deep stages of 256 x 256 tiles");
-  static_assert(5 * HALF * 16 <= 160 * 1024, "LDS");
-  static_assert(BM * kEpPitch * 2 <= 5 * HALF * 16, "epilogue staging fits in the ring");
-  __shared__ uint4 ring[5 * HALF];
+  constexpr int BM = 256;
+  constexpr int R = 2;                  // split parts are whole stage pairs
+  constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
+  static_assert(BK == kDmaBK, "stage depth");
+  static_assert(4 * 128 * (128 + 8) * 2 <= 160 * 1024, "epilogue staging fits in the ring");
+  __shared__ uint4 ring[5 * 256 * (kDmaBK / 8)];
 
   const int n_tiles = (p.N + HC - 1) / HC;
   const int m_total = p.ts[p.E];
   const int V = m_total * n_tiles;
-  const int KT = p.K / BK;              // multiple of R
+  const int KT = p.K / BK;              // even
   const SplitPlan sp = split_plan(V, KT, R, p.n_cu, p.split_max);
   const int per = (sp.full + kXcds - 1) / kXcds;
   const int b = blockIdx.x;
@@ -646,208 +643,241 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   const int ks0 = unit < 0 ? 0 : (unit % sp.S) * sp.chunk;   // first stage of this block
   const int nks = unit < 0 ? KT : min(sp.chunk, KT - ks0);    // stages (even, >= 2)
   const TileCoord tc = tile_coord(p, L, m_total, n_tiles, BM);
-  const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
-  const int K = p.K;
-  const int N = p.N;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int fr = lane & 31;
-  const int fc = lane >> 5;
+  auto tile = [&](auto fmc) __attribute__((always_inline)) {
+    constexpr int FM = decltype(fmc)::value;
+    constexpr int BN = 256;
+    constexpr int BMA = 64 * FM;            // A rows of the tile
+    constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
+    constexpr int NKS = BK / 16;            // MFMA k-steps per stage
+    constexpr int WM = 32 * FM, WN = 128;
+    constexpr int FN = WN / 32;
+    constexpr int LDA = BMA * CH / kThreads;  // DMA instructions per stage: A
+    constexpr int LDB = BN * CH / kThreads;   //   and B
+    constexpr int RPI = kThreads / CH;        // rows covered by one DMA instruction
+    constexpr int HALF = BN * CH;             // uint4 per half-slot (one operand of one stage)
+    static_assert(BK == 64 && (FM == 4 || FM == 2), "tile shapes");
+    const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
+    const int K = p.K;
+    const int N = p.N;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int fr = lane & 31;
+    const int fc = lane >> 5;
 
-  // DMA instruction i of this thread fills slot i * 256 + tid of an operand
-  // image: row i * RPI + tid / CH, stored chunk tid % CH, which holds the
-  // global chunk (tid % CH) ^ ((tid >> 4) % CH) (the swizzle term of that row,
-  // the same for every i).  Addresses: a uniform base (advanced by 2 BK bytes
-  // per stage) plus a 32-bit per-lane byte offset fixed for the whole loop.
-  const int cq = (tid & (CH - 1)) ^ ((tid >> 4) & (CH - 1));
-  const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K));
-  uint32_t a_vo[LD];
+    // DMA instruction i of this thread fills slot i * 256 + tid of an operand
+    // image: row i * RPI + tid / CH, stored chunk tid % CH, which holds the
+    // global chunk (tid % CH) ^ ((tid >> 4) % CH) (the swizzle term of that row,
+    // the same for every i).  Addresses: a uniform base (advanced by 2 BK bytes
+    // per stage) plus a 32-bit per-lane byte offset fixed for the whole loop.
+    const int cq = (tid & (CH - 1)) ^ ((tid >> 4) & (CH - 1));
+    const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K));
+    uint32_t a_vo[LDA];
 #pragma unroll
-  for (int i = 0; i < LD; ++i)
-    a_vo[i] = static_cast<uint32_t>((min(i * RPI + tid / CH, rows_valid - 1) * K + cq * 8) * 2);
-  const char* b_sb[LD];
-  uint32_t b_vo[LD];
+    for (int i = 0; i < LDA; ++i)
+      a_vo[i] = static_cast<uint32_t>((min(i * RPI + tid / CH, rows_valid - 1) * K + cq * 8) * 2);
+    const char* b_sb[LDB];
+    uint32_t b_vo[LDB];
 #pragma unroll
-  for (int i = 0; i < LD; ++i) {
-    const int r = i * RPI + tid / CH;
-    int n;
-    const void* base = p.B1;
-    if (EPI == EPI_SWIGLU) {
-      // rows [128 w, 128 w + 64) are gate rows of hidden columns
-      // nt * HC + 64 w + (0..63), the next 64 the up rows of the same columns;
-      // one instruction's RPI rows lie in one such half
-      n = nt * HC + (r >> 7) * 64 + (r & 63);
-      if ((i * RPI) & 64) base = p.B3;
-    } else {
-      n = nt * BN + r;
-    }
-    n = min(n, N - 1);
-    b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(e) * N * K * 2);
-    b_vo[i] = static_cast<uint32_t>((n * K + cq * 8) * 2);
-  }
-  const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
-  // half-slot index (2 s + c) % 5 from (2 s) % 5 (both < 5)
-  auto hs = [](int c) __attribute__((always_inline)) { return c >= 5 ? c - 5 : c; };
-  // one DMA instruction: instruction q (< LD) of operand A or B of stage st
-  // into half-slot h
-  auto issue_a = [&](int st, int h, int q) __attribute__((always_inline)) {
-    dma16(a_sb + (ks0 + st) * BK * 2, a_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
-  };
-  auto issue_b = [&](int st, int h, int q) __attribute__((always_inline)) {
-    dma16(b_sb[q] + (ks0 + st) * BK * 2, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
-  };
-  auto read_one = [&](const uint4* SA, const uint4* SB, int ks, int r, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN])
-      __attribute__((always_inline)) {
-    if (r < FN) {
-      uint4 v = SB[dma_swz<CH>(wn * WN + r * 32 + fr, 2 * ks + fc)];
-      fb[r] = *reinterpret_cast<bf16x8_t*>(&v);
-    } else {
-      uint4 v = SA[dma_swz<CH>(wm * WM + (r - FN) * 32 + fr, 2 * ks + fc)];
-      fa[r - FN] = *reinterpret_cast<bf16x8_t*>(&v);
-    }
-  };
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  auto mma_one = [&](int q, const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) __attribute__((always_inline)) {
-    acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / FN], fb[q % FN], acc[q / FN][q % FN], 0, 0, 0);
-  };
-
-  bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  // The 160 KB of LDS are five half-slots of 32 KB, each holding one operand
-  // of one stage: stage s keeps A in half-slot (2 s) % 5 and B in (2 s + 1) % 5.
-  // One stage, issued in a fixed order (sched_barrier keeps the compiler from
-  // regrouping it); each MFMA is followed by at most one LDS read and one DMA:
-  //   k-steps 0-2: MFMAs with the next k-step's fragment reads;
-  //   k-step 3: kPre MFMAs; wait for stage s + 1 (vmcnt), barrier s; the
-  //   other MFMAs with the reads of stage s + 1's k-step 0.
-  // Barrier s frees both half-slots of stage s.  The "window" from barrier s
-  // to barrier s + 1 spans 64 MFMAs (the 14 after barrier s, then k-steps 0-2
-  // and the kPre MFMAs of stage s + 1); one DMA goes out every fourth MFMA:
-  // B(s + 2) at positions 0, 4, .., 28 into A(s)'s half-slot, then A(s + 3)
-  // at 32, .., 60 into B(s)'s.  B(s + 2) must land by barrier s + 1, A(s + 3)
-  // only by barrier s + 2.  The DMA path moves ~60 B/clk per CU at 128-byte
-  // rows, so a stage's 64 KB take about half of its 2048 MFMA cycles; issued
-  // in bursts they stall the MFMAs queued behind them, hence the spreading.
-  // Compile-time flags: NEXT = stage s + 1 exists; PREB / PREA = this stage
-  // issues B(s + 1) (second half) / A(s + 2) of window s - 1; POSTB = B(s + 2)
-  // (first half) is issued after barrier s; WAITN = DMAs allowed in flight at
-  // the wait (A(s + 2), issued last).
-  constexpr int NQ = FM * FN;           // MFMAs per k-step
-  constexpr int kPre = 2;
-  constexpr int NM = NQ - kPre;         // MFMAs after the barrier
-  constexpr int NRD = FM + FN;          // fragment reads per k-step
-  static_assert(NKS == 4 && LD == 8 && NM == 14, "window layout");
-  auto stage = [&](auto next, auto preb, auto prea, auto postb, auto waitn, int s, int cA)
-      __attribute__((always_inline)) {
-    const uint4* Ac = ring + cA * HALF;
-    const uint4* Bc = ring + hs(cA + 1) * HALF;
-    const uint4* An = ring + hs(cA + 2) * HALF;
-    const uint4* Bn = ring + hs(cA + 3) * HALF;
-    const int h_preb = hs(cA + 3);       // B(s + 1) = (2 s + 3) % 5
-    const int h_prea = hs(cA + 4);       // A(s + 2) = (2 s + 4) % 5
-    template_for<NKS - 1>([&](auto sc) __attribute__((always_inline)) {
-      constexpr int S = decltype(sc)::value;
-      auto& ca = (S & 1) ? fa1 : fa0;
-      auto& cb = (S & 1) ? fb1 : fb0;
-      auto& na = (S & 1) ? fa0 : fa1;
-      auto& nb = (S & 1) ? fb0 : fb1;
-      template_for<NQ>([&](auto qc) __attribute__((always_inline)) {
-        constexpr int q = decltype(qc)::value;
-        constexpr int i = NM + S * NQ + q;      // window position
-        mma_one(q, ca, cb);
-#pragma unroll
-        for (int c = q * NRD / NQ; c < (q + 1) * NRD / NQ; ++c) read_one(Ac, Bc, S + 1, c, na, nb);
-        if constexpr (i % 4 == 0 && i < 32 && decltype(preb)::value) issue_b(s + 1, h_preb, i / 4);
-        if constexpr (i % 4 == 0 && i >= 32 && decltype(prea)::value) issue_a(s + 2, h_prea, (i - 32) / 4);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    });
-    // k-step 3 (fa1/fb1); window positions 62, 63 carry no DMA
-#pragma unroll
-    for (int q = 0; q < kPre; ++q) {
-      mma_one(q, fa1, fb1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vmcnt<decltype(waitn)::value>();
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    template_for<NM>([&](auto qc) __attribute__((always_inline)) {
-      constexpr int q = decltype(qc)::value;
-      mma_one(kPre + q, fa1, fb1);
-      if constexpr (decltype(next)::value) {
-#pragma unroll
-        for (int c = q * NRD / NM; c < (q + 1) * NRD / NM; ++c) read_one(An, Bn, 0, c, fa0, fb0);
+    for (int i = 0; i < LDB; ++i) {
+      const int r = i * RPI + tid / CH;
+      int n;
+      const void* base = p.B1;
+      if (EPI == EPI_SWIGLU) {
+        // rows [128 w, 128 w + 64) are gate rows of hidden columns
+        // nt * HC + 64 w + (0..63), the next 64 the up rows of the same columns;
+        // one instruction's RPI rows lie in one such half
+        n = nt * HC + (r >> 7) * 64 + (r & 63);
+        if ((i * RPI) & 64) base = p.B3;
+      } else {
+        n = nt * BN + r;
       }
-      if constexpr (q % 4 == 0 && decltype(postb)::value) issue_b(s + 2, cA, q / 4);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  using W0 = std::integral_constant<int, 0>;
-  using W8 = std::integral_constant<int, LD>;
-  // prologue: A(0), B(0), A(1), B(1), A(2) into half-slots 0 .. 4; wait for stage 0
-#pragma unroll
-  for (int q = 0; q < LD; ++q) issue_a(0, 0, q);
-#pragma unroll
-  for (int q = 0; q < LD; ++q) issue_b(0, 1, q);
-#pragma unroll
-  for (int q = 0; q < LD; ++q) issue_a(1, 2, q);
-#pragma unroll
-  for (int q = 0; q < LD; ++q) issue_b(1, 3, q);
-  if (nks > 2) {
-#pragma unroll
-    for (int q = 0; q < LD; ++q) issue_a(2, 4, q);
-    wait_vmcnt<3 * LD>();
-  } else {
-    wait_vmcnt<2 * LD>();
-  }
-  lds_barrier();
-  {
-#pragma unroll
-    for (int r = 0; r < FM + FN; ++r) read_one(ring, ring + HALF, 0, r, fa0, fb0);
-  }
-  if (nks == 2) {
-    stage(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
-    stage(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
-  } else {
-    stage(T_{}, F_{}, F_{}, T_{}, W8{}, 0, 0);
-    int cA = 2;
-    for (int s = 1; s <= nks - 3; ++s) {
-      stage(T_{}, T_{}, T_{}, T_{}, W8{}, s, cA);
-      cA = hs(cA + 2);
+      n = min(n, N - 1);
+      b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(e) * N * K * 2);
+      b_vo[i] = static_cast<uint32_t>((n * K + cq * 8) * 2);
     }
-    // s = nks - 2: only B(nks - 1)'s second half left to issue
-    stage(T_{}, T_{}, F_{}, F_{}, W0{}, nks - 2, cA);
-    stage(F_{}, F_{}, F_{}, F_{}, W0{}, nks - 1, hs(cA + 2));
-  }
+    const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
+    // half-slot index (2 s + c) % 5 from (2 s) % 5 (both < 5)
+    auto hs = [](int c) __attribute__((always_inline)) { return c >= 5 ? c - 5 : c; };
+    // one DMA instruction: instruction q of operand A or B of stage st into
+    // half-slot h
+    auto issue_a = [&](int st, int h, int q) __attribute__((always_inline)) {
+      dma16(a_sb + (ks0 + st) * BK * 2, a_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+    };
+    auto issue_b = [&](int st, int h, int q) __attribute__((always_inline)) {
+      dma16(b_sb[q] + (ks0 + st) * BK * 2, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+    };
+    auto read_one = [&](const uint4* SA, const uint4* SB, int ks, int r, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN])
+        __attribute__((always_inline)) {
+      if (r < FN) {
+        uint4 v = SB[dma_swz<CH>(wn * WN + r * 32 + fr, 2 * ks + fc)];
+        fb[r] = *reinterpret_cast<bf16x8_t*>(&v);
+      } else {
+        uint4 v = SA[dma_swz<CH>(wm * WM + (r - FN) * 32 + fr, 2 * ks + fc)];
+        fa[r - FN] = *reinterpret_cast<bf16x8_t*>(&v);
+      }
+    };
 
-  if (unit >= 0) {
-    // split unit: raw accumulators to the partial buffer, in the MFMA layout
-    float* pt = p.partial + static_cast<size_t>(unit) * (BM * BN);
+    f32x16_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        float4* dst = reinterpret_cast<float4*>(pt + ((static_cast<size_t>(wave) * (FM * FN) + i * FN + j) * 64 + lane) * 16);
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          dst[v] = make_float4(acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]);
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    auto mma_one = [&](int q, const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) __attribute__((always_inline)) {
+      acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / FN], fb[q % FN], acc[q / FN][q % FN], 0, 0, 0);
+    };
+
+    bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    // The 160 KB of LDS are five half-slots of 32 KB, each holding one operand
+    // of one stage: stage s keeps A in half-slot (2 s) % 5 and B in (2 s + 1) % 5
+    // (A of a 128-row tile fills half of it).
+    // One stage, issued in a fixed order (sched_barrier keeps the compiler from
+    // regrouping it); each MFMA is followed by about one LDS read and one DMA:
+    //   k-steps 0-2: MFMAs with the next k-step's fragment reads;
+    //   k-step 3: kPre MFMAs; wait for stage s + 1 (vmcnt), barrier s; the
+    //   other MFMAs with the reads of stage s + 1's k-step 0.
+    // Barrier s frees both half-slots of stage s.  The "window" from barrier s
+    // to barrier s + 1 spans WIN MFMAs (the NM after barrier s, then k-steps
+    // 0-2 and the kPre MFMAs of stage s + 1).  B(s + 2) goes out evenly over its
+    // first half, into A(s)'s half-slot, then A(s + 3) over the second half,
+    // into B(s)'s.  B(s + 2) must land by barrier s + 1, A(s + 3) only by
+    // barrier s + 2.  The DMA path moves ~60 B/clk per CU at 128-byte rows, so
+    // a stage's 64 KB take about half of its 2048 MFMA cycles; issued in bursts
+    // they stall the MFMAs queued behind them, hence the spreading.
+    // Compile-time flags: NEXT = stage s + 1 exists; PREB / PREA = this stage
+    // issues the rest of B(s + 1) / A(s + 2) (window s - 1); POSTB = B(s + 2)'s
+    // first part is issued after barrier s; WAITN = DMAs allowed in flight at
+    // the wait (A(s + 2), issued last).
+    constexpr int NQ = FM * FN;           // MFMAs per k-step
+    constexpr int kPre = 2;
+    constexpr int NM = NQ - kPre;         // MFMAs after the barrier
+    constexpr int NRD = FM + FN;          // fragment reads per k-step
+    constexpr int WIN = NQ * NKS;
+    constexpr int SB_ = WIN / 2 / LDB;    // window positions between B DMAs
+    constexpr int SA_ = WIN / 2 / LDA;    //   and between A DMAs
+    static_assert(NKS == 4 && SB_ * LDB == WIN / 2 && SA_ * LDA == WIN / 2 && WIN - SA_ < WIN - kPre, "window layout");
+    // window position i: B DMA i / SB_ if i < WIN/2 and i % SB_ == 0; A DMA (i - WIN/2) / SA_ likewise
+    auto stage = [&](auto next, auto preb, auto prea, auto postb, auto waitn, int s, int cA)
+        __attribute__((always_inline)) {
+      const uint4* Ac = ring + cA * HALF;
+      const uint4* Bc = ring + hs(cA + 1) * HALF;
+      const uint4* An = ring + hs(cA + 2) * HALF;
+      const uint4* Bn = ring + hs(cA + 3) * HALF;
+      const int h_preb = hs(cA + 3);       // B(s + 1) = (2 s + 3) % 5
+      const int h_prea = hs(cA + 4);       // A(s + 2) = (2 s + 4) % 5
+      auto pre_dma = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < WIN / 2 && i % SB_ == 0 && decltype(preb)::value) issue_b(s + 1, h_preb, i / SB_);
+        if constexpr (i >= WIN / 2 && (i - WIN / 2) % SA_ == 0 && decltype(prea)::value)
+          issue_a(s + 2, h_prea, (i - WIN / 2) / SA_);
+      };
+      template_for<NKS - 1>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int S = decltype(sc)::value;
+        auto& ca = (S & 1) ? fa1 : fa0;
+        auto& cb = (S & 1) ? fb1 : fb0;
+        auto& na = (S & 1) ? fa0 : fa1;
+        auto& nb = (S & 1) ? fb0 : fb1;
+        template_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          mma_one(q, ca, cb);
+#pragma unroll
+          for (int c = q * NRD / NQ; c < (q + 1) * NRD / NQ; ++c) read_one(Ac, Bc, S + 1, c, na, nb);
+          pre_dma(std::integral_constant<int, NM + S * NQ + q>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+      // k-step 3 (fa1/fb1)
+      template_for<kPre>([&](auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        mma_one(q, fa1, fb1);
+        pre_dma(std::integral_constant<int, WIN - kPre + q>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      wait_vmcnt<decltype(waitn)::value>();
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      template_for<NM>([&](auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        mma_one(kPre + q, fa1, fb1);
+        if constexpr (decltype(next)::value) {
+#pragma unroll
+          for (int c = q * NRD / NM; c < (q + 1) * NRD / NM; ++c) read_one(An, Bn, 0, c, fa0, fb0);
+        }
+        if constexpr (q % SB_ == 0 && decltype(postb)::value) issue_b(s + 2, cA, q / SB_);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using W0 = std::integral_constant<int, 0>;
+    using WA = std::integral_constant<int, LDA>;
+    // prologue: A(0), B(0), A(1), B(1), A(2) into half-slots 0 .. 4; wait for stage 0
+#pragma unroll
+    for (int q = 0; q < LDA; ++q) issue_a(0, 0, q);
+#pragma unroll
+    for (int q = 0; q < LDB; ++q) issue_b(0, 1, q);
+#pragma unroll
+    for (int q = 0; q < LDA; ++q) issue_a(1, 2, q);
+#pragma unroll
+    for (int q = 0; q < LDB; ++q) issue_b(1, 3, q);
+    if (nks > 2) {
+#pragma unroll
+      for (int q = 0; q < LDA; ++q) issue_a(2, 4, q);
+      wait_vmcnt<2 * LDA + LDB>();
+    } else {
+      wait_vmcnt<LDA + LDB>();
+    }
+    lds_barrier();
+    {
+#pragma unroll
+      for (int r = 0; r < FM + FN; ++r) read_one(ring, ring + HALF, 0, r, fa0, fb0);
+    }
+    if (nks == 2) {
+      stage(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
+      stage(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
+    } else {
+      stage(T_{}, F_{}, F_{}, T_{}, WA{}, 0, 0);
+      int cA = 2;
+      for (int s = 1; s <= nks - 3; ++s) {
+        stage(T_{}, T_{}, T_{}, T_{}, WA{}, s, cA);
+        cA = hs(cA + 2);
       }
-    return;
-  }
-  // the ring is free: the last LDS reads came before the last barrier and no
-  // load is in flight
-  dma_epilogue<EPI>(acc, reinterpret_cast<uint16_t*>(ring), p, e, nt, row0, rows_valid);
+      // s = nks - 2: only the rest of B(nks - 1) left to issue
+      stage(T_{}, T_{}, F_{}, F_{}, W0{}, nks - 2, cA);
+      stage(F_{}, F_{}, F_{}, F_{}, W0{}, nks - 1, hs(cA + 2));
+    }
+
+    if constexpr (FM == 4) {
+      if (unit >= 0) {
+        // split unit: raw accumulators to the partial buffer, in the MFMA layout
+        float* pt = p.partial + static_cast<size_t>(unit) * (256 * 256);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            float4* dst = reinterpret_cast<float4*>(pt + ((static_cast<size_t>(wave) * (FM * FN) + i * FN + j) * 64 + lane) * 16);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              dst[v] = make_float4(acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]);
+          }
+        return;
+      }
+    }
+    // the ring is free: the last LDS reads of every wavefront came before the
+    // last barrier and no load is in flight
+    constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
+    const int col0 = EPI == EPI_SWIGLU ? nt * HC + wn * 64 : nt * BN + wn * 128;
+    wave_epilogue<EPI, FM>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * (OC + 8), p, e, row0 + wm * WM,
+                           rows_valid - wm * WM, col0);
+  };
+  if (unit < 0 && tc.rows_valid <= 128)
+    tile(std::integral_constant<int, 2>{});
+  else
+    tile(std::integral_constant<int, 4>{});
 }
 
 template <int EPI, int BK>
