@@ -33,6 +33,53 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// fp32 softmax and top-k of one token's logits z[0..E) by one wavefront:
+// expert e lives on lane e % 64, slot e / 64; k rounds of a wavefront arg-max
+// (largest logit, lower id on ties), the winning lane marks its slot taken.
+// Adds the probabilities to wcol[0..E) and writes the outputs of token t.
+__device__ __forceinline__ void token_softmax_topk(const float* z, int t, const RouterArgs& a, float* wcol,
+                                                   int lane) {
+  float m = -INFINITY;
+  for (int e = lane; e < a.E; e += 64) m = fmaxf(m, z[e]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float s = 0.f;
+  for (int e = lane; e < a.E; e += 64) s += expf(z[e] - m);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  const float inv = 1.0f / s;
+  for (int e = lane; e < a.E; e += 64) {
+    if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z[e];
+    wcol[e] += expf(z[e] - m) * inv;
+  }
+  uint32_t taken = 0;
+  float myp = 0.f;
+  int myi = 0;
+  float psum = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int e = lane, i = 0; e < a.E; e += 64, ++i) {
+      if (!((taken >> i) & 1u) && better(z[e], e, bv, bi)) { bv = z[e]; bi = e; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const float p = expf(bv - m) * inv;
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) { myp = p; myi = bi; }
+    psum += p;
+  }
+  if (lane < a.k) {
+    const size_t o = static_cast<size_t>(t) * a.k + lane;
+    a.topk_idx[o] = myi;
+    a.topk_gate[o] = a.mode == MOE_GATE_RENORM ? myp / psum : myp;
+  }
+}
+
 // One block = 32 tokens x all E experts.  Logits are accumulated in
 // registers (2 tokens x 4 experts per thread per 64-expert group) from LDS
 // tiles of x and W_g, then kept in LDS for the softmax/top-k phase, which
@@ -121,50 +168,9 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
   const int wave = tid >> 6;
   for (int e = lane; e < a.E; e += 64) wcol[wave * a.E + e] = 0.f;
   for (int tl = wave; tl < kRtTok; tl += kRtThreads / 64) {
-    int t = t0 + tl;
+    const int t = t0 + tl;
     if (t >= a.T) break;
-    const float* z = lg + tl * a.E;
-    float m = -INFINITY;
-    for (int e = lane; e < a.E; e += 64) m = fmaxf(m, z[e]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float s = 0.f;
-    for (int e = lane; e < a.E; e += 64) s += expf(z[e] - m);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    const float inv = 1.0f / s;
-    for (int e = lane; e < a.E; e += 64) {
-      if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z[e];
-      wcol[wave * a.E + e] += expf(z[e] - m) * inv;
-    }
-    // top-k: k rounds of a wavefront arg-max; expert e lives on lane e % 64,
-    // slot e / 64, and the winning lane marks that slot as taken.
-    uint32_t taken = 0;
-    float myp = 0.f;
-    int myi = 0;
-    float psum = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int e = lane, i = 0; e < a.E; e += 64, ++i) {
-        if (!((taken >> i) & 1u) && better(z[e], e, bv, bi)) { bv = z[e]; bi = e; }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ov = __shfl_xor(bv, o);
-        int oi = __shfl_xor(bi, o);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      const float p = expf(bv - m) * inv;
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == j) { myp = p; myi = bi; }
-      psum += p;
-    }
-    if (lane < a.k) {
-      const size_t o = static_cast<size_t>(t) * a.k + lane;
-      a.topk_idx[o] = myi;
-      a.topk_gate[o] = a.mode == MOE_GATE_RENORM ? myp / psum : myp;
-    }
+    token_softmax_topk(lg + tl * a.E, t, a, wcol + wave * a.E, lane);
   }
   __syncthreads();
   // per-block probability column sums, fixed order over the 4 waves
@@ -333,6 +339,158 @@ __global__ __launch_bounds__(kSmThreads) void router_stream_kernel(RouterArgs a)
   }
 }
 
+// MFMA router for bf16 activations.  W_g is split exactly into three bf16
+// planes, w = hi + mid + lo, each the truncation of what the previous ones
+// leave (a float's 24-bit significand in three 8-bit pieces), so every
+// product with a bf16 x is exact and the logits are fp32 sums as in the VALU
+// kernels.  A block takes 16 TG tokens and NE groups of 16 experts per pass;
+// its 8 wavefronts split K by 32-column steps (wavefront w takes steps w,
+// w + 8, ...) and keep kMfPd steps of loads in flight: per step a 16-byte x
+// fragment per token group (v_mfma_f32_16x16x32_bf16 A operand: token lane %
+// 16, columns 8 (lane / 16) ..) and 32 bytes of fp32 W_g per expert group (B
+// operand: expert lane % 16, same columns), split in registers.  The
+// wavefronts' partial logits are added in LDS in wavefront order, then one
+// wavefront per token does the fp32 softmax and top-k, and per-block
+// probability column sums go to the workspace.
+constexpr int kMfWaves = 8;
+constexpr int kMfThreads = 64 * kMfWaves;
+constexpr int kMfPd = 4;                      // k-steps of loads in flight
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_mf;
+
+// bf16 pair (lo in bits 0-15) from the high halves of two words
+__device__ __forceinline__ uint32_t hi16_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// three exact bf16 planes of 8 fp32 values
+__device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x8_t& hi, bf16x8_t& mid,
+                                       bf16x8_t& lo) {
+  const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = __float_as_uint(w[i]) & 0xffff0000u;
+    const float r = w[i] - __uint_as_float(h[i]);          // exact
+    m[i] = __float_as_uint(r) & 0xffff0000u;
+    l[i] = __float_as_uint(r - __uint_as_float(m[i]));     // exact; fits in bf16
+  }
+  uint4 ph, pm, pl;
+  ph.x = hi16_pair(h[0], h[1]); ph.y = hi16_pair(h[2], h[3]); ph.z = hi16_pair(h[4], h[5]); ph.w = hi16_pair(h[6], h[7]);
+  pm.x = hi16_pair(m[0], m[1]); pm.y = hi16_pair(m[2], m[3]); pm.z = hi16_pair(m[4], m[5]); pm.w = hi16_pair(m[6], m[7]);
+  pl.x = hi16_pair(l[0], l[1]); pl.y = hi16_pair(l[2], l[3]); pl.z = hi16_pair(l[4], l[5]); pl.w = hi16_pair(l[6], l[7]);
+  hi = __builtin_bit_cast(bf16x8_t, ph);
+  mid = __builtin_bit_cast(bf16x8_t, pm);
+  lo = __builtin_bit_cast(bf16x8_t, pl);
+}
+
+template <int TG, int NE>
+__global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(RouterArgs a) {
+  constexpr int TPB = 16 * TG;                // tokens per block
+  constexpr int EC = 16 * NE;                 // experts per pass
+  extern __shared__ float smem[];
+  float* part = smem;                         // [kMfWaves][TPB][EC]
+  float* lg = part + kMfWaves * TPB * EC;     // [TPB][E]
+  float* wcol = lg + TPB * a.E;               // [kMfWaves][E]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 8;             // first column of the lane within a step
+  const int t0 = blockIdx.x * TPB;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const int nks = (a.d + 31) / 32;
+  const int my = nks > wave ? (nks - wave + kMfWaves - 1) / kMfWaves : 0;   // k-steps of this wavefront
+
+  for (int e0 = 0; e0 < a.E; e0 += EC) {
+    uint4 xb[kMfPd][TG];
+    float4 wb[kMfPd][NE][2];
+    auto load = [&](int i, uint4 (&xs)[TG], float4 (&ws)[NE][2]) __attribute__((always_inline)) {
+      const int col = (wave + i * kMfWaves) * 32 + kq;
+      const bool kv = i < my && col < a.d;    // d % 8 == 0: a lane's 8 columns are all in or all out
+#pragma unroll
+      for (int g = 0; g < TG; ++g) {
+        const int t = t0 + g * 16 + r16;
+        xs[g] = (kv && t < a.T) ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * a.d + col)
+                                : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int n = 0; n < NE; ++n) {
+        const int e = e0 + n * 16 + r16;
+        if (kv && e < a.E) {
+          const float4* src = reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + col);
+          ws[n][0] = src[0];
+          ws[n][1] = src[1];
+        } else {
+          ws[n][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+          ws[n][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    };
+    f32x4_mf acc[TG][NE];
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+      for (int n = 0; n < NE; ++n) acc[g][n] = f32x4_mf{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMfPd; ++j) load(j, xb[j], wb[j]);
+    for (int i0 = 0; i0 < my; i0 += kMfPd) {
+#pragma unroll
+      for (int j = 0; j < kMfPd; ++j) {
+        if (i0 + j < my) {
+#pragma unroll
+          for (int n = 0; n < NE; ++n) {
+            bf16x8_t hi, mid, lo;
+            split3(wb[j][n][0], wb[j][n][1], hi, mid, lo);
+#pragma unroll
+            for (int g = 0; g < TG; ++g) {
+              const bf16x8_t xv = __builtin_bit_cast(bf16x8_t, xb[j][g]);
+              acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, hi, acc[g][n], 0, 0, 0);
+              acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, mid, acc[g][n], 0, 0, 0);
+              acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, lo, acc[g][n], 0, 0, 0);
+            }
+          }
+          load(i0 + j + kMfPd, xb[j], wb[j]);
+        }
+      }
+    }
+    // partial logits: lane holds expert n*16 + lane % 16 of tokens g*16 + 4 (lane / 16) + q
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+      for (int n = 0; n < NE; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          part[(wave * TPB + g * 16 + (lane >> 4) * 4 + q) * EC + n * 16 + r16] = acc[g][n][q];
+    __syncthreads();
+    for (int j = tid; j < TPB * EC; j += kMfThreads) {
+      const int tl = j / EC, ec = j % EC, e = e0 + ec;
+      if (e < a.E) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kMfWaves; ++w) s += part[(w * TPB + tl) * EC + ec];
+        lg[tl * a.E + e] = s + (a.b_g ? a.b_g[e] : 0.f);
+      }
+    }
+    __syncthreads();
+  }
+
+  // softmax + top-k: one wavefront per token
+  for (int e = lane; e < a.E; e += 64) wcol[wave * a.E + e] = 0.f;
+  for (int tl = wave; tl < TPB; tl += kMfWaves) {
+    const int t = t0 + tl;
+    if (t >= a.T) break;
+    token_softmax_topk(lg + tl * a.E, t, a, wcol + wave * a.E, lane);
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += kMfThreads) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMfWaves; ++w) v += wcol[w * a.E + e];
+    a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + e] = v;
+  }
+}
+
 // prob_colsum[e] = sum over blocks of the partial sums.  One block per
 // expert: strided partial sums in double, then a fixed-order tree, so the
 // result is deterministic and does not drift with the block count.
@@ -367,9 +525,38 @@ inline int stream_blocks(int T, int d) {
 // upper bound of the block count of either router kernel (per-block
 // probability partial sums live in the workspace)
 inline int router_max_blocks(int T) {
-  const int small = (T + kSmTpt - 1) / kSmTpt;   // stream kernel: at least kSmTpt tokens per block
+  const int small = (T + kSmTpt - 1) / kSmTpt;   // stream and MFMA kernels: at least 16 tokens per block
   const int generic = router_blocks(T);
   return small > generic ? small : generic;
+}
+
+
+// token groups of 16 per block of the MFMA router: enough blocks for the
+// CUs, more tokens per block (fewer W_g reads) for long batches
+inline int mfma_tg(int T) { return T >= 16384 ? 4 : (T >= 8192 ? 2 : 1); }
+// expert groups of 16 per pass (TG * NE <= 8 keeps the partial sums in LDS)
+inline int mfma_ne(int E, int tg) {
+  int ne = (E + 15) / 16;
+  ne = ne >= 4 ? 4 : (ne >= 2 ? 2 : 1);
+  while (tg * ne > 8) ne /= 2;
+  return ne;
+}
+inline size_t mfma_lds_bytes(int tg, int ne, int E) {
+  return (static_cast<size_t>(kMfWaves) * 16 * tg * 16 * ne + static_cast<size_t>(16) * tg * E +
+          static_cast<size_t>(kMfWaves) * E) * sizeof(float);
+}
+template <int TG, int NE>
+int launch_mfma(const RouterArgs& a, int nb, size_t lds, hipStream_t stream) {
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_mfma_kernel<TG, NE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) {
+      record_hip_error(e);
+      return MOE_ERR_HIP;
+    }
+  }
+  hipLaunchKernelGGL((router_mfma_kernel<TG, NE>), dim3(nb), dim3(kMfThreads), lds, stream, a);
+  return check_launch();
 }
 
 }  // namespace
@@ -402,9 +589,14 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
   if (prob_colsum && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
 
+  // bf16: the streaming VALU kernel for up to 8 experts (bound by reading x
+  // once), the MFMA kernel beyond; fp32 activations: the generic kernel
   const bool small = x_dt == MOE_BF16 && E <= kSmE && d % 8 == 0 && d <= 8 * kSmThreads;
+  const bool mf = x_dt == MOE_BF16 && !small;
   float* part = static_cast<float*>(workspace);
-  const int nb = small ? stream_blocks(T, d) : router_blocks(T);
+  const int tg = mfma_tg(T);
+  const int ne = mfma_ne(E, tg);
+  const int nb = small ? stream_blocks(T, d) : (mf ? (T + 16 * tg - 1) / (16 * tg) : router_blocks(T));
   if (T > 0 && small) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
     const int tpr = stream_tpr(d);
@@ -419,7 +611,18 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
     int st = check_launch();
     if (st != MOE_OK) return st;
   }
-  if (T > 0 && !small) {
+  if (T > 0 && mf) {
+    RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
+    const size_t lds = mfma_lds_bytes(tg, ne, E);
+    int st = MOE_OK;
+#define MOE_RT_MF(TG_, NE_) \
+  if (tg == TG_ && ne == NE_) st = launch_mfma<TG_, NE_>(a, nb, lds, stream);
+    MOE_RT_MF(1, 1) MOE_RT_MF(1, 2) MOE_RT_MF(1, 4) MOE_RT_MF(2, 1) MOE_RT_MF(2, 2) MOE_RT_MF(2, 4)
+    MOE_RT_MF(4, 1) MOE_RT_MF(4, 2)
+#undef MOE_RT_MF
+    if (st != MOE_OK) return st;
+  }
+  if (T > 0 && !small && !mf) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
     size_t lds = (static_cast<size_t>(kRtDc) * kRtTok + static_cast<size_t>(kRtDc) * kRtExp +
                   static_cast<size_t>(kRtTok) * E + 4 * static_cast<size_t>(E)) * sizeof(float);
