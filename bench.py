@@ -8,9 +8,10 @@ workload, with inputs already resident in HBM.  Prints one JSON line.
 
 The roofline object describes the grouped expert FFN (the only dense
 contraction, and the dominant cost): algorithmic FLOPs of one call over its
-mean duration, measured with HIP events on the stream the kernels run on.
-The CPU baseline times the float64 oracle on a bounded sample of the same
-workload on the host cores.
+median duration, measured with HIP events on the stream the kernels run on.
+A third pass repeats the steps after a 512 MB scratch write each ("cold":
+no input left in the last-level cache).  The CPU baseline times the float64
+oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -161,7 +162,7 @@ def main():
     ms_step = total_ms / args.steps
 
     # timed region 2: the same steps with HIP events between the stages, on
-    # the stream the kernels are launched on (per-stage times, roofline)
+    # the stream the kernels are launched on (per-stage medians, roofline)
     stages = ["router", "dispatch", "experts", "shared", "combine", "aux"]
     ev = {s: [] for s in stages}
     torch.cuda.synchronize()
@@ -183,7 +184,36 @@ def main():
         for i, s in enumerate(stages):
             ev[s].append((marks[i], marks[i + 1]))
     torch.cuda.synchronize()
-    st_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+    st_ms = {s: float(np.median([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+
+    # timed region 3 (reported apart, labelled cold): every step after a
+    # 512 MB scratch write, so that no input is left in the 256 MB
+    # last-level cache; the scratch write itself is outside the events
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold_step, cold_st = [], {s: [] for s in stages}
+    for _ in range(args.steps):
+        scratch.fill_(1)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        marks[0].record()
+        layer.router(x)
+        marks[1].record()
+        layer.dispatch(x)
+        marks[2].record()
+        layer.experts()
+        marks[3].record()
+        layer.shared(x)
+        marks[4].record()
+        layer.combine()
+        marks[5].record()
+        layer.aux()
+        marks[6].record()
+        torch.cuda.synchronize()
+        cold_step.append(marks[0].elapsed_time(marks[-1]))
+        for i, s in enumerate(stages):
+            cold_st[s].append(marks[i].elapsed_time(marks[i + 1]))
+    del scratch
+    cold_ms = float(np.median(cold_step))
+    cold_st_ms = {s: float(np.median(v)) for s, v in cold_st.items()}
 
     a_kept = int(layer.offsets[-1].item())
     ffn_flops = ffn_flops_per_row(cfg) * a_kept
@@ -212,7 +242,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": ffn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ffn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "moe_expert_ffn_grouped (routed experts): gate/up GEMM + down GEMM",
-                     "flops_per_launch": ffn_flops, "mean_ms": st_ms["experts"]},
+                     "flops_per_launch": ffn_flops, "median_ms": st_ms["experts"]},
         "stages_ms": st_ms,
         "stages_hbm_frac": {
             "router": byts["router"] / (st_ms["router"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -221,6 +251,13 @@ def main():
         },
         "shared_tflops": (sh_flops / (st_ms["shared"] * 1e-3) / 1e12) if cfg.n_shared else None,
         "kept_rows": a_kept,
+        "cold": {
+            "note": "median step with a 512 MB scratch write before each step (no input in the last-level cache)",
+            "ms_per_step": cold_ms, "value": cfg.T / (cold_ms * 1e-3), "stages_ms": cold_st_ms,
+            "stages_hbm_frac": {k_: byts[k_] / (cold_st_ms[k_] * 1e-3) / 1e9 / PEAK_HBM_GBPS
+                                for k_ in ("router", "dispatch", "combine")},
+            "ffn_tflops": ffn_flops / (cold_st_ms["experts"] * 1e-3) / 1e12,
+        },
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, arr, C, min(args.cpu_tokens, cfg.T))
