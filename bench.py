@@ -186,6 +186,25 @@ def main():
     torch.cuda.synchronize()
     st_ms = {s: float(np.median([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
 
+    # timed region 2b: each stage alone, `steps` back-to-back calls between
+    # one event pair (the stages are idempotent: each rewrites the same
+    # outputs from the same inputs).  An event recorded between two kernels
+    # costs a 6-11 us bubble before the next one, which region 2 charges to
+    # the short stages; here it is paid once per loop.  Inputs a stage re-reads
+    # stay in the last-level cache, as in the layer for all but the router.
+    def loop_ms(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+    loop_st_ms = {"router": loop_ms(lambda: layer.router(x)), "dispatch": loop_ms(lambda: layer.dispatch(x)),
+                  "combine": loop_ms(layer.combine), "aux": loop_ms(layer.aux)}
+
     # timed region 3 (reported apart, labelled cold): every step after a
     # 512 MB scratch write, so that no input is left in the 256 MB
     # last-level cache; the scratch write itself is outside the events
@@ -249,6 +268,9 @@ def main():
             "dispatch": byts["dispatch"] / (st_ms["dispatch"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "combine": byts["combine"] / (st_ms["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         },
+        "stages_ms_loop": loop_st_ms,
+        "stages_hbm_frac_loop": {k_: byts[k_] / (loop_st_ms[k_] * 1e-3) / 1e9 / PEAK_HBM_GBPS
+                                 for k_ in ("router", "dispatch", "combine")},
         "shared_tflops": (sh_flops / (st_ms["shared"] * 1e-3) / 1e12) if cfg.n_shared else None,
         "kept_rows": a_kept,
         "cold": {

@@ -464,11 +464,12 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
   const size_t row_bytes = copy_rows ? static_cast<size_t>(d) * dtype_bytes(x_dt) : 0;
   if (static_cast<long>(T) * k <= kFusedMaxEntries && row_bytes % 16 == 0) {
     // tokens per block: at most 16 row vectors per thread, at most 256 entries,
-    // and about 512 blocks when T allows
+    // and about 1024 blocks when T allows (four per CU: the row loads of one
+    // block overlap the index work and stores of the others)
     const int nvec = static_cast<int>(row_bytes / 16);
     int tpb = nvec > 0 ? (16 * kFusedThreads) / nvec : kFusedThreads;
     tpb = min(tpb, kFusedThreads / k);
-    tpb = min(tpb, max(1, (T + 511) / 512));
+    tpb = min(tpb, max(1, (T + 1023) / 1024));
     tpb = max(tpb, 1);
     const int nq = (tpb * nvec + kFusedThreads - 1) / kFusedThreads;
     const int nblk = (T + tpb - 1) / tpb;
