@@ -447,6 +447,8 @@ __device__ __forceinline__ SplitPlan split_plan(int V, int KT, int R, int n_cu, 
 //   SwiGLU: fragments j and j + 2 hold the gate and up columns of the same
 //   hidden units: 64 output columns, silu(gate) * up.
 //   Plain/ReLU: 128 output columns (+ bias).
+// e4m3 weights (p.s1 set): each column's accumulator is scaled by its weight
+// row's scale first.
 // row0: first output row of the wavefront, rows_valid: valid rows from there
 // (may be <= 0), col0: first output column (pieces at col0 + c >= N are
 // skipped; N % 8 == 0).  st must hold 32 FM x (OC + 8) bf16 of LDS that no
@@ -463,10 +465,14 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
   const int fc = lane >> 5;
 #pragma unroll
   for (int j = 0; j < OC / 32; ++j) {
-    float bias = 0.f;
-    if (EPI != EPI_SWIGLU && p.bias) {
-      const int col = col0 + j * 32 + fr;
-      bias = col < N ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+    const int col = col0 + j * 32 + fr;
+    float bias = 0.f, sg = 1.f, su = 1.f;
+    if (EPI != EPI_SWIGLU && p.bias) bias = col < N ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+    if (p.s1) {
+      // e4m3 weights: the row scales of the output columns (gate and up rows
+      // of the same hidden unit for SwiGLU)
+      sg = col < N ? p.s1[static_cast<size_t>(e) * N + col] : 0.f;
+      if (EPI == EPI_SWIGLU) su = col < N ? p.s3[static_cast<size_t>(e) * N + col] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -476,9 +482,9 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           if (EPI == EPI_SWIGLU) {
-            v[h] = silu_fast(acc[i][j][q + h]) * acc[i][j + 2][q + h];
+            v[h] = silu_fast(acc[i][j][q + h] * sg) * (acc[i][j + 2][q + h] * su);
           } else {
-            v[h] = acc[i][j][q + h] + bias;
+            v[h] = acc[i][j][q + h] * sg + bias;
             if (EPI == EPI_RELU) v[h] = fmaxf(v[h], 0.f);
           }
         }
@@ -572,19 +578,21 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 #pragma unroll
   for (int jj = 0; jj < (EPI == EPI_SWIGLU ? 2 : 4); ++jj) {
     const int lc = jj * 32 + fr;
-    float bias = 0.f;
-    if (EPI != EPI_SWIGLU && p.bias) {
-      const int col = t.nt * 256 + wn * 128 + lc;
-      bias = col < N ? p.bias[static_cast<size_t>(t.e) * N + col] : 0.f;
+    const int col = (EPI == EPI_SWIGLU ? t.nt * HC + wn * 64 : t.nt * 256 + wn * 128) + lc;
+    float bias = 0.f, sg = 1.f, su = 1.f;
+    if (EPI != EPI_SWIGLU && p.bias) bias = col < N ? p.bias[static_cast<size_t>(t.e) * N + col] : 0.f;
+    if (p.s1) {
+      sg = col < N ? p.s1[static_cast<size_t>(t.e) * N + col] : 0.f;
+      if (EPI == EPI_SWIGLU) su = col < N ? p.s3[static_cast<size_t>(t.e) * N + col] : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int lr = fi * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
       float v;
       if (EPI == EPI_SWIGLU) {
-        v = silu_fast(acc[jj][q]) * acc[jj + 2][q];
+        v = silu_fast(acc[jj][q] * sg) * (acc[jj + 2][q] * su);
       } else {
-        v = acc[jj][q] + bias;
+        v = acc[jj][q] * sg + bias;
         if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
       }
       ep[lr * kEpPitch + lc] = f32_to_bf16(v);
@@ -615,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 // tile and store raw accumulators.  (The tile body is a generic lambda
 // rather than a function template: written as a function, the register
 // allocator spilled some 200 accumulator registers around the stage loop.)
-template <int EPI, int BK>
+template <int EPI, int BK, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr int BM = 256;
   constexpr int R = 2;                  // split parts are whole stage pairs
@@ -651,9 +659,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     constexpr int NKS = BK / 16;            // MFMA k-steps per stage
     constexpr int WM = 32 * FM, WN = 128;
     constexpr int FN = WN / 32;
+    constexpr int CHB = FP8 ? CH / 2 : CH;    // 16-byte chunks per B row (e4m3: one byte per value)
+    constexpr int EB = FP8 ? 1 : 2;           // bytes per B value
     constexpr int LDA = BMA * CH / kThreads;  // DMA instructions per stage: A
-    constexpr int LDB = BN * CH / kThreads;   //   and B
-    constexpr int RPI = kThreads / CH;        // rows covered by one DMA instruction
+    constexpr int LDB = BN * CHB / kThreads;  //   and B
+    constexpr int RPI = kThreads / CH;        // rows covered by one DMA instruction: A
+    constexpr int RPIB = kThreads / CHB;      //   and B
     constexpr int HALF = BN * CH;             // uint4 per half-slot (one operand of one stage)
     static_assert(BK == 64 && (FM == 4 || FM == 2), "tile shapes");
     const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
@@ -678,11 +689,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
 #pragma unroll
     for (int i = 0; i < LDA; ++i)
       a_vo[i] = static_cast<uint32_t>((min(i * RPI + tid / CH, rows_valid - 1) * K + cq * 8) * 2);
+    const int cqb = (tid & (CHB - 1)) ^ ((tid >> 4) & (CHB - 1));
     const char* b_sb[LDB];
     uint32_t b_vo[LDB];
 #pragma unroll
     for (int i = 0; i < LDB; ++i) {
-      const int r = i * RPI + tid / CH;
+      const int r = i * RPIB + tid / CHB;
       int n;
       const void* base = p.B1;
       if (EPI == EPI_SWIGLU) {
@@ -690,13 +702,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
         // nt * HC + 64 w + (0..63), the next 64 the up rows of the same columns;
         // one instruction's RPI rows lie in one such half
         n = nt * HC + (r >> 7) * 64 + (r & 63);
-        if ((i * RPI) & 64) base = p.B3;
+        if ((i * RPIB) & 64) base = p.B3;
       } else {
         n = nt * BN + r;
       }
       n = min(n, N - 1);
-      b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(e) * N * K * 2);
-      b_vo[i] = static_cast<uint32_t>((n * K + cq * 8) * 2);
+      b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(e) * N * K * EB);
+      b_vo[i] = static_cast<uint32_t>(n * K * EB + cqb * 16);
     }
     const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
     // half-slot index (2 s + c) % 5 from (2 s) % 5 (both < 5)
@@ -707,7 +719,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       dma16(a_sb + (ks0 + st) * BK * 2, a_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
     };
     auto issue_b = [&](int st, int h, int q) __attribute__((always_inline)) {
-      dma16(b_sb[q] + (ks0 + st) * BK * 2, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+      dma16(b_sb[q] + (ks0 + st) * BK * EB, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
     };
     auto read_one = [&](const uint4* SA, const uint4* SB, int ks, int r, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN])
         __attribute__((always_inline)) {
@@ -718,6 +730,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
         uint4 v = SA[dma_swz<CH>(wm * WM + (r - FN) * 32 + fr, 2 * ks + fc)];
         fa[r - FN] = *reinterpret_cast<bf16x8_t*>(&v);
       }
+    };
+    // e4m3 weights: a lane reads 16 bytes of its B row per k-step pair p
+    // (columns 32 p + 16 fc + 0..15); the first 8 feed k-step 2 p, the other 8
+    // k-step 2 p + 1, so the A fragment of k-step ks takes bf16 chunk
+    // 4 (ks / 2) + 2 fc + ks % 2 (the same columns; any order of the k values
+    // inside one MFMA is fine as long as A and B agree).  The bytes are widened
+    // with v_cvt_scalef32_pk_bf16_fp8 (scale 1: exact for every finite code).
+    uint4 braw[FN];
+    auto read_a8 = [&](const uint4* SA, int ks, int i, bf16x8_t (&fa)[FM]) __attribute__((always_inline)) {
+      uint4 v = SA[dma_swz<CH>(wm * WM + i * 32 + fr, 4 * (ks >> 1) + 2 * fc + (ks & 1))];
+      fa[i] = *reinterpret_cast<bf16x8_t*>(&v);
+    };
+    auto read_b8 = [&](const uint4* SB, int pair, int j) __attribute__((always_inline)) {
+      braw[j] = SB[dma_swz<CHB>(wn * WN + j * 32 + fr, 2 * pair + fc)];
+    };
+    auto cvt_b8 = [&](int j, bool hi, bf16x8_t (&fb)[FN]) __attribute__((always_inline)) {
+      const uint32_t w0 = hi ? braw[j].z : braw[j].x;
+      const uint32_t w1 = hi ? braw[j].w : braw[j].y;
+      uint4 o;
+      o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+      o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+      o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+      o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+      fb[j] = __builtin_bit_cast(bf16x8_t, o);
     };
 
     f32x16_t acc[FM][FN];
@@ -783,9 +819,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
         auto& nb = (S & 1) ? fb0 : fb1;
         template_for<NQ>([&](auto qc) __attribute__((always_inline)) {
           constexpr int q = decltype(qc)::value;
-          mma_one(q, ca, cb);
+          if constexpr (FP8) {
+            // braw holds pair 0 (k-steps 0, 1) on entry, pair 1 from late in
+            // k-step 0: k-step 0 widens its B fragments on demand and those of
+            // k-step 1 next, k-step 1 those of k-step 2, k-step 2 those of 3
+            if constexpr (S == 0 && q < FN) cvt_b8(q, false, fb0);
+            mma_one(q, ca, cb);
+            if constexpr (q % (NQ / FM) == 0) read_a8(Ac, S + 1, q / (NQ / FM), na);
+            if constexpr (S == 0 && q >= FN && q < 2 * FN) cvt_b8(q - FN, true, fb1);
+            if constexpr (S == 0 && q >= NQ - FN) read_b8(Bc, 1, q - (NQ - FN));
+            if constexpr (S == 1 && q >= NQ - FN) cvt_b8(q - (NQ - FN), false, fb0);
+            if constexpr (S == 2 && q < FN) cvt_b8(q, true, fb1);
+          } else {
+            mma_one(q, ca, cb);
 #pragma unroll
-          for (int c = q * NRD / NQ; c < (q + 1) * NRD / NQ; ++c) read_one(Ac, Bc, S + 1, c, na, nb);
+            for (int c = q * NRD / NQ; c < (q + 1) * NRD / NQ; ++c) read_one(Ac, Bc, S + 1, c, na, nb);
+          }
           pre_dma(std::integral_constant<int, NM + S * NQ + q>{});
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -805,7 +854,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
         mma_one(kPre + q, fa1, fb1);
         if constexpr (decltype(next)::value) {
 #pragma unroll
-          for (int c = q * NRD / NM; c < (q + 1) * NRD / NM; ++c) read_one(An, Bn, 0, c, fa0, fb0);
+          for (int c = q * NRD / NM; c < (q + 1) * NRD / NM; ++c) {
+            if constexpr (FP8) {
+              if (c < FN) read_b8(Bn, 0, c);
+              else read_a8(An, 0, c - FN, fa0);
+            } else {
+              read_one(An, Bn, 0, c, fa0, fb0);
+            }
+          }
         }
         if constexpr (q % SB_ == 0 && decltype(postb)::value) issue_b(s + 2, cA, q / SB_);
         __builtin_amdgcn_sched_barrier(0);
@@ -832,7 +888,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       wait_vmcnt<LDA + LDB>();
     }
     lds_barrier();
-    {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) read_b8(ring + HALF, 0, j);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) read_a8(ring, 0, i, fa0);
+    } else {
 #pragma unroll
       for (int r = 0; r < FM + FN; ++r) read_one(ring, ring + HALF, 0, r, fa0, fb0);
     }
@@ -880,7 +941,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     tile(std::integral_constant<int, 4>{});
 }
 
-template <int EPI, int BK>
+template <int EPI, int BK, bool FP8>
 int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   const long n_tiles = (p.N + HC - 1) / HC;
@@ -893,8 +954,8 @@ int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
   GemmParams q = p;
   if (!split) q.split_max = 1;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                     q);
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK, FP8>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, q);
   int st = check_launch();
   if (st != MOE_OK || !split) return st;
   hipLaunchKernelGGL((split_reduce_kernel<EPI, BK>), dim3(static_cast<unsigned>(4 * p.n_cu)), dim3(kThreads), 0, stream,
@@ -936,12 +997,18 @@ int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, in
   // LDS-DMA kernel: bf16 weights, K a multiple of the ring's K per round,
   // 16-byte output rows (N % 8 == 0), and 31-bit byte offsets inside one
   // expert's weight matrix and one m-tile
-  const bool dma_ok = !fp8 && p.K % kDmaKMult == 0 && p.N % 8 == 0 && static_cast<size_t>(p.N) * p.K * 2 < (size_t(1) << 31) &&
+  const size_t wbytes = fp8 ? 1 : 2;
+  const bool dma_ok = p.K % kDmaKMult == 0 && p.N % 8 == 0 && static_cast<size_t>(p.N) * p.K * wbytes < (size_t(1) << 31) &&
                       static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31);
+  if (dma_ok && fp8) {
+    if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK, true>(p, m_tiles_max, stream);
+    if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK, true>(p, m_tiles_max, stream);
+    return launch_dma<EPI_PLAIN, kDmaBK, true>(p, m_tiles_max, stream);
+  }
   if (dma_ok) {
-    if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK>(p, m_tiles_max, stream);
-    if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK>(p, m_tiles_max, stream);
-    return launch_dma<EPI_PLAIN, kDmaBK>(p, m_tiles_max, stream);
+    if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK, false>(p, m_tiles_max, stream);
+    if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK, false>(p, m_tiles_max, stream);
+    return launch_dma<EPI_PLAIN, kDmaBK, false>(p, m_tiles_max, stream);
   }
   return launch_epi<kGemmBM, 128, 1>(epi, fp8, p, m_tiles_max, stream);
 }

@@ -79,6 +79,13 @@ EDGE = {
     # MFMA router at the largest expert count (four experts per lane slot)
     "router_e256": _cfg("router_e256", T=1100, d=256, E=256, k=8, ffn="linear", d_ff=0, gate="renorm",
                         wg_dist=("normal", 1 / 256), w1_var=1 / 256, seed=34),
+    # e4m3 weights on the LDS-DMA GEMM (K % 128 == 0): ReLU with biases, and a
+    # Linear layer whose output width is off the 256-column tiles
+    "fp8_dma_relu_bias": _cfg("fp8_dma_relu_bias", T=300, d=256, E=6, k=2, ffn="relu", d_ff=384, gate="renorm",
+                              w_dtype="fp8", wg_dist=("normal", 1 / 256), w1_var=1 / 256, w2_var=1 / 384,
+                              b1_var=0.1, b2_var=0.1, seed=35),
+    "fp8_dma_linear": _cfg("fp8_dma_linear", T=260, d=384, d_out=200, E=5, k=2, ffn="linear", d_ff=0, gate="prob",
+                           w_dtype="fp8", wg_dist=("normal", 1 / 384), w1_var=1 / 384, seed=36),
     "t1": _cfg("t1", T=1, d=64, E=4, k=2, ffn="swiglu", d_ff=64, gate="renorm", wg_dist=("normal", 1 / 64),
                w1_var=1 / 64, w3_var=1 / 64, w2_var=1 / 64, seed=29),
 }
