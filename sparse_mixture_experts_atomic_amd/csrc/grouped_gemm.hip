@@ -6,25 +6,21 @@
 // of P1 §3.2 / P3 §3.1 / P4 公式：三步走, one batch per expert as P1 §2.4
 // describes).
 //
-// Design (gfx950 / CDNA4):
-//  * block tile BM x BN (weight rows) x 32 (K per stage), 4 wavefronts in a
-//    2x2 grid; each wavefront owns a (BM/2) x (BN/2) accumulator tile made of
-//    v_mfma_f32_32x32x16_bf16 fragments.  On gfx950 this instruction reaches
-//    the bf16 peak with a handful of independent accumulators per wavefront,
-//    and a 128x128 wave tile needs ~64 B of LDS reads per 4096 FLOP, inside
-//    the ~100-150 B/clk a CU's LDS delivers
-//  * global -> registers one stage (64 of K) ahead, registers -> LDS double
-//    buffer, one barrier per stage; LDS rows are 32 bf16 = 4 chunks of 16 B, chunk c of
-//    row r stored at c ^ ((r >> 2) & 3) so 16 fragment rows hit 16 distinct
-//    bank groups
-//  * fp8 e4m3 weights are widened to bf16 on the way into LDS (exact); the
-//    per-output-row scale multiplies the fp32 accumulator in the epilogue
-//  * SwiGLU: each wavefront's weight rows are half gate rows and half up rows
-//    of the same hidden columns, so silu(gate) * up is formed in registers
-//  * tiles are numbered so that the blocks resident on one XCD (blockIdx %
-//    8) take a contiguous range, m-tiles of a group of n-tiles innermost, and
-//    the valid tiles (known only on the device) are spread evenly over the
-//    eight XCDs.
+// Two kernels share one device-built tile map (segment, m-tile, n-tile per
+// block; no count goes back to the host) and the XCD-aware tile order (the
+// blocks resident on one XCD, blockIdx % 8, take a contiguous range of
+// tiles, m-tiles of a group of n-tiles innermost):
+//  * grouped_gemm_dma_kernel (bf16 or e4m3 weights, K % 128 == 0): 256 x 256
+//    tiles (128 x 256 for short segment tails), four wavefronts of 128 x 128
+//    v_mfma_f32_32x32x16_bf16 fragments, operands moved global -> LDS by
+//    global_load_lds_dwordx4 through a ring of five 32 KB half-slots, one DMA
+//    every fourth MFMA; see the comments at the kernel.
+//  * grouped_gemm_kernel (the rest): 256 x 128 tiles, 2x2 wavefronts,
+//    register prefetch one stage ahead into a double-buffered LDS; e4m3
+//    weights are widened to bf16 on the way into LDS (exact).
+// In both, e4m3 row scales multiply the fp32 accumulators in the epilogue,
+// and for SwiGLU each wavefront's weight rows are half gate and half up rows
+// of the same hidden columns, so silu(gate) * up is formed in registers.
 #include <type_traits>
 #include <utility>
 
@@ -77,6 +73,13 @@ __device__ __forceinline__ int find_segment(const int32_t* ts, int E, int m) {
   return lo;
 }
 
+// Register-staged kernel for shapes the DMA kernel does not take (K not a
+// multiple of 128): block tile BM x BN (weight rows), 4 wavefronts in a 2x2
+// grid, each owning a (BM/2) x (BN/2) accumulator tile; global -> registers
+// one stage ahead, registers -> a double-buffered LDS, one barrier per stage.
+// LDS rows of 32 bf16 = 4 chunks of 16 B, chunk c of row r stored at
+// c ^ ((r >> 2) & 3) so 16 fragment rows hit 16 distinct bank groups; K tails
+// load a clamped address and select zero.
 template <int BM, int BN, int NH, int EPI, bool B_FP8>
 __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
   constexpr int WM = BM / 2, WN = BN / 2;        // wave tile
