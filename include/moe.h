@@ -182,6 +182,14 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
  *             are left untouched
  * Accumulation is fp32.  With bf16 activations the hidden layer is rounded
  * to bf16 between the two matrix products.
+ * Constraints: E <= 1024; with bf16 activations d and d_ff multiples of 8
+ * (16 for fp8 weights); no biases with SWIGLU (else MOE_ERR_UNSUPPORTED).
+ * w3 must be given exactly for SWIGLU, w2 exactly for RELU / SWIGLU, the
+ * scales exactly for fp8 weights, no b2 for LINEAR (else
+ * MOE_ERR_INVALID_ARG).  max_rows == 0 returns MOE_OK without launching.
+ * Products with K % 128 == 0 go through the LDS-DMA kernel, others through
+ * the register-staged one; results differ only in the order of the fp32
+ * accumulation.
  */
 size_t moe_ffn_workspace_size(int kind, int act_dt, int max_rows, int E, int d, int d_ff, int d_out);
 int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
