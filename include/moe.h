@@ -114,7 +114,8 @@ int moe_capacity(int T, int k, int E, double cf, int round_mode);
  *   prob_colsum [E]     fp32 out or NULL: sum over tokens of the softmax
  *                       probabilities (the P_e numerator of the aux loss)
  *   logits_dbg  [T, E]  fp32 out or NULL: the fp32 router logits
- * Constraints: 1 <= k <= E, T >= 0, d >= 1 (else MOE_ERR_INVALID_ARG);
+ * Constraints: 1 <= k <= E, T >= 0, d >= 1, d % 8 == 0 for bf16 x (else
+ * MOE_ERR_INVALID_ARG);
  * E <= 256 and k <= 64 (else MOE_ERR_UNSUPPORTED).  T == 0 writes zeros to
  * prob_colsum and returns MOE_OK.  The workspace is needed whenever T > 0
  * or prob_colsum is requested.

@@ -80,6 +80,47 @@ __device__ __forceinline__ void token_softmax_topk(const float* z, int t, const 
   }
 }
 
+// fp32 softmax and top-k of one token's logits, E <= 8, by a group of 8
+// consecutive lanes: lane e of the group holds logit z of expert e (-inf past
+// E).  k rounds of a group arg-max (largest logit, lower id on ties); lane j
+// of the group keeps the winner of round j.  Writes the outputs of token t
+// when t < T and returns the lane's probability (0 past E or T).
+__device__ __forceinline__ float token8_softmax_topk(float z, int e, int t, const RouterArgs& a) {
+  if (t >= a.T) return 0.f;                   // whole groups leave together
+  float m = z;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 8));
+  const float ex = e < a.E ? expf(z - m) : 0.f;
+  float s = ex;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, 8);
+  const float p = ex * (1.0f / s);
+  if (a.logits_dbg && e < a.E) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z;
+  bool taken = e >= a.E;
+  float psum = 0.f, myp = 0.f;
+  int myi = 0;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = taken ? -INFINITY : z;
+    int bi = taken ? 0x7fffffff : e;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 8);
+      const int oi = __shfl_xor(bi, o, 8);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const float pw = __shfl(p, bi, 8);        // probability of the winner
+    if (bi == e) taken = true;
+    if (e == j) { myp = pw; myi = bi; }
+    psum += pw;
+  }
+  if (e < a.k) {
+    const size_t o = static_cast<size_t>(t) * a.k + e;
+    a.topk_idx[o] = myi;
+    a.topk_gate[o] = a.mode == MOE_GATE_RENORM ? myp / psum : myp;
+  }
+  return p;
+}
+
 // One block = 32 tokens x all E experts.  Logits are accumulated in
 // registers (2 tokens x 4 experts per thread per 64-expert group) from LDS
 // tiles of x and W_g, then kept in LDS for the softmax/top-k phase, which
@@ -180,165 +221,6 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
   }
 }
 
-// Streaming router for few experts (E <= 8), bf16 activations, d % 8 == 0,
-// d <= 4096.  The work is bound by reading x once.  A block of 512 threads is
-// split into token lanes of TPR threads; thread c of a lane keeps the fp32
-// router weights of column chunk c (8 columns x 8 experts) in registers and
-// streams the lane's tokens in halves of kSmTph: one 16-byte load and 64 FMAs
-// per token, the next half's loads in flight while the current half is
-// reduced.  The kSmTph x 8 per-thread partial logits of a half are
-// reduce-scattered over the wavefront (each lane ends with one sum), the
-// TPR / 64 wavefronts of a lane are added in LDS in a fixed order, and one
-// thread per token does the fp32 softmax and top-k.  Per-block probability
-// column sums go to the workspace for colsum_reduce_kernel.
-constexpr int kSmE = 8;
-constexpr int kSmThreads = 512;
-constexpr int kSmTph = 8;                     // tokens per thread and half
-constexpr int kSmHalves = 2;
-constexpr int kSmTpt = kSmTph * kSmHalves;    // tokens per thread
-constexpr int kSmNv = kSmTph * kSmE;          // partial logits per thread and half (64)
-
-template <int TPR>
-__global__ __launch_bounds__(kSmThreads) void router_stream_kernel(RouterArgs a) {
-  constexpr int G = kSmThreads / TPR;         // token lanes per block
-  constexpr int WPL = TPR / 64;               // wavefronts per token lane
-  constexpr int TPB = G * kSmTpt;             // tokens per block
-  static_assert(kSmNv == 64, "one reduced value per lane");
-  __shared__ float wred[kSmHalves][kSmThreads / 64][kSmNv];
-  __shared__ float lg[TPB][kSmE];
-  __shared__ float pr[TPB][kSmE];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int c = tid % TPR;                    // column chunk
-  const int g = tid / TPR;                    // token lane
-  const int nchunk = a.d / 8;
-  const int t0 = blockIdx.x * TPB;
-  const int tl0 = t0 + g * kSmTpt;            // first token of this lane
-  const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  const bool cv = c < nchunk;
-
-  auto load_half = [&](int h, uint4 (&dst)[kSmTph]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kSmTph; ++i) {
-      const int t = tl0 + h * kSmTph + i;
-      dst[i] = (cv && t < a.T) ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * a.d + c * 8)
-                               : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  uint4 xa[kSmTph], xb[kSmTph];
-  load_half(0, xa);
-  float w[kSmE][8];
-#pragma unroll
-  for (int e = 0; e < kSmE; ++e) {
-    if (cv && e < a.E) {
-      const float4 lo = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + c * 8);
-      const float4 hi = *reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + c * 8 + 4);
-      w[e][0] = lo.x; w[e][1] = lo.y; w[e][2] = lo.z; w[e][3] = lo.w;
-      w[e][4] = hi.x; w[e][5] = hi.y; w[e][6] = hi.z; w[e][7] = hi.w;
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) w[e][q] = 0.f;
-    }
-  }
-  load_half(1, xb);
-  auto half = [&](int h, const uint4 (&xv)[kSmTph]) __attribute__((always_inline)) {
-    float v[kSmNv];                           // entry i * 8 + e
-#pragma unroll
-    for (int i = 0; i < kSmTph; ++i) {
-      const uint32_t q[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-      float xf[8];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        xf[2 * m] = __uint_as_float(q[m] << 16);
-        xf[2 * m + 1] = __uint_as_float(q[m] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int e = 0; e < kSmE; ++e) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) s = fmaf(xf[m], w[e][m], s);
-        v[i * kSmE + e] = s;
-      }
-    }
-    // reduce-scatter over the wavefront: in the round with partner lane ^ o
-    // the lane keeps the upper half of its entries if (lane & o), so after
-    // the six rounds lane l holds entry l summed over all 64 lanes
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
-      const int o = 32 >> r;
-      const int n = kSmNv >> (r + 1);
-      const bool upper = (lane & o) != 0;
-#pragma unroll
-      for (int i = 0; i < n; ++i) {
-        const float send = upper ? v[i] : v[i + n];
-        const float keep = upper ? v[i + n] : v[i];
-        v[i] = keep + __shfl_xor(send, o);
-      }
-    }
-    wred[h][wave][lane] = v[0];
-  };
-  half(0, xa);
-  half(1, xb);
-  __syncthreads();
-  // logits: token lane gg, half h, entry en = i * 8 + e, summed over the
-  // lane's wavefronts
-  for (int j = tid; j < kSmHalves * G * kSmNv; j += kSmThreads) {
-    const int h = j / (G * kSmNv);
-    const int gg = (j / kSmNv) % G, en = j % kSmNv;
-    float sum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < WPL; ++ww) sum += wred[h][gg * WPL + ww][en];
-    const int e = en % kSmE;
-    lg[gg * kSmTpt + h * kSmTph + en / kSmE][e] = sum + ((a.b_g && e < a.E) ? a.b_g[e] : 0.f);
-  }
-  __syncthreads();
-  if (tid < TPB) {
-    const int t = t0 + tid;
-    const float* z = lg[tid];
-    float p[kSmE];
-    for (int e = 0; e < kSmE; ++e) p[e] = 0.f;
-    if (t < a.T) {
-      float m = -INFINITY;
-      for (int e = 0; e < a.E; ++e) m = fmaxf(m, z[e]);
-      float s = 0.f;
-      for (int e = 0; e < a.E; ++e) { p[e] = expf(z[e] - m); s += p[e]; }
-      const float inv = 1.0f / s;
-      for (int e = 0; e < a.E; ++e) {
-        p[e] *= inv;
-        if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z[e];
-      }
-      // top-k by repeated selection (largest logit, lower index on ties)
-      uint32_t taken = 0;
-      float psum = 0.f;
-      float ps[kSmE];
-      int is[kSmE];
-      for (int j = 0; j < a.k; ++j) {
-        int bi = -1;
-        float bv = -INFINITY;
-        for (int e = 0; e < a.E; ++e)
-          if (!((taken >> e) & 1u) && (bi < 0 || z[e] > bv)) { bv = z[e]; bi = e; }
-        taken |= 1u << bi;
-        is[j] = bi;
-        ps[j] = p[bi];
-        psum += p[bi];
-      }
-      for (int j = 0; j < a.k; ++j) {
-        a.topk_idx[static_cast<size_t>(t) * a.k + j] = is[j];
-        a.topk_gate[static_cast<size_t>(t) * a.k + j] = a.mode == MOE_GATE_RENORM ? ps[j] / psum : ps[j];
-      }
-    }
-    for (int e = 0; e < kSmE; ++e) pr[tid][e] = p[e];
-  }
-  __syncthreads();
-  // block column sums in token order
-  if (tid < a.E) {
-    float cs = 0.f;
-    for (int i = 0; i < TPB; ++i) cs += pr[i][tid];
-    a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + tid] = cs;
-  }
-}
-
 // MFMA router for bf16 activations.  W_g is split exactly into three bf16
 // planes, w = hi + mid + lo, each the truncation of what the previous ones
 // leave (a float's 24-bit significand in three 8-bit pieces), so every
@@ -361,6 +243,11 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_mf;
 // bf16 pair (lo in bits 0-15) from the high halves of two words
 __device__ __forceinline__ uint32_t hi16_pair(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// the value of lane (l + 8) mod 16 of the same 16-lane row (DPP row_ror:8)
+__device__ __forceinline__ float dpp_swap8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
 }
 
 // three exact bf16 planes of 8 fp32 values
@@ -491,6 +378,137 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(RouterArgs a) {
   }
 }
 
+// MFMA router for bf16 activations and at most 8 experts.  A block takes tg
+// groups of 16 tokens; the kw wavefronts of a group split the columns into
+// 128-column chunks, two per wavefront and round (wavefront j takes chunks j
+// and j + kw of each run of 2 kw).  A chunk is four 32-column k-steps of
+// v_mfma_f32_16x16x32_bf16 with the tokens as rows: a lane loads 16 bytes of
+// x per k-step (token lane % 16, columns 8 (lane / 16) ..).  W_g is split
+// exactly into bf16 planes as in router_mfma_kernel; the first MFMA's B
+// operand holds hi of expert n in column n < 8 and mid of expert n - 8 in
+// column n >= 8, the second adds lo in columns < 8, so logit e is column e
+// plus column e + 8.  Lanes n and n + 8 need the same eight fp32 values of
+// W_g row n % 8: each loads one half (so that a wavefront's load covers eight
+// whole 128-byte rows) and takes the other half from its partner by DPP.
+// The W_g loads go out before the x loads and are split while x is in
+// flight: moving W_g from L2 costs more than the split.  The wavefronts'
+// partial logits are added in LDS in wavefront order; 8 lanes per token do
+// the fp32 softmax and top-k.
+constexpr int kM8MaxE = 8;
+constexpr int kM8Cpw = 2;                     // chunks per wavefront and round
+constexpr int kM8Waves = 16;                  // at most, per block
+constexpr int kM8Tok = 16 * kM8Waves;         // at most, per block
+constexpr int kCUs = 256;                     // compute units of an MI355X
+
+__global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a, int kw, int tg) {
+  __shared__ float part[kM8Waves][16][16];
+  __shared__ float lg[kM8Tok][kM8MaxE];
+  __shared__ float pr[kM8Tok][kM8MaxE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nthr = 64 * kw * tg;
+  const int tpb = 16 * tg;
+  const int g = wave / kw;                    // token group
+  const int kv = wave % kw;                   // column slot
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const int t0 = blockIdx.x * tpb;
+  const int t = t0 + g * 16 + r16;
+  const bool tv = t < a.T;
+  const int e = r16 & 7;
+  const bool ev = e < a.E;
+  const bool hl = r16 < 8;
+  // loads are unconditional (clamped rows and columns) so that the compiler
+  // can wait for them one by one; W_g columns past d and rows past E are
+  // zeroed after the load, rows of x past T only feed discarded logits
+  const uint16_t* xr = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(tv ? t : a.T - 1) * a.d;
+  const float* wr = a.w_g + static_cast<size_t>(ev ? e : a.E - 1) * a.d;
+  f32x4_mf acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.d; c0 += 2 * kw * 128) {
+    float4 wb[kM8Cpw][4];                     // columns 0-3 (lanes < 8) or 4-7 of the lane's eight
+    uint4 xb[kM8Cpw][4];
+    bool ok[kM8Cpw][4];
+#pragma unroll
+    for (int i = 0; i < kM8Cpw; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int col = c0 + (kv + i * kw) * 128 + s * 32 + kq;
+        ok[i][s] = ev && col < a.d;           // d % 8 == 0: a lane's 8 columns are all in or all out
+        const int cc = col < a.d ? col : a.d - 8;
+        wb[i][s] = *reinterpret_cast<const float4*>(wr + cc + (hl ? 0 : 4));
+      }
+#pragma unroll
+    for (int i = 0; i < kM8Cpw; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int col = c0 + (kv + i * kw) * 128 + s * 32 + kq;
+        xb[i][s] = *reinterpret_cast<const uint4*>(xr + (col < a.d ? col : a.d - 8));
+      }
+    // every load of the round is in flight before the first use
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 b1[kM8Cpw][4], b2[kM8Cpw][4];
+#pragma unroll
+    for (int i = 0; i < kM8Cpw; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // lanes n and n + 8 hold the two halves of the same eight W_g values
+        const float4 mine = wb[i][s];
+        const float4 other = make_float4(dpp_swap8(mine.x), dpp_swap8(mine.y), dpp_swap8(mine.z), dpp_swap8(mine.w));
+        bf16x8_t hi, mid, lo;
+        split3(hl ? mine : other, hl ? other : mine, hi, mid, lo);
+        const uint4 h = __builtin_bit_cast(uint4, hi), m = __builtin_bit_cast(uint4, mid),
+                    l = __builtin_bit_cast(uint4, lo);
+        // a mask rather than a select of the loaded values, which the
+        // compiler would turn into a conditional load waited for at once
+        const uint32_t m1 = ok[i][s] ? ~0u : 0u, m2 = (ok[i][s] && hl) ? ~0u : 0u;
+        b1[i][s] = hl ? h : m;
+        b1[i][s].x &= m1; b1[i][s].y &= m1; b1[i][s].z &= m1; b1[i][s].w &= m1;
+        b2[i][s] = make_uint4(l.x & m2, l.y & m2, l.z & m2, l.w & m2);
+      }
+    // the planes are ready before the first wait for x
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kM8Cpw; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8_t xv = __builtin_bit_cast(bf16x8_t, xb[i][s]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8_t, b1[i][s]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8_t, b2[i][s]), acc, 0, 0, 0);
+      }
+  }
+  // lane holds column r16 of tokens 4 (lane / 16) + q of its group
+#pragma unroll
+  for (int q = 0; q < 4; ++q) part[wave][(lane >> 4) * 4 + q][r16] = acc[q];
+  __syncthreads();
+  for (int j = tid; j < tpb * kM8MaxE; j += nthr) {
+    const int tl = j / kM8MaxE, ee = j % kM8MaxE;
+    float z = 0.f;
+    if (ee < a.E) {
+      const int gg = tl / 16, tr = tl % 16;
+      for (int w = 0; w < kw; ++w) {
+        const float* pp = part[gg * kw + w][tr];
+        z += pp[ee] + pp[ee + 8];
+      }
+      if (a.b_g) z += a.b_g[ee];
+    }
+    lg[tl][ee] = z;
+  }
+  __syncthreads();
+  // groups of 8 lanes per token (the stride keeps groups whole)
+  for (int j = tid; j < tpb * kM8MaxE; j += nthr) {
+    const int tl = j / kM8MaxE, ee = j % kM8MaxE;
+    pr[tl][ee] = token8_softmax_topk(ee < a.E ? lg[tl][ee] : -INFINITY, ee, t0 + tl, a);
+  }
+  __syncthreads();
+  // block column sums in token order
+  if (tid < a.E) {
+    float cs = 0.f;
+    for (int i = 0; i < tpb; ++i) cs += pr[i][tid];
+    a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + tid] = cs;
+  }
+}
+
 // prob_colsum[e] = sum over blocks of the partial sums.  One block per
 // expert: strided partial sums in double, then a fixed-order tree, so the
 // result is deterministic and does not drift with the block count.
@@ -510,27 +528,27 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* part, i
 
 inline int router_blocks(int T) { return (T + kRtTok - 1) / kRtTok; }
 
-// block count of the streaming kernel for d columns (threads per token
-// lane: a power of two >= 64 covering the d/8 chunks)
-inline int stream_tpr(int d) {
-  int tpr = 64;
-  while (tpr < d / 8) tpr *= 2;
-  return tpr;
-}
-inline int stream_blocks(int T, int d) {
-  const int tpb = (kSmThreads / stream_tpr(d)) * kSmTpt;
-  return (T + tpb - 1) / tpb;
-}
-
-// upper bound of the block count of either router kernel (per-block
+// upper bound of the block count of any router kernel (per-block
 // probability partial sums live in the workspace)
 inline int router_max_blocks(int T) {
-  const int small = (T + kSmTpt - 1) / kSmTpt;   // stream and MFMA kernels: at least 16 tokens per block
+  const int mfma = (T + 15) / 16;             // MFMA kernels: at least 16 tokens per block
   const int generic = router_blocks(T);
-  return small > generic ? small : generic;
+  return mfma > generic ? mfma : generic;
 }
 
 
+// wavefronts per token group (two 128-column chunks each per round) and token
+// groups per block of router_mf8_kernel: whole rows in one round up to 4096
+// columns; more tokens per block for narrow rows while the grid keeps at
+// least one block per CU
+inline void mf8_shape(int T, int d, int& kw, int& tg) {
+  const int nch = (d + 127) / 128;
+  kw = (nch + kM8Cpw - 1) / kM8Cpw;
+  if (kw > kM8Waves) kw = kM8Waves;
+  tg = T / (16 * kCUs);
+  if (tg > kM8Waves / kw) tg = kM8Waves / kw;
+  if (tg < 1) tg = 1;
+}
 // token groups of 16 per block of the MFMA router: enough blocks for the
 // CUs, more tokens per block (fewer W_g reads) for long batches
 inline int mfma_tg(int T) { return T >= 16384 ? 4 : (T >= 8192 ? 2 : 1); }
@@ -579,6 +597,7 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
   if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (E > kRtMaxE || k > kRtMaxK) return MOE_ERR_UNSUPPORTED;
   if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (x_dt == MOE_BF16 && d % 8 != 0) return MOE_ERR_INVALID_ARG;   // 16-byte row pieces
   if (gate_mode != MOE_GATE_PROB && gate_mode != MOE_GATE_RENORM) return MOE_ERR_INVALID_ARG;
   if (!w_g || !aligned16(w_g) || (b_g && !aligned16(b_g))) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!x || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
@@ -589,25 +608,20 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
   if (prob_colsum && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
 
-  // bf16: the streaming VALU kernel for up to 8 experts (bound by reading x
-  // once), the MFMA kernel beyond; fp32 activations: the generic kernel
-  const bool small = x_dt == MOE_BF16 && E <= kSmE && d % 8 == 0 && d <= 8 * kSmThreads;
-  const bool mf = x_dt == MOE_BF16 && !small;
+  // bf16: the MFMA kernels (the one for up to 8 experts takes whole rows per
+  // block); fp32 activations: the generic kernel
+  const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE;
+  const bool mf = x_dt == MOE_BF16 && !m8;
   float* part = static_cast<float*>(workspace);
   const int tg = mfma_tg(T);
   const int ne = mfma_ne(E, tg);
-  const int nb = small ? stream_blocks(T, d) : (mf ? (T + 16 * tg - 1) / (16 * tg) : router_blocks(T));
-  if (T > 0 && small) {
+  int kw8 = 1, tg8 = 1;
+  mf8_shape(T, d, kw8, tg8);
+  const int nb = m8 ? (T + 16 * tg8 - 1) / (16 * tg8)
+                    : (mf ? (T + 16 * tg - 1) / (16 * tg) : router_blocks(T));
+  if (T > 0 && m8) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
-    const int tpr = stream_tpr(d);
-    if (tpr == 64)
-      hipLaunchKernelGGL(router_stream_kernel<64>, dim3(nb), dim3(kSmThreads), 0, stream, a);
-    else if (tpr == 128)
-      hipLaunchKernelGGL(router_stream_kernel<128>, dim3(nb), dim3(kSmThreads), 0, stream, a);
-    else if (tpr == 256)
-      hipLaunchKernelGGL(router_stream_kernel<256>, dim3(nb), dim3(kSmThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(router_stream_kernel<512>, dim3(nb), dim3(kSmThreads), 0, stream, a);
+    hipLaunchKernelGGL(router_mf8_kernel, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
     int st = check_launch();
     if (st != MOE_OK) return st;
   }
@@ -622,7 +636,7 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
 #undef MOE_RT_MF
     if (st != MOE_OK) return st;
   }
-  if (T > 0 && !small && !mf) {
+  if (T > 0 && !mf && !m8) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
     size_t lds = (static_cast<size_t>(kRtDc) * kRtTok + static_cast<size_t>(kRtDc) * kRtExp +
                   static_cast<size_t>(kRtTok) * E + 4 * static_cast<size_t>(E)) * sizeof(float);

@@ -75,6 +75,8 @@ def test_router_validation_before_launch():
     assert lib.moe_router_topk(fake, 7, fake, None, 8, 16, 4, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_INVALID_ARG
     assert lib.moe_router_topk(fake, L.BF16, None, None, 8, 16, 4, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_INVALID_ARG
     assert lib.moe_router_topk(fake + 4, L.BF16, fake, None, 8, 16, 4, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_INVALID_ARG
+    # bf16 rows are read in 16-byte pieces: the width must be a multiple of 8
+    assert lib.moe_router_topk(fake, L.BF16, fake, None, 8, 12, 4, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_INVALID_ARG
     assert lib.moe_router_topk(fake, L.BF16, fake, None, 8, 16, 4, 2, 0, fake, fake, None, None, None, 0, None) == L.ERR_WORKSPACE
     assert lib.moe_router_topk(fake, L.BF16, fake, None, 8, 16, 512, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_UNSUPPORTED
 

@@ -86,6 +86,14 @@ EDGE = {
                               b1_var=0.1, b2_var=0.1, seed=35),
     "fp8_dma_linear": _cfg("fp8_dma_linear", T=260, d=384, d_out=200, E=5, k=2, ffn="linear", d_ff=0, gate="prob",
                            w_dtype="fp8", wg_dist=("normal", 1 / 384), w1_var=1 / 384, seed=36),
+    # E <= 8 MFMA router: rows wider than one round of chunks, with a last
+    # chunk of 8 columns; seven experts, router bias
+    "router_e8_wide": _cfg("router_e8_wide", T=300, d=4360, d_out=16, E=7, k=3, ffn="linear", d_ff=0,
+                           gate="renorm", wg_dist=("normal", 1 / 4360), bg_var=0.5, w1_var=1 / 4360, seed=37),
+    # E <= 8 MFMA router with several token groups per block (narrow rows,
+    # long batch) and a ragged last block
+    "router_e8_groups": _cfg("router_e8_groups", T=8200, d=64, d_out=16, E=8, k=2, ffn="linear", d_ff=0,
+                             gate="prob", wg_dist=("normal", 1 / 64), w1_var=1 / 64, seed=38),
     "t1": _cfg("t1", T=1, d=64, E=4, k=2, ffn="swiglu", d_ff=64, gate="renorm", wg_dist=("normal", 1 / 64),
                w1_var=1 / 64, w3_var=1 / 64, w2_var=1 / 64, seed=29),
 }
