@@ -9,7 +9,7 @@
 // Two kernels share one device-built tile map (segment, m-tile, n-tile per
 // block; no count goes back to the host) and the XCD-aware tile order (the
 // blocks resident on one XCD, blockIdx % 8, take a contiguous range of
-// tiles, m-tiles of a group of n-tiles innermost):
+// tiles; per group of n-tiles: segment, n-tile, then the segment's m-tiles):
 //  * grouped_gemm_dma_kernel (bf16 or e4m3 weights, K % 128 == 0): 256 x 256
 //    tiles (128 x 256 for short segment tails), four wavefronts of 128 x 128
 //    v_mfma_f32_32x32x16_bf16 fragments, operands moved global -> LDS by
@@ -107,10 +107,12 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
   const int grp = L / (m_total * kNGroup);
   const int gs = min(kNGroup, n_tiles - grp * kNGroup);
   const int Lr = L - grp * m_total * kNGroup;
-  const int mt_g = Lr / gs;
-  const int nt = grp * kNGroup + Lr % gs;
+  const int e = find_segment(p.ts, p.E, Lr / gs);
+  const int me = p.ts[e + 1] - p.ts[e];
+  const int r = Lr - p.ts[e] * gs;
+  const int mt_g = p.ts[e] + r % me;
+  const int nt = grp * kNGroup + r / me;
 
-  const int e = find_segment(p.ts, p.E, mt_g);
   const int seg0 = p.offsets[e];
   const int seg1 = p.offsets[e + 1];
   const int row0 = seg0 + (mt_g - p.ts[e]) * BM;
@@ -513,7 +515,10 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
   }
 }
 
-// tile L of the grouped grid -> (segment e, n-tile nt, first row, valid rows)
+// tile L of the grouped grid -> (segment e, n-tile nt, first row, valid rows).
+// Within a group of gs n-tiles the order is segment, then n-tile, then the
+// segment's m-tiles, so the m-tiles that share a weight tile are neighbours
+// in L and run at the same time on one XCD whatever the segment lengths.
 struct TileCoord {
   int e, nt, row0, rows_valid, seg0;
 };
@@ -521,10 +526,12 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, int L, int 
   const int grp = L / (m_total * kNGroup);
   const int gs = min(kNGroup, n_tiles - grp * kNGroup);
   const int Lr = L - grp * m_total * kNGroup;
-  const int mt_g = Lr / gs;
   TileCoord t;
-  t.nt = grp * kNGroup + Lr % gs;
-  t.e = find_segment(p.ts, p.E, mt_g);
+  t.e = find_segment(p.ts, p.E, Lr / gs);
+  const int me = p.ts[t.e + 1] - p.ts[t.e];
+  const int r = Lr - p.ts[t.e] * gs;
+  const int mt_g = p.ts[t.e] + r % me;
+  t.nt = grp * kNGroup + r / me;
   t.seg0 = p.offsets[t.e];
   t.row0 = t.seg0 + (mt_g - p.ts[t.e]) * BM;
   t.rows_valid = min(BM, p.offsets[t.e + 1] - t.row0);
