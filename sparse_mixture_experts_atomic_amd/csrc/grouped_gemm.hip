@@ -388,6 +388,17 @@ __device__ __forceinline__ void template_for(F&& f) {
   template_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
+// n DMAs spread evenly over a window of w MFMA positions: DMA j goes after
+// position j * w / n; slot_at gives the DMA at a position (-1: none)
+template <int W, int N>
+constexpr int slot_pos(int j) { return j * W / N; }
+template <int W, int N>
+constexpr int slot_at(int i) {
+  for (int j = 0; j < N; ++j)
+    if (slot_pos<W, N>(j) == i) return j;
+  return -1;
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -881,45 +892,144 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     using F_ = std::false_type;
     using W0 = std::integral_constant<int, 0>;
     using WA = std::integral_constant<int, LDA>;
-    // prologue: A(0), B(0), A(1), B(1), A(2) into half-slots 0 .. 4; wait for stage 0
+    if constexpr (FM == 2 && !FP8) {
+      // 128-row tiles, bf16: the mirrored ring.  A stage moves 48 KB (A is
+      // half as tall) for half the MFMAs, so issued as above the B DMAs come
+      // at one per two MFMAs and stall them.  Here B takes the even half-slot
+      // of a stage and the long lead: stage s keeps B in (2 s) % 5 and A in
+      // (2 s + 1) % 5; the window from barrier s to barrier s + 1 spreads all
+      // twelve DMAs evenly, A(s + 2) first (into B(s)'s half-slot, landing by
+      // barrier s + 1), then B(s + 3) (into A(s)'s, landing by barrier s + 2).
+      // Window positions as in stage(); flags: POSTA = A(s + 2)'s first part
+      // after barrier s; PREA / PREB = this stage issues the rest of A(s + 1)
+      // / B(s + 2) (window s - 1); WAITN = DMAs allowed in flight at the
+      // wait (B(s + 2), issued last).
+      constexpr int NS = LDA + LDB;
+      static_assert(slot_pos<WIN, NS>(LDA) >= NM && slot_pos<WIN, NS>(LDA - 1) < WIN - kPre, "mirrored window layout");
+      auto stage2 = [&](auto next, auto posta, auto prea, auto preb, auto waitn, int s, int cB)
+          __attribute__((always_inline)) {
+        const uint4* Bc = ring + cB * HALF;
+        const uint4* Ac = ring + hs(cB + 1) * HALF;
+        const uint4* Bn = ring + hs(cB + 2) * HALF;
+        const uint4* An = ring + hs(cB + 3) * HALF;
+        const int h_prea = hs(cB + 3);       // A(s + 1) = (2 s + 3) % 5
+        const int h_preb = hs(cB + 4);       // B(s + 2) = (2 s + 4) % 5
+        auto pre_dma = [&](auto ic) __attribute__((always_inline)) {
+          constexpr int j = slot_at<WIN, NS>(decltype(ic)::value);
+          if constexpr (j >= 0 && j < LDA && decltype(prea)::value) issue_a(s + 1, h_prea, j);
+          if constexpr (j >= LDA && decltype(preb)::value) issue_b(s + 2, h_preb, j - LDA);
+        };
+        template_for<NKS - 1>([&](auto sc) __attribute__((always_inline)) {
+          constexpr int S = decltype(sc)::value;
+          auto& ca = (S & 1) ? fa1 : fa0;
+          auto& cb = (S & 1) ? fb1 : fb0;
+          auto& na = (S & 1) ? fa0 : fa1;
+          auto& nb = (S & 1) ? fb0 : fb1;
+          template_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            mma_one(q, ca, cb);
 #pragma unroll
-    for (int q = 0; q < LDA; ++q) issue_a(0, 0, q);
+            for (int c = q * NRD / NQ; c < (q + 1) * NRD / NQ; ++c) read_one(Ac, Bc, S + 1, c, na, nb);
+            pre_dma(std::integral_constant<int, NM + S * NQ + q>{});
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        });
+        template_for<kPre>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          mma_one(q, fa1, fb1);
+          pre_dma(std::integral_constant<int, WIN - kPre + q>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_vmcnt<decltype(waitn)::value>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        template_for<NM>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          mma_one(kPre + q, fa1, fb1);
+          if constexpr (decltype(next)::value) {
 #pragma unroll
-    for (int q = 0; q < LDB; ++q) issue_b(0, 1, q);
+            for (int c = q * NRD / NM; c < (q + 1) * NRD / NM; ++c) read_one(An, Bn, 0, c, fa0, fb0);
+          }
+          constexpr int j = slot_at<WIN, NS>(q);
+          if constexpr (j >= 0 && j < LDA && decltype(posta)::value) issue_a(s + 2, cB, j);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      using WB = std::integral_constant<int, LDB>;
+      // prologue: B(0), A(0), B(1), A(1), B(2) into half-slots 0 .. 4; wait for stage 0
 #pragma unroll
-    for (int q = 0; q < LDA; ++q) issue_a(1, 2, q);
+      for (int q = 0; q < LDB; ++q) issue_b(0, 0, q);
 #pragma unroll
-    for (int q = 0; q < LDB; ++q) issue_b(1, 3, q);
-    if (nks > 2) {
+      for (int q = 0; q < LDA; ++q) issue_a(0, 1, q);
 #pragma unroll
-      for (int q = 0; q < LDA; ++q) issue_a(2, 4, q);
-      wait_vmcnt<2 * LDA + LDB>();
-    } else {
-      wait_vmcnt<LDA + LDB>();
-    }
-    lds_barrier();
-    if constexpr (FP8) {
+      for (int q = 0; q < LDB; ++q) issue_b(1, 2, q);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) read_b8(ring + HALF, 0, j);
+      for (int q = 0; q < LDA; ++q) issue_a(1, 3, q);
+      if (nks > 2) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) read_a8(ring, 0, i, fa0);
-    } else {
-#pragma unroll
-      for (int r = 0; r < FM + FN; ++r) read_one(ring, ring + HALF, 0, r, fa0, fb0);
-    }
-    if (nks == 2) {
-      stage(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
-      stage(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
-    } else {
-      stage(T_{}, F_{}, F_{}, T_{}, WA{}, 0, 0);
-      int cA = 2;
-      for (int s = 1; s <= nks - 3; ++s) {
-        stage(T_{}, T_{}, T_{}, T_{}, WA{}, s, cA);
-        cA = hs(cA + 2);
+        for (int q = 0; q < LDB; ++q) issue_b(2, 4, q);
+        wait_vmcnt<LDA + 2 * LDB>();
+      } else {
+        wait_vmcnt<LDA + LDB>();
       }
-      // s = nks - 2: only the rest of B(nks - 1) left to issue
-      stage(T_{}, T_{}, F_{}, F_{}, W0{}, nks - 2, cA);
-      stage(F_{}, F_{}, F_{}, F_{}, W0{}, nks - 1, hs(cA + 2));
+      lds_barrier();
+#pragma unroll
+      for (int r = 0; r < FM + FN; ++r) read_one(ring + HALF, ring, 0, r, fa0, fb0);
+      if (nks == 2) {
+        stage2(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
+        stage2(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
+      } else {
+        stage2(T_{}, T_{}, F_{}, F_{}, WB{}, 0, 0);
+        int cB = 2;
+        for (int s = 1; s <= nks - 3; ++s) {
+          stage2(T_{}, T_{}, T_{}, T_{}, WB{}, s, cB);
+          cB = hs(cB + 2);
+        }
+        // s = nks - 2: only the rest of A(nks - 1) left to issue
+        stage2(T_{}, F_{}, T_{}, F_{}, W0{}, nks - 2, cB);
+        stage2(F_{}, F_{}, F_{}, F_{}, W0{}, nks - 1, hs(cB + 2));
+      }
+    } else {
+      // prologue: A(0), B(0), A(1), B(1), A(2) into half-slots 0 .. 4; wait for stage 0
+  #pragma unroll
+      for (int q = 0; q < LDA; ++q) issue_a(0, 0, q);
+  #pragma unroll
+      for (int q = 0; q < LDB; ++q) issue_b(0, 1, q);
+  #pragma unroll
+      for (int q = 0; q < LDA; ++q) issue_a(1, 2, q);
+  #pragma unroll
+      for (int q = 0; q < LDB; ++q) issue_b(1, 3, q);
+      if (nks > 2) {
+  #pragma unroll
+        for (int q = 0; q < LDA; ++q) issue_a(2, 4, q);
+        wait_vmcnt<2 * LDA + LDB>();
+      } else {
+        wait_vmcnt<LDA + LDB>();
+      }
+      lds_barrier();
+      if constexpr (FP8) {
+  #pragma unroll
+        for (int j = 0; j < FN; ++j) read_b8(ring + HALF, 0, j);
+  #pragma unroll
+        for (int i = 0; i < FM; ++i) read_a8(ring, 0, i, fa0);
+      } else {
+  #pragma unroll
+        for (int r = 0; r < FM + FN; ++r) read_one(ring, ring + HALF, 0, r, fa0, fb0);
+      }
+      if (nks == 2) {
+        stage(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
+        stage(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
+      } else {
+        stage(T_{}, F_{}, F_{}, T_{}, WA{}, 0, 0);
+        int cA = 2;
+        for (int s = 1; s <= nks - 3; ++s) {
+          stage(T_{}, T_{}, T_{}, T_{}, WA{}, s, cA);
+          cA = hs(cA + 2);
+        }
+        // s = nks - 2: only the rest of B(nks - 1) left to issue
+        stage(T_{}, T_{}, F_{}, F_{}, W0{}, nks - 2, cA);
+        stage(F_{}, F_{}, F_{}, F_{}, W0{}, nks - 1, hs(cA + 2));
+      }
     }
 
     if constexpr (FM == 4) {
