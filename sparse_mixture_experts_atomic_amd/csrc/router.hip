@@ -33,6 +33,55 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Wavefront reductions in DPP steps (gfx9): butterflies inside quads, row
+// shifts by 4 and 8, then the row-15 and row-31 broadcasts; the result is in
+// lane 63 and is read back as a uniform value.  Lanes whose source lies
+// outside the row keep the identity passed as the old value.  Six ALU steps
+// instead of six dependent cross-lane LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int identity, int v) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(-INFINITY, v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4e>(-INFINITY, v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x114>(-INFINITY, v));   // row_shr:4
+  v = fmaxf(v, dpp_f<0x118>(-INFINITY, v));   // row_shr:8
+  v = fmaxf(v, dpp_f<0x142>(-INFINITY, v));   // row_bcast:15
+  v = fmaxf(v, dpp_f<0x143>(-INFINITY, v));   // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xb1>(0.f, v);
+  v += dpp_f<0x4e>(0.f, v);
+  v += dpp_f<0x114>(0.f, v);
+  v += dpp_f<0x118>(0.f, v);
+  v += dpp_f<0x142>(0.f, v);
+  v += dpp_f<0x143>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(-INFINITY, bv);
+  const int oi = dpp_i<CTRL>(0x7fffffff, bi);
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+// largest value over the wavefront, lower index on ties; uniform result
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_step<0xb1>(bv, bi);
+  argmax_step<0x4e>(bv, bi);
+  argmax_step<0x114>(bv, bi);
+  argmax_step<0x118>(bv, bi);
+  argmax_step<0x142>(bv, bi);
+  argmax_step<0x143>(bv, bi);
+  bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 63));
+  bi = __builtin_amdgcn_readlane(bi, 63);
+}
+
 // fp32 softmax and top-k of one token's logits z[0..E) by one wavefront:
 // expert e lives on lane e % 64, slot e / 64; k rounds of a wavefront arg-max
 // (largest logit, lower id on ties), the winning lane marks its slot taken.
@@ -41,12 +90,10 @@ __device__ __forceinline__ void token_softmax_topk(const float* z, int t, const 
                                                    int lane) {
   float m = -INFINITY;
   for (int e = lane; e < a.E; e += 64) m = fmaxf(m, z[e]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  m = wave_max(m);
   float s = 0.f;
   for (int e = lane; e < a.E; e += 64) s += expf(z[e] - m);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  s = wave_sum(s);
   const float inv = 1.0f / s;
   for (int e = lane; e < a.E; e += 64) {
     if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z[e];
@@ -62,12 +109,7 @@ __device__ __forceinline__ void token_softmax_topk(const float* z, int t, const 
     for (int e = lane, i = 0; e < a.E; e += 64, ++i) {
       if (!((taken >> i) & 1u) && better(z[e], e, bv, bi)) { bv = z[e]; bi = e; }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    wave_argmax(bv, bi);
     const float p = expf(bv - m) * inv;
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == j) { myp = p; myi = bi; }
