@@ -348,6 +348,7 @@ constexpr int kDmaBK = 64;         // K columns per stage
 // the Mixtral-shaped layer reads 3.8 GB instead of 6.7 GB and the FFN is 2%
 // faster; 12-16 measured alike, 20 makes the tails the slowest tiles.
 constexpr int kTailPace = 14;
+constexpr int kTailPace64 = 18;    // the same for a 64-row tile (~1100 cycles a stage unpaced)
 
 // a pointer that is the same in every lane, moved to scalar registers
 template <typename T>
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     constexpr int RPI = kThreads / CH;        // rows covered by one DMA instruction: A
     constexpr int RPIB = kThreads / CHB;      //   and B
     constexpr int HALF = BN * CH;             // uint4 per half-slot (one operand of one stage)
-    static_assert(BK == 64 && (FM == 4 || FM == 2), "tile shapes");
+    static_assert(BK == 64 && (FM == 4 || FM == 2 || (FM == 1 && !FP8)), "tile shapes");
     const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
     const int K = p.K;
     const int N = p.N;
@@ -901,8 +902,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     using F_ = std::false_type;
     using W0 = std::integral_constant<int, 0>;
     using WA = std::integral_constant<int, LDA>;
-    if constexpr (FM == 2 && !FP8) {
-      // 128-row tiles, bf16: the mirrored ring.  A stage moves 48 KB (A is
+    if constexpr (FM <= 2 && !FP8) {
+      // 128- and 64-row tiles, bf16: the mirrored ring.  A stage moves 48 KB (A is
       // half as tall) for half the MFMAs, so issued as above the B DMAs come
       // at one per two MFMAs and stall them.  Here B takes the even half-slot
       // of a stage and the long lead: stage s keeps B in (2 s) % 5 and A in
@@ -952,7 +953,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
         });
         wait_vmcnt<decltype(waitn)::value>();
         lds_barrier();
-        __builtin_amdgcn_s_sleep(kTailPace);
+        __builtin_amdgcn_s_sleep(FM == 2 ? kTailPace : kTailPace64);
         __builtin_amdgcn_sched_barrier(0);
         template_for<NM>([&](auto qc) __attribute__((always_inline)) {
           constexpr int q = decltype(qc)::value;
@@ -1066,6 +1067,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     wave_epilogue<EPI, FM>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * (OC + 8), p, e, row0 + wm * WM,
                            rows_valid - wm * WM, col0);
   };
+  if constexpr (!FP8) {
+    if (unit < 0 && tc.rows_valid <= 64) {
+      tile(std::integral_constant<int, 1>{});
+      return;
+    }
+  }
   if (unit < 0 && tc.rows_valid <= 128)
     tile(std::integral_constant<int, 2>{});
   else
