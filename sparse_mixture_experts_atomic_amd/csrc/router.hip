@@ -88,16 +88,29 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
 // Adds the probabilities to wcol[0..E) and writes the outputs of token t.
 __device__ __forceinline__ void token_softmax_topk(const float* z, int t, const RouterArgs& a, float* wcol,
                                                    int lane) {
-  float m = -INFINITY;
-  for (int e = lane; e < a.E; e += 64) m = fmaxf(m, z[e]);
+  constexpr int S = kRtMaxE / 64;             // slots per lane
+  float zr[S], ex[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) zr[i] = lane + 64 * i < a.E ? z[lane + 64 * i] : -INFINITY;
+  float m = zr[0];
+#pragma unroll
+  for (int i = 1; i < S; ++i) m = fmaxf(m, zr[i]);
   m = wave_max(m);
   float s = 0.f;
-  for (int e = lane; e < a.E; e += 64) s += expf(z[e] - m);
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    ex[i] = lane + 64 * i < a.E ? expf(zr[i] - m) : 0.f;
+    s += ex[i];
+  }
   s = wave_sum(s);
   const float inv = 1.0f / s;
-  for (int e = lane; e < a.E; e += 64) {
-    if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = z[e];
-    wcol[e] += expf(z[e] - m) * inv;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int e = lane + 64 * i;
+    if (e < a.E) {
+      if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = zr[i];
+      wcol[e] += ex[i] * inv;
+    }
   }
   uint32_t taken = 0;
   float myp = 0.f;
@@ -106,8 +119,10 @@ __device__ __forceinline__ void token_softmax_topk(const float* z, int t, const 
   for (int j = 0; j < a.k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int e = lane, i = 0; e < a.E; e += 64, ++i) {
-      if (!((taken >> i) & 1u) && better(z[e], e, bv, bi)) { bv = z[e]; bi = e; }
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int e = lane + 64 * i;
+      if (e < a.E && !((taken >> i) & 1u) && better(zr[i], e, bv, bi)) { bv = zr[i]; bi = e; }
     }
     wave_argmax(bv, bi);
     const float p = expf(bv - m) * inv;
@@ -263,23 +278,10 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
   }
 }
 
-// MFMA router for bf16 activations.  W_g is split exactly into three bf16
-// planes, w = hi + mid + lo, each the truncation of what the previous ones
-// leave (a float's 24-bit significand in three 8-bit pieces), so every
-// product with a bf16 x is exact and the logits are fp32 sums as in the VALU
-// kernels.  A block takes 16 TG tokens and NE groups of 16 experts per pass;
-// its 8 wavefronts split K by 32-column steps (wavefront w takes steps w,
-// w + 8, ...) and keep kMfPd steps of loads in flight: per step a 16-byte x
-// fragment per token group (v_mfma_f32_16x16x32_bf16 A operand: token lane %
-// 16, columns 8 (lane / 16) ..) and 32 bytes of fp32 W_g per expert group (B
-// operand: expert lane % 16, same columns), split in registers.  The
-// wavefronts' partial logits are added in LDS in wavefront order, then one
-// wavefront per token does the fp32 softmax and top-k, and per-block
-// probability column sums go to the workspace.
-constexpr int kMfWaves = 8;
-constexpr int kMfThreads = 64 * kMfWaves;
-constexpr int kMfPd = 4;                      // k-steps of loads in flight
-
+// The MFMA routers split W_g exactly into three bf16 planes, w = hi + mid +
+// lo, each the truncation of what the previous ones leave (a float's 24-bit
+// significand in three 8-bit pieces), so every product with a bf16 x is
+// exact and the logits are fp32 sums of exact products.
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_mf;
 
 // bf16 pair (lo in bits 0-15) from the high halves of two words
@@ -313,120 +315,13 @@ __device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x
   lo = __builtin_bit_cast(bf16x8_t, pl);
 }
 
-template <int TG, int NE>
-__global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(RouterArgs a) {
-  constexpr int TPB = 16 * TG;                // tokens per block
-  constexpr int EC = 16 * NE;                 // experts per pass
-  extern __shared__ float smem[];
-  float* part = smem;                         // [kMfWaves][TPB][EC]
-  float* lg = part + kMfWaves * TPB * EC;     // [TPB][E]
-  float* wcol = lg + TPB * a.E;               // [kMfWaves][E]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int r16 = lane & 15;
-  const int kq = (lane >> 4) * 8;             // first column of the lane within a step
-  const int t0 = blockIdx.x * TPB;
-  const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  const int nks = (a.d + 31) / 32;
-  const int my = nks > wave ? (nks - wave + kMfWaves - 1) / kMfWaves : 0;   // k-steps of this wavefront
-
-  for (int e0 = 0; e0 < a.E; e0 += EC) {
-    uint4 xb[kMfPd][TG];
-    float4 wb[kMfPd][NE][2];
-    auto load = [&](int i, uint4 (&xs)[TG], float4 (&ws)[NE][2]) __attribute__((always_inline)) {
-      const int col = (wave + i * kMfWaves) * 32 + kq;
-      const bool kv = i < my && col < a.d;    // d % 8 == 0: a lane's 8 columns are all in or all out
-#pragma unroll
-      for (int g = 0; g < TG; ++g) {
-        const int t = t0 + g * 16 + r16;
-        xs[g] = (kv && t < a.T) ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * a.d + col)
-                                : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int n = 0; n < NE; ++n) {
-        const int e = e0 + n * 16 + r16;
-        if (kv && e < a.E) {
-          const float4* src = reinterpret_cast<const float4*>(a.w_g + static_cast<size_t>(e) * a.d + col);
-          ws[n][0] = src[0];
-          ws[n][1] = src[1];
-        } else {
-          ws[n][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-          ws[n][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-    };
-    f32x4_mf acc[TG][NE];
-#pragma unroll
-    for (int g = 0; g < TG; ++g)
-#pragma unroll
-      for (int n = 0; n < NE; ++n) acc[g][n] = f32x4_mf{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < kMfPd; ++j) load(j, xb[j], wb[j]);
-    for (int i0 = 0; i0 < my; i0 += kMfPd) {
-#pragma unroll
-      for (int j = 0; j < kMfPd; ++j) {
-        if (i0 + j < my) {
-#pragma unroll
-          for (int n = 0; n < NE; ++n) {
-            bf16x8_t hi, mid, lo;
-            split3(wb[j][n][0], wb[j][n][1], hi, mid, lo);
-#pragma unroll
-            for (int g = 0; g < TG; ++g) {
-              const bf16x8_t xv = __builtin_bit_cast(bf16x8_t, xb[j][g]);
-              acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, hi, acc[g][n], 0, 0, 0);
-              acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, mid, acc[g][n], 0, 0, 0);
-              acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, lo, acc[g][n], 0, 0, 0);
-            }
-          }
-          load(i0 + j + kMfPd, xb[j], wb[j]);
-        }
-      }
-    }
-    // partial logits: lane holds expert n*16 + lane % 16 of tokens g*16 + 4 (lane / 16) + q
-#pragma unroll
-    for (int g = 0; g < TG; ++g)
-#pragma unroll
-      for (int n = 0; n < NE; ++n)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          part[(wave * TPB + g * 16 + (lane >> 4) * 4 + q) * EC + n * 16 + r16] = acc[g][n][q];
-    __syncthreads();
-    for (int j = tid; j < TPB * EC; j += kMfThreads) {
-      const int tl = j / EC, ec = j % EC, e = e0 + ec;
-      if (e < a.E) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kMfWaves; ++w) s += part[(w * TPB + tl) * EC + ec];
-        lg[tl * a.E + e] = s + (a.b_g ? a.b_g[e] : 0.f);
-      }
-    }
-    __syncthreads();
-  }
-
-  // softmax + top-k: one wavefront per token
-  for (int e = lane; e < a.E; e += 64) wcol[wave * a.E + e] = 0.f;
-  for (int tl = wave; tl < TPB; tl += kMfWaves) {
-    const int t = t0 + tl;
-    if (t >= a.T) break;
-    token_softmax_topk(lg + tl * a.E, t, a, wcol + wave * a.E, lane);
-  }
-  __syncthreads();
-  for (int e = tid; e < a.E; e += kMfThreads) {
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMfWaves; ++w) v += wcol[w * a.E + e];
-    a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + e] = v;
-  }
-}
-
 // MFMA router for bf16 activations and at most 8 experts.  A block takes tg
 // groups of 16 tokens; the kw wavefronts of a group split the columns into
 // 128-column chunks, two per wavefront and round (wavefront j takes chunks j
 // and j + kw of each run of 2 kw).  A chunk is four 32-column k-steps of
 // v_mfma_f32_16x16x32_bf16 with the tokens as rows: a lane loads 16 bytes of
 // x per k-step (token lane % 16, columns 8 (lane / 16) ..).  W_g is split
-// exactly into bf16 planes as in router_mfma_kernel; the first MFMA's B
+// exactly into bf16 planes (see split3); the first MFMA's B
 // operand holds hi of expert n in column n < 8 and mid of expert n - 8 in
 // column n >= 8, the second adds lo in columns < 8, so logit e is column e
 // plus column e + 8.  Lanes n and n + 8 need the same eight fp32 values of
@@ -551,6 +446,185 @@ __global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a,
   }
 }
 
+// Router logits for bf16 activations and more than 8 experts as a tiled
+// GEMM.  A block takes BM tokens x 64 experts x one slice of K; W_g is split
+// exactly into its three bf16 planes (see split3) once per
+// block and 64-column chunk, into LDS, where every token of the block uses
+// it, and x is staged beside it.  Four wavefronts of (BM / 2) tokens x 32
+// experts run v_mfma_f32_16x16x32_bf16 (one per plane).  The slice's partial
+// logits go to part[slice][t][e]; router_finish_kernel adds the slices.
+constexpr int kLgBN = 64;                     // experts per block
+constexpr int kLgBK = 64;                     // columns per LDS chunk
+constexpr int kLgPad = kLgBK + 8;             // LDS row pitch (bf16): 16 rows of a read hit distinct banks
+constexpr int kLgThreads = 256;
+
+template <int BM>
+__global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ w_g, int T, int d, int E,
+                                                                  int kslice, float* __restrict__ part) {
+  constexpr int WT = BM / 2;                  // tokens per wavefront
+  constexpr int FT = WT / 16;                 // 16-token fragments per wavefront
+  constexpr int XL = BM * kLgBK / 8 / kLgThreads;     // 16-byte x loads per thread and chunk
+  constexpr int WL = kLgBN * kLgBK / 4 / kLgThreads;  // 16-byte W_g loads per thread and chunk
+  __shared__ uint16_t xs[BM * kLgPad];
+  __shared__ uint16_t wp[3 * kLgBN * kLgPad]; // planes hi, mid, lo
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const int t0 = blockIdx.x * BM;
+  const int e0 = blockIdx.y * kLgBN;
+  const int k0 = blockIdx.z * kslice;
+  const int k1 = min(d, k0 + kslice);
+  f32x4_mf acc[FT][2];
+#pragma unroll
+  for (int i = 0; i < FT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_mf{0.f, 0.f, 0.f, 0.f};
+  // the next chunk's global loads are in flight while the current one is
+  // multiplied out of LDS; d % 8 == 0 and slices are whole chunks, so a
+  // piece is all in or all out
+  uint4 xr[XL];
+  float4 wr[WL];
+  auto load = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int q = tid + kLgThreads * i;
+      const int r = q / (kLgBK / 8), c = (q % (kLgBK / 8)) * 8;
+      const int t = t0 + r, col = kc + c;
+      xr[i] = (t < T && col < k1) ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * d + col)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int q = tid + kLgThreads * i;
+      const int r = q / (kLgBK / 4), c = (q % (kLgBK / 4)) * 4;
+      const int e = e0 + r, col = kc + c;
+      wr[i] = (e < E && col < k1) ? *reinterpret_cast<const float4*>(w_g + static_cast<size_t>(e) * d + col)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (k0 < k1) load(k0);
+  for (int kc = k0; kc < k1; kc += kLgBK) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int q = tid + kLgThreads * i;
+      const int r = q / (kLgBK / 8), c = (q % (kLgBK / 8)) * 8;
+      *reinterpret_cast<uint4*>(xs + r * kLgPad + c) = xr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int q = tid + kLgThreads * i;
+      const int r = q / (kLgBK / 4), c = (q % (kLgBK / 4)) * 4;
+      const float wv[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
+      uint32_t h[4], m[4], l[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        h[u] = __float_as_uint(wv[u]) & 0xffff0000u;
+        const float rr = wv[u] - __uint_as_float(h[u]);           // exact
+        m[u] = __float_as_uint(rr) & 0xffff0000u;
+        l[u] = __float_as_uint(rr - __uint_as_float(m[u]));        // exact; fits in bf16
+      }
+      *reinterpret_cast<uint2*>(wp + (0 * kLgBN + r) * kLgPad + c) = make_uint2(hi16_pair(h[0], h[1]), hi16_pair(h[2], h[3]));
+      *reinterpret_cast<uint2*>(wp + (1 * kLgBN + r) * kLgPad + c) = make_uint2(hi16_pair(m[0], m[1]), hi16_pair(m[2], m[3]));
+      *reinterpret_cast<uint2*>(wp + (2 * kLgBN + r) * kLgPad + c) = make_uint2(hi16_pair(l[0], l[1]), hi16_pair(l[2], l[3]));
+    }
+    __syncthreads();
+    if (kc + kLgBK < k1) load(kc + kLgBK);
+#pragma unroll
+    for (int ks = 0; ks < kLgBK / 32; ++ks) {
+      bf16x8_t fa[FT], fb[2][3];
+#pragma unroll
+      for (int i = 0; i < FT; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(xs + (wm * WT + i * 16 + r16) * kLgPad + ks * 32 + kq);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+          fb[j][pl] = *reinterpret_cast<const bf16x8_t*>(wp + (pl * kLgBN + wn * 32 + j * 16 + r16) * kLgPad + ks * 32 + kq);
+#pragma unroll
+      for (int i = 0; i < FT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int pl = 0; pl < 3; ++pl)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j][pl], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // lane holds expert column r16 of tokens 4 (lane / 16) + q of each fragment
+  float* out = part + static_cast<size_t>(blockIdx.z) * T * E;
+#pragma unroll
+  for (int i = 0; i < FT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + wn * 32 + j * 16 + r16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + wm * WT + i * 16 + (lane >> 4) * 4 + q;
+        if (t < T && e < E) out[static_cast<size_t>(t) * E + e] = acc[i][j][q];
+      }
+    }
+}
+
+// Sum of the logit slices (in slice order) plus the router bias, then the
+// fp32 softmax and top-k of each token by one wavefront, and per-block
+// probability column sums (wavefronts added in order) to the workspace.
+constexpr int kFnTok = 16;                    // tokens per block
+constexpr int kFnWaves = 8;
+
+__global__ __launch_bounds__(64 * kFnWaves) void router_finish_kernel(RouterArgs a, const float* __restrict__ part,
+                                                                       int nslice) {
+  __shared__ float lg[kFnTok * kRtMaxE];
+  __shared__ float wcol[kFnWaves * kRtMaxE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t0 = blockIdx.x * kFnTok;
+  for (int e = lane; e < a.E; e += 64) wcol[wave * a.E + e] = 0.f;
+  // the block's logits first (all loads in flight together), then one
+  // wavefront per token
+  constexpr int kPer = kFnTok * kRtMaxE / (64 * kFnWaves);   // entries per thread at most
+  const int n_ent = min(kFnTok, a.T - t0) * a.E;             // the block's tokens are contiguous
+  const float* src = part + static_cast<size_t>(t0) * a.E;
+  float z[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) z[u] = 0.f;
+  // unconditional loads (clamped index) so that they are all in flight at
+  // once; entries past the block's tokens are not stored
+  for (int sl = 0; sl < nslice; ++sl) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = min(tid + 64 * kFnWaves * u, n_ent - 1);
+      z[u] += src[static_cast<size_t>(sl) * a.T * a.E + j];
+    }
+  }
+  if (a.b_g) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) z[u] += a.b_g[min(tid + 64 * kFnWaves * u, n_ent - 1) % a.E];
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = tid + 64 * kFnWaves * u;
+    if (j < n_ent) lg[j] = z[u];
+  }
+  __syncthreads();
+  for (int tl = wave; tl < kFnTok; tl += kFnWaves) {
+    const int t = t0 + tl;
+    if (t >= a.T) break;
+    token_softmax_topk(lg + tl * a.E, t, a, wcol + wave * a.E, lane);
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += 64 * kFnWaves) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFnWaves; ++w) v += wcol[w * a.E + e];
+    a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + e] = v;
+  }
+}
+
 // prob_colsum[e] = sum over blocks of the partial sums.  One block per
 // expert: strided partial sums in double, then a fixed-order tree, so the
 // result is deterministic and does not drift with the block count.
@@ -591,32 +665,20 @@ inline void mf8_shape(int T, int d, int& kw, int& tg) {
   if (tg > kM8Waves / kw) tg = kM8Waves / kw;
   if (tg < 1) tg = 1;
 }
-// token groups of 16 per block of the MFMA router: enough blocks for the
-// CUs, more tokens per block (fewer W_g reads) for long batches
-inline int mfma_tg(int T) { return T >= 16384 ? 4 : (T >= 8192 ? 2 : 1); }
-// expert groups of 16 per pass (TG * NE <= 8 keeps the partial sums in LDS)
-inline int mfma_ne(int E, int tg) {
-  int ne = (E + 15) / 16;
-  ne = ne >= 4 ? 4 : (ne >= 2 ? 2 : 1);
-  while (tg * ne > 8) ne /= 2;
-  return ne;
+// tiled logits GEMM (more than 8 experts, bf16 x): token rows per block;
+// K slices so that the grid has about one block per CU, each slice at least
+// 256 columns; the slice width in whole 64-column chunks
+inline int logit_bm(int T) { return T >= 8192 ? 128 : 64; }
+inline int logit_slices(int T, int d, int E) {
+  const long mn = static_cast<long>((T + logit_bm(T) - 1) / logit_bm(T)) * ((E + kLgBN - 1) / kLgBN);
+  int ks = 1;
+  while (mn * ks < kCUs && d / (2 * ks) >= 256) ks *= 2;
+  return ks;
 }
-inline size_t mfma_lds_bytes(int tg, int ne, int E) {
-  return (static_cast<size_t>(kMfWaves) * 16 * tg * 16 * ne + static_cast<size_t>(16) * tg * E +
-          static_cast<size_t>(kMfWaves) * E) * sizeof(float);
-}
-template <int TG, int NE>
-int launch_mfma(const RouterArgs& a, int nb, size_t lds, hipStream_t stream) {
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_mfma_kernel<TG, NE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) {
-      record_hip_error(e);
-      return MOE_ERR_HIP;
-    }
-  }
-  hipLaunchKernelGGL((router_mfma_kernel<TG, NE>), dim3(nb), dim3(kMfThreads), lds, stream, a);
-  return check_launch();
+inline int logit_kslice(int d, int ks) { return ((d + ks - 1) / ks + kLgBK - 1) / kLgBK * kLgBK; }
+// byte offset of the partial logits in the workspace (after the column sums)
+inline size_t logit_ws_offset(int T, int E) {
+  return align_up(static_cast<size_t>(router_max_blocks(T)) * E * sizeof(float), kWsAlign);
 }
 
 }  // namespace
@@ -627,10 +689,12 @@ using namespace moe;
 extern "C" {
 
 size_t moe_router_workspace_size(int T, int d, int E, int x_dt) {
-  (void)d;
-  (void)x_dt;
   if (T < 0 || E < 1) return 0;
-  return align_up(static_cast<size_t>(router_max_blocks(T)) * E * sizeof(float), kWsAlign);
+  size_t s = logit_ws_offset(T, E);
+  // partial logits of the tiled router GEMM
+  if (x_dt == MOE_BF16 && E > kM8MaxE && d > 0)
+    s += align_up(static_cast<size_t>(logit_slices(T, d, E)) * T * E * sizeof(float), kWsAlign);
+  return s;
 }
 
 int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g, int T, int d, int E,
@@ -650,17 +714,15 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
   if (prob_colsum && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
 
-  // bf16: the MFMA kernels (the one for up to 8 experts takes whole rows per
-  // block); fp32 activations: the generic kernel
+  // bf16: MFMA kernels (up to 8 experts: whole rows per block, one launch;
+  // beyond: the tiled logits GEMM, then the finishing kernel); fp32
+  // activations: the generic kernel
   const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE;
   const bool mf = x_dt == MOE_BF16 && !m8;
   float* part = static_cast<float*>(workspace);
-  const int tg = mfma_tg(T);
-  const int ne = mfma_ne(E, tg);
   int kw8 = 1, tg8 = 1;
   mf8_shape(T, d, kw8, tg8);
-  const int nb = m8 ? (T + 16 * tg8 - 1) / (16 * tg8)
-                    : (mf ? (T + 16 * tg - 1) / (16 * tg) : router_blocks(T));
+  const int nb = m8 ? (T + 16 * tg8 - 1) / (16 * tg8) : (mf ? (T + kFnTok - 1) / kFnTok : router_blocks(T));
   if (T > 0 && m8) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
     hipLaunchKernelGGL(router_mf8_kernel, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
@@ -669,13 +731,19 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
   }
   if (T > 0 && mf) {
     RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
-    const size_t lds = mfma_lds_bytes(tg, ne, E);
-    int st = MOE_OK;
-#define MOE_RT_MF(TG_, NE_) \
-  if (tg == TG_ && ne == NE_) st = launch_mfma<TG_, NE_>(a, nb, lds, stream);
-    MOE_RT_MF(1, 1) MOE_RT_MF(1, 2) MOE_RT_MF(1, 4) MOE_RT_MF(2, 1) MOE_RT_MF(2, 2) MOE_RT_MF(2, 4)
-    MOE_RT_MF(4, 1) MOE_RT_MF(4, 2)
-#undef MOE_RT_MF
+    float* lgp = reinterpret_cast<float*>(static_cast<char*>(workspace) + logit_ws_offset(T, E));
+    const int bm = logit_bm(T), ks = logit_slices(T, d, E), kslice = logit_kslice(d, ks);
+    const dim3 grid((T + bm - 1) / bm, (E + kLgBN - 1) / kLgBN, ks);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    if (bm == 128)
+      hipLaunchKernelGGL(router_logits_kernel<128>, grid, dim3(kLgThreads), 0, stream, xb, w_g, T, d, E, kslice, lgp);
+    else
+      hipLaunchKernelGGL(router_logits_kernel<64>, grid, dim3(kLgThreads), 0, stream, xb, w_g, T, d, E, kslice, lgp);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+    hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(64 * kFnWaves), 0, stream, a,
+                       static_cast<const float*>(lgp), ks);
+    st = check_launch();
     if (st != MOE_OK) return st;
   }
   if (T > 0 && !mf && !m8) {
