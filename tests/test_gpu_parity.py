@@ -71,12 +71,16 @@ EDGE = {
     "f32_swiglu_shared": _cfg("f32_swiglu_shared", T=90, d=24, E=6, k=2, ffn="swiglu", d_ff=40, gate="renorm",
                               n_shared=1, act_dtype="f32", w_dtype="f32", wg_dist=("normal", 1 / 24),
                               w1_var=1 / 24, w3_var=1 / 24, w2_var=1 / 40, seed=28),
-    # MFMA router: expert count off the 16-expert groups, a partial last
-    # 32-column step, a token count off the 16-token groups, router bias
+    # tiled router GEMM: expert count off the 64-expert blocks, a partial
+    # last 64-column chunk, a token count off the 64-token blocks, router bias
     "router_mfma_tails": _cfg("router_mfma_tails", T=77, d=72, E=20, k=3, ffn="swiglu", d_ff=64, gate="prob",
                               wg_dist=("normal", 1 / 72), bg_var=0.5, w1_var=1 / 72, w3_var=1 / 72,
                               w2_var=1 / 64, seed=33),
-    # MFMA router at the largest expert count (four experts per lane slot)
+    # tiled router GEMM split over four K slices (the last one ends in a
+    # partial chunk), two expert blocks (the second of 6 experts), bias
+    "router_kslices": _cfg("router_kslices", T=300, d=1544, d_out=16, E=70, k=5, ffn="linear", d_ff=0,
+                           gate="prob", wg_dist=("normal", 1 / 1544), bg_var=0.5, w1_var=1 / 1544, seed=39),
+    # router at the largest expert count (four experts per lane slot)
     "router_e256": _cfg("router_e256", T=1100, d=256, E=256, k=8, ffn="linear", d_ff=0, gate="renorm",
                         wg_dist=("normal", 1 / 256), w1_var=1 / 256, seed=34),
     # e4m3 weights on the LDS-DMA GEMM (K % 128 == 0): ReLU with biases, and a
