@@ -339,16 +339,18 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
 // in its slot.
 constexpr int kDmaKMult = 128;     // K granularity of the DMA kernel
 constexpr int kDmaBK = 64;         // K columns per stage
-// s_sleep per stage of a 128-row bf16 tile (about 64 cycles a unit).  Such a
-// tile shares its weight tile with the 256-row tiles of the same n-tile,
-// which start with it, but does half their MFMAs: unpaced (~1400 cycles a
-// stage against ~2400) it runs ahead, reads every weight stage from HBM
-// before the others, and they miss in L2 too.  The workgroups of an XCD run
-// in rounds, so finishing early gains nothing.  Paced, the gate/up GEMM of
-// the Mixtral-shaped layer reads 3.8 GB instead of 6.7 GB and the FFN is 2%
-// faster; 12-16 measured alike, 20 makes the tails the slowest tiles.
-constexpr int kTailPace = 14;
-constexpr int kTailPace64 = 18;    // the same for a 64-row tile (~1100 cycles a stage unpaced)
+// Pace of a 128- or 64-row bf16 tail tile: stage s + 1 may start no earlier
+// than kTailStage shader cycles (s_memtime) per stage after the prologue.  A
+// tail tile shares its weight tile with the 256-row tiles of the same n-tile,
+// which start with it, but does a half or a quarter of their MFMAs: unpaced
+// (~1400 or ~1100 cycles a stage against ~2400) it runs ahead, reads every
+// weight stage from HBM before the others, and they miss in L2 too.  The
+// workgroups of an XCD run in rounds, so finishing early gains nothing.  A
+// target on the clock (not a fixed sleep) holds both tail sizes to the pace
+// of the full tiles whatever the clock does.  Paced, the gate/up GEMM of the
+// Mixtral-shaped layer reads 3.8 GB instead of 6.7 GB and the down GEMM
+// 2.1 GB instead of 2.4 GB; 2200-2400 measured alike in time.
+constexpr unsigned long long kTailStage = 2280;
 
 // a pointer that is the same in every lane, moved to scalar registers
 template <typename T>
@@ -910,13 +912,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       // (2 s + 1) % 5; the window from barrier s to barrier s + 1 spreads all
       // twelve DMAs evenly, A(s + 2) first (into B(s)'s half-slot, landing by
       // barrier s + 1), then B(s + 3) (into A(s)'s, landing by barrier s + 2).
-      // Each stage sleeps kTailPace after its barrier (see there).
+      // Each stage waits for its kTailStage target after its barrier (see there).
       // Window positions as in stage(); flags: POSTA = A(s + 2)'s first part
       // after barrier s; PREA / PREB = this stage issues the rest of A(s + 1)
       // / B(s + 2) (window s - 1); WAITN = DMAs allowed in flight at the
       // wait (B(s + 2), issued last).
       constexpr int NS = LDA + LDB;
       static_assert(slot_pos<WIN, NS>(LDA) >= NM && slot_pos<WIN, NS>(LDA - 1) < WIN - kPre, "mirrored window layout");
+      unsigned long long t_pace = 0;   // shader clock when stage 0's MFMAs may start
       auto stage2 = [&](auto next, auto posta, auto prea, auto preb, auto waitn, int s, int cB)
           __attribute__((always_inline)) {
         const uint4* Bc = ring + cB * HALF;
@@ -953,7 +956,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
         });
         wait_vmcnt<decltype(waitn)::value>();
         lds_barrier();
-        __builtin_amdgcn_s_sleep(FM == 2 ? kTailPace : kTailPace64);
+        {
+          const unsigned long long tgt = t_pace + static_cast<unsigned long long>(s + 1) * kTailStage;
+          while (__builtin_amdgcn_s_memtime() < tgt) __builtin_amdgcn_s_sleep(1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         template_for<NM>([&](auto qc) __attribute__((always_inline)) {
           constexpr int q = decltype(qc)::value;
@@ -987,6 +993,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       lds_barrier();
 #pragma unroll
       for (int r = 0; r < FM + FN; ++r) read_one(ring + HALF, ring, 0, r, fa0, fb0);
+      t_pace = __builtin_amdgcn_s_memtime();
       if (nks == 2) {
         stage2(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
         stage2(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
