@@ -6,13 +6,14 @@ CPU-baseline leg of the benchmark, never by the product library.
 from .moe_oracle import (E4M3_TABLE, aux_loss, bf16_to_f64, capacity, combine,
                          decode_weights, dense_moe, dispatch, e4m3_to_f64,
                          expert_ffn, experts_packed, forward, gates,
-                         near_tie_mask, permute, router_logits, shared_experts,
-                         silu, softmax, to_f64, topk_select)
+                         near_tie_mask, noisy_router, noisy_router_logits,
+                         permute, router_logits, shared_experts, silu,
+                         softmax, softplus, to_f64, topk_select)
 
 __all__ = [
     "E4M3_TABLE", "aux_loss", "bf16_to_f64", "capacity", "combine",
     "decode_weights", "dense_moe", "dispatch", "e4m3_to_f64", "expert_ffn",
-    "experts_packed", "forward", "gates", "near_tie_mask", "permute",
-    "router_logits", "shared_experts", "silu", "softmax", "to_f64",
-    "topk_select",
+    "experts_packed", "forward", "gates", "near_tie_mask", "noisy_router",
+    "noisy_router_logits", "permute", "router_logits", "shared_experts",
+    "silu", "softmax", "softplus", "to_f64", "topk_select",
 ]

@@ -156,6 +156,53 @@ def gates(p: np.ndarray, idx: np.ndarray, mode: str) -> np.ndarray:
     raise ValueError(mode)
 
 
+def softplus(u: np.ndarray) -> np.ndarray:
+    """softplus(u) = ln(1 + e^u), written as max(u, 0) + ln(1 + e^-|u|) so
+    that large |u| neither overflows nor loses the small term."""
+    u = np.asarray(u, np.float64)
+    return np.maximum(u, 0.0) + np.log1p(np.exp(-np.abs(u)))
+
+
+def noisy_router_logits(x: np.ndarray, w_g: np.ndarray, b_g: Optional[np.ndarray],
+                        w_n: np.ndarray, b_n: Optional[np.ndarray], noise: np.ndarray,
+                        eps: float = 0.0) -> np.ndarray:
+    """Noisy router logits: clean logits plus a standard normal draw times a
+    learned, input-dependent noise scale.
+
+    P2 §2.1 (Noisy Top-k 门控): the noise scale is softplus of a second
+    projection x W_noise of the input, multiplied by a standard normal
+    sample and added to the clean logits x W_gate; the top-k gating then
+    runs on these noisy logits.  P5 代码实战 (NoisyTop1Gate, training mode):
+    the second projection is a Linear layer with a bias, and the scale gets a
+    floor of 1e-2 added after the softplus.  Both are this function, with
+    eps = 0 (P2) or 1e-2 (P5).  The normal samples are an input
+    (noise[t, e], one per token and expert), so the GPU and this function see
+    the same draws.
+    """
+    z = router_logits(x, w_g, b_g)
+    zn = router_logits(x, w_n, b_n)
+    return z + np.asarray(noise, np.float64) * (softplus(zn) + float(eps))
+
+
+def noisy_router(x: np.ndarray, w_g: np.ndarray, b_g: Optional[np.ndarray],
+                 w_n: np.ndarray, b_n: Optional[np.ndarray], noise: np.ndarray, eps: float,
+                 k: int, gate_mode: str) -> Dict[str, np.ndarray]:
+    """Router in training mode with noisy gating: softmax, top-k and gates of
+    the noisy logits, as the clean router does for its logits.
+
+    P2 §2.1 passes the noisy logits to the same top-k gating (softmax over the
+    k selected logits: gate mode 'renorm').  P5 代码实战 takes the softmax of
+    the noisy logits, the arg-max as the top-1 expert, the probability as its
+    weight (gate mode 'prob') and those probabilities in its balance loss, so
+    the column sums here are of the noisy softmax.
+    """
+    z = noisy_router_logits(x, w_g, b_g, w_n, b_n, noise, eps)
+    p = softmax(z)
+    idx = topk_select(z, k)
+    return {"logits": z, "probs": p, "topk_idx": idx, "topk_gate": gates(p, idx, gate_mode),
+            "prob_colsum": np.sum(p, axis=0), "near_tie": near_tie_mask(z, k)}
+
+
 # ---------------------------------------------------------------------------
 # capacity and dispatch
 # ---------------------------------------------------------------------------

@@ -446,3 +446,119 @@ def test_combine_with_every_slot_dropped_is_zero_with_full_width():
     assert out["y"].shape == (T, d) and np.all(out["y"] == 0.0)
     out = O.forward(x, rng.standard_normal((E, d)), None, 2, "renorm", 0, "linear", w, residual=x)
     assert np.array_equal(out["y"], x)
+
+
+# ---------------------------------------------------------------------------
+# noisy gating (P2 §2.1 Noisy Top-k 门控; P5 代码实战 NoisyTop1Gate)
+# ---------------------------------------------------------------------------
+
+
+def _inv_softplus(a):
+    # the u with ln(1 + e^u) = a
+    return math.log(math.expm1(a))
+
+
+def test_softplus_closed_forms_and_library():
+    assert O.softplus(0.0) == pytest.approx(math.log(2.0), rel=1e-15)
+    for a in (0.25, 0.5, 1.0, 2.0, 5.0, 30.0):
+        assert O.softplus(_inv_softplus(a)) == pytest.approx(a, rel=1e-13)
+    u = np.linspace(-40.0, 40.0, 801)
+    # softplus(u) - softplus(-u) = u, and the function never overflows
+    np.testing.assert_allclose(O.softplus(u) - O.softplus(-u), u, atol=1e-12)
+    assert O.softplus(800.0) == 800.0 and 0.0 <= O.softplus(-800.0) < 1e-300
+    ref = torch.nn.functional.softplus(torch.from_numpy(u), threshold=50.0).numpy()
+    np.testing.assert_allclose(O.softplus(u), ref, rtol=1e-14, atol=1e-300)
+
+
+def test_noisy_logits_worked_example_noise_scale_from_the_projection():
+    # P4's three-expert example for the clean logits ([1, 2, 3] from x = [2],
+    # W_g = [0.5, 1, 1.5]); the noise projection W_n x is chosen so that
+    # softplus gives the scales 1, 2 and 0.5 exactly; noise draws 1, -1, 2;
+    # no floor (P2's form): noisy logits 1 + 1, 2 - 2, 3 + 1 by hand
+    x = np.array([[2.0]])
+    w_g = np.array([[0.5], [1.0], [1.5]])
+    w_n = np.array([[_inv_softplus(1.0) / 2], [_inv_softplus(2.0) / 2], [_inv_softplus(0.5) / 2]])
+    noise = np.array([[1.0, -1.0, 2.0]])
+    z = O.noisy_router_logits(x, w_g, None, w_n, None, noise, 0.0)
+    np.testing.assert_allclose(z, [[2.0, 0.0, 4.0]], atol=1e-13)
+    r = O.noisy_router(x, w_g, None, w_n, None, noise, 0.0, 2, "renorm")
+    # top-2 of the noisy logits is {2, 0}; softmax over the two selected logits
+    assert r["topk_idx"].tolist() == [[2, 0]]
+    g_hi = 1.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(r["topk_gate"], [[g_hi, 1.0 - g_hi]], rtol=1e-13)
+    # the clean router would pick {2, 1}: the noise changed the choice
+    assert O.topk_select(O.router_logits(x, w_g), 2).tolist() == [[2, 1]]
+
+
+def test_noisy_logits_worked_example_bias_and_floor():
+    # P5's form: the noise projection has a bias and the scale a floor of
+    # 1e-2.  W_n = 0, so the scales are softplus(b_n) + 0.01 = 1.01, 2.01,
+    # 0.51; draws 1, -1, 2 give 1 + 1.01, 2 - 2.01, 3 + 1.02
+    x = np.array([[2.0]])
+    w_g = np.array([[0.5], [1.0], [1.5]])
+    w_n = np.zeros((3, 1))
+    b_n = np.array([_inv_softplus(1.0), _inv_softplus(2.0), _inv_softplus(0.5)])
+    noise = np.array([[1.0, -1.0, 2.0]])
+    z = O.noisy_router_logits(x, w_g, None, w_n, b_n, noise, 1e-2)
+    np.testing.assert_allclose(z, [[2.01, -0.01, 4.02]], atol=1e-13)
+    r = O.noisy_router(x, w_g, None, w_n, b_n, noise, 1e-2, 1, "prob")
+    assert r["topk_idx"].tolist() == [[2]]
+    den = math.exp(2.01) + math.exp(-0.01) + math.exp(4.02)
+    np.testing.assert_allclose(r["topk_gate"], [[math.exp(4.02) / den]], rtol=1e-13)
+    np.testing.assert_allclose(r["prob_colsum"], np.array([math.exp(2.01), math.exp(-0.01), math.exp(4.02)]) / den,
+                               rtol=1e-13)
+
+
+def test_noisy_router_with_zero_draws_is_the_clean_router():
+    rng = np.random.default_rng(11)
+    T, d, E, k = 40, 24, 10, 3
+    x = rng.standard_normal((T, d))
+    w_g = rng.standard_normal((E, d))
+    b_g = rng.standard_normal(E)
+    w_n = rng.standard_normal((E, d))
+    b_n = rng.standard_normal(E)
+    r = O.noisy_router(x, w_g, b_g, w_n, b_n, np.zeros((T, E)), 1e-2, k, "renorm")
+    z = O.router_logits(x, w_g, b_g)
+    np.testing.assert_array_equal(r["logits"], z)
+    np.testing.assert_array_equal(r["topk_idx"], O.topk_select(z, k))
+    np.testing.assert_array_equal(r["topk_gate"], O.gates(O.softmax(z), O.topk_select(z, k), "renorm"))
+
+
+def test_noisy_scale_is_the_floor_when_the_projection_is_very_negative():
+    # softplus(-60) ~ 9e-27: the logit moves by exactly the draw times 1e-2
+    rng = np.random.default_rng(12)
+    T, d, E = 16, 8, 5
+    x = rng.standard_normal((T, d))
+    w_g = rng.standard_normal((E, d))
+    noise = rng.standard_normal((T, E))
+    z = O.noisy_router_logits(x, w_g, None, np.zeros((E, d)), np.full(E, -60.0), noise, 1e-2)
+    np.testing.assert_allclose(z - O.router_logits(x, w_g), noise * 1e-2, rtol=1e-12, atol=1e-24)
+
+
+def test_noisy_top1_matches_page_gate_module_written_in_torch():
+    # P5 代码实战, NoisyTop1Gate in training mode, with the normal draws
+    # passed in: softplus scale + 1e-2 times the draw added to the gate
+    # logits; softmax; arg-max as the expert; probs times its one-hot as the
+    # routing weights; balance loss E * sum(load * importance)
+    rng = np.random.default_rng(13)
+    T, d, E = 64, 16, 6
+    x = rng.standard_normal((T, d))
+    w_g, b_g = rng.standard_normal((E, d)), rng.standard_normal(E)
+    w_n, b_n = rng.standard_normal((E, d)) * 0.5, rng.standard_normal(E)
+    noise = rng.standard_normal((T, E))
+    F = torch.nn.functional
+    xt = torch.from_numpy(x)
+    logits = F.linear(xt, torch.from_numpy(w_g), torch.from_numpy(b_g))
+    std = F.softplus(F.linear(xt, torch.from_numpy(w_n), torch.from_numpy(b_n)), threshold=50.0) + 1e-2
+    logits = logits + torch.from_numpy(noise) * std
+    probs = F.softmax(logits, dim=-1)
+    top = torch.argmax(logits, dim=-1)
+    mask = F.one_hot(top, num_classes=E).double()
+    route = probs * mask
+    aux = E * torch.sum(mask.mean(dim=0) * probs.mean(dim=0))
+
+    r = O.noisy_router(x, w_g, b_g, w_n, b_n, noise, 1e-2, 1, "prob")
+    np.testing.assert_array_equal(r["topk_idx"][:, 0], top.numpy())
+    np.testing.assert_allclose(r["topk_gate"][:, 0], route.sum(dim=-1).numpy(), rtol=1e-12)
+    counts = np.bincount(r["topk_idx"][:, 0], minlength=E)
+    np.testing.assert_allclose(O.aux_loss(counts, r["prob_colsum"], T, 1, E, 1.0), aux.item(), rtol=1e-12)
