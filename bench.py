@@ -47,9 +47,11 @@ def stage_bytes(cfg, a_kept: int) -> dict:
     sx = 4 if cfg.act_dtype == "f32" else 2
     T, d, E, k, do = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_out
     router = T * d * sx + E * d * 4 + T * k * 8 + E * 4
+    # noisy gating adds the noise projection, its bias and the draws
+    router_noisy = router + E * d * 4 + E * 4 + T * E * 4
     dispatch = T * k * 4 + T * d * sx + a_kept * d * sx + T * k * 4 * 2
     combine = a_kept * do * sx + T * k * 8 + T * do * sx + (cfg.n_shared * T * do * sx)
-    return {"router": router, "dispatch": dispatch, "combine": combine}
+    return {"router": router, "dispatch": dispatch, "combine": combine, "router_noisy": router_noisy}
 
 
 FFN_SOURCES = ("ffn.hip", "grouped_gemm.hip", "moe_internal.hpp")
@@ -204,6 +206,14 @@ def main():
         return a.elapsed_time(b) / args.steps
     loop_st_ms = {"router": loop_ms(lambda: layer.router(x)), "dispatch": loop_ms(lambda: layer.dispatch(x)),
                   "combine": loop_ms(layer.combine), "aux": loop_ms(layer.aux)}
+    # the training-mode router with noisy gating (normal draws and the noise
+    # projection resident like the other inputs; floor 1e-2), timed the same
+    # way; it rewrites the router outputs, so the layer router runs again after
+    w_n, b_n, noise = W.gen_noisy_gate(cfg)
+    w_n, b_n, noise = to_tensor(w_n, "cuda"), to_tensor(b_n, "cuda"), to_tensor(noise, "cuda")
+    loop_st_ms["router_noisy"] = loop_ms(lambda: layer.router_noisy(x, w_n, b_n, noise, 1e-2))
+    layer.router(x)
+    torch.cuda.synchronize()
 
     # timed region 3 (reported apart, labelled cold): every step after a
     # 512 MB scratch write, so that no input is left in the 256 MB
@@ -270,7 +280,7 @@ def main():
         },
         "stages_ms_loop": loop_st_ms,
         "stages_hbm_frac_loop": {k_: byts[k_] / (loop_st_ms[k_] * 1e-3) / 1e9 / PEAK_HBM_GBPS
-                                 for k_ in ("router", "dispatch", "combine")},
+                                 for k_ in ("router", "dispatch", "combine", "router_noisy")},
         "shared_tflops": (sh_flops / (st_ms["shared"] * 1e-3) / 1e12) if cfg.n_shared else None,
         "kept_rows": a_kept,
         "cold": {

@@ -128,6 +128,38 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
                     hipStream_t stream);
 
 /*
+ * ---- (a') Router with noisy gating (training mode) ---------------------------
+ * P2 §2.1 (Noisy Top-k 门控): the router logits get a standard normal draw
+ * times softplus(x W_noise) added before the top-k gating; P5 代码实战
+ * (NoisyTop1Gate) gives the noise projection a bias and adds a floor of 1e-2
+ * to the scale.  Per token t and expert e:
+ *   z[t,e] = (x W_g^T)[t,e] + b_g[e]
+ *            + noise[t,e] * (softplus((x W_n^T)[t,e] + b_n[e]) + noise_eps)
+ * then everything as moe_router_topk does with its logits: fp32 softmax of
+ * z, top-k of z, gates per `gate_mode` (MOE_GATE_RENORM is P2's softmax over
+ * the selected noisy logits; MOE_GATE_PROB with k = 1 is P5's gate),
+ * prob_colsum of the noisy softmax, logits_dbg = z.
+ *
+ *   w_n         [E, d]  fp32 noise projection
+ *   b_n         [E]     fp32, or NULL for no bias
+ *   noise       [T, E]  fp32 in: the normal draws, one per token and expert
+ *                       (drawn by the caller, so that a run can be replayed)
+ *   noise_eps   >= 0 and finite (0: P2's form, 1e-2: P5's), else
+ *               MOE_ERR_INVALID_ARG
+ * Every other argument, constraint and error as for moe_router_topk; the
+ * workspace is sized by moe_router_noisy_workspace_size.  w_n and noise
+ * must be 16-byte aligned; noise may be NULL only when T == 0.  Inference
+ * (no noise) is moe_router_topk.
+ */
+size_t moe_router_noisy_workspace_size(int T, int d, int E, int x_dt);
+int moe_router_topk_noisy(const void* x, int x_dt, const float* w_g, const float* b_g,
+                          const float* w_n, const float* b_n, const float* noise, float noise_eps,
+                          int T, int d, int E, int k, int gate_mode,
+                          int32_t* topk_idx, float* topk_gate, float* prob_colsum,
+                          float* logits_dbg, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * ---- (b) Dispatch: histogram, scan, stable token-order rank, capacity, permute
  * P1 §2.4: tokens of one expert are gathered together, run as a batch, and
  * scattered back.  P5 专家容量: beyond the capacity the remaining tokens skip

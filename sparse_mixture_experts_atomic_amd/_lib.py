@@ -44,6 +44,9 @@ _SIGS = {
     "moe_capacity": (_i, [_i, _i, _i, ctypes.c_double, _i]),
     "moe_router_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_router_topk": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_router_noisy_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "moe_router_topk_noisy": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                   _vp, _sz, _vp]),
     "moe_dispatch_workspace_size": (_sz, [_i, _i, _i]),
     "moe_dispatch_permute": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_ffn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
@@ -139,6 +142,21 @@ def router_topk(x, w_g, b_g, k, gate_mode, topk_idx, topk_gate, prob_colsum=None
                                _p(topk_idx), _p(topk_gate), _p(prob_colsum), _p(logits_dbg),
                                _p(workspace), ws_bytes, _stream(stream))
     _check("moe_router_topk", st)
+
+
+def router_noisy_workspace_size(T, d, E, x_dt) -> int:
+    return lib().moe_router_noisy_workspace_size(T, d, E, x_dt)
+
+
+def router_topk_noisy(x, w_g, b_g, w_n, b_n, noise, noise_eps, k, gate_mode, topk_idx, topk_gate,
+                      prob_colsum=None, logits_dbg=None, workspace=None, stream=None):
+    T, d = x.shape
+    E = w_g.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().moe_router_topk_noisy(_p(x), dtype_code(x), _p(w_g), _p(b_g), _p(w_n), _p(b_n), _p(noise),
+                                     float(noise_eps), T, d, E, k, gate_mode, _p(topk_idx), _p(topk_gate),
+                                     _p(prob_colsum), _p(logits_dbg), _p(workspace), ws_bytes, _stream(stream))
+    _check("moe_router_topk_noisy", st)
 
 
 def dispatch_permute(topk_idx, E, capacity_, x, x_perm, counts_routed, counts_kept, offsets, dest_pos,

@@ -27,7 +27,15 @@ struct RouterArgs {
   float* topk_gate;
   float* colsum_part;   // [gridDim.x, E]
   float* logits_dbg;
+  // noisy gating: z += noise[t, e] * (softplus((x W_n^T)[t, e] + b_n[e]) + eps)
+  const float* w_n;
+  const float* b_n;
+  const float* noise;   // [T, E] standard normal draws
+  float eps;
 };
+
+// ln(1 + e^u) without overflow for large u or loss of the small term
+__device__ __forceinline__ float softplus_f(float u) { return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))); }
 
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -182,7 +190,7 @@ __device__ __forceinline__ float token8_softmax_topk(float z, int e, int t, cons
 // registers (2 tokens x 4 experts per thread per 64-expert group) from LDS
 // tiles of x and W_g, then kept in LDS for the softmax/top-k phase, which
 // runs one wavefront per token.
-template <typename XT>
+template <typename XT, bool NOISY>
 __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a) {
   extern __shared__ float smem[];
   float* xs = smem;                          // [kRtDc][kRtTok]
@@ -196,10 +204,14 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
   const int tx = tid & 15;                   // expert quad
   const int ty = tid >> 4;                   // token pair
 
-  for (int eg = 0; eg < a.E; eg += kRtExp) {
-    // each 32-column chunk is summed in fp32, the running total in fp64, so
-    // the rounding error does not grow with d the way one long fp32 chain does
-    double tot[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  // logits of 32 tokens x experts [eg, eg + 64) against the rows of W: each
+  // 32-column chunk is summed in fp32, the running total in fp64, so the
+  // rounding error does not grow with d the way one long fp32 chain does
+  auto logits = [&](const float* W, int eg, double (&tot)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tot[i][j] = 0.0;
     for (int c0 = 0; c0 < a.d; c0 += kRtDc) {
       float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       // x chunk: 32 tokens x 32 columns, 4 per thread, stored column-major
@@ -222,7 +234,7 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
         for (int i = 0; i < 8; ++i) {
           int cg = c0 + c + i;
           float v = 0.f;
-          if (eg2 < a.E && cg < a.d) v = a.w_g[static_cast<size_t>(eg2) * a.d + cg];
+          if (eg2 < a.E && cg < a.d) v = W[static_cast<size_t>(eg2) * a.d + cg];
           ws[(c + i) * kRtExp + e] = v;
         }
       }
@@ -247,6 +259,11 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
         for (int j = 0; j < 4; ++j) tot[i][j] += static_cast<double>(acc[i][j]);
       __syncthreads();
     }
+  };
+
+  for (int eg = 0; eg < a.E; eg += kRtExp) {
+    double tot[2][4];
+    logits(a.w_g, eg, tot);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -258,6 +275,22 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
           lg[(ty * 2 + i) * a.E + e] = v;
         }
       }
+    if constexpr (NOISY) {
+      // the same thread owns the same logits in both passes
+      logits(a.w_n, eg, tot);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = eg + tx * 4 + j;
+          const int t = t0 + ty * 2 + i;
+          if (e < a.E && t < a.T) {
+            float u = static_cast<float>(tot[i][j]);
+            if (a.b_n) u += a.b_n[e];
+            lg[(ty * 2 + i) * a.E + e] += a.noise[static_cast<size_t>(t) * a.E + e] * (softplus_f(u) + a.eps);
+          }
+        }
+    }
   }
   __syncthreads();
 
@@ -453,6 +486,10 @@ __global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a,
 // it, and x is staged beside it.  Four wavefronts of (BM / 2) tokens x 32
 // experts run v_mfma_f32_16x16x32_bf16 (one per plane).  The slice's partial
 // logits go to part[slice][t][e]; router_finish_kernel adds the slices.
+// The E rows are those of W_g stacked on those of the noise projection W_n:
+// rows e < E1 come from W_g, the others from row e - E1 of W_n (E1 = E for
+// the clean router, E = 2 E1 for noisy gating; the noisy router takes this
+// kernel for any number of experts).
 constexpr int kLgBN = 64;                     // experts per block
 constexpr int kLgBK = 64;                     // columns per LDS chunk
 constexpr int kLgPad = kLgBK + 8;             // LDS row pitch (bf16): 16 rows of a read hit distinct banks
@@ -460,8 +497,9 @@ constexpr int kLgThreads = 256;
 
 template <int BM>
 __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                                  const float* __restrict__ w_g, int T, int d, int E,
-                                                                  int kslice, float* __restrict__ part) {
+                                                                  const float* __restrict__ w_g,
+                                                                  const float* __restrict__ w_n, int E1, int T,
+                                                                  int d, int E, int kslice, float* __restrict__ part) {
   constexpr int WT = BM / 2;                  // tokens per wavefront
   constexpr int FT = WT / 16;                 // 16-token fragments per wavefront
   constexpr int XL = BM * kLgBK / 8 / kLgThreads;     // 16-byte x loads per thread and chunk
@@ -502,8 +540,8 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
       const int q = tid + kLgThreads * i;
       const int r = q / (kLgBK / 4), c = (q % (kLgBK / 4)) * 4;
       const int e = e0 + r, col = kc + c;
-      wr[i] = (e < E && col < k1) ? *reinterpret_cast<const float4*>(w_g + static_cast<size_t>(e) * d + col)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float* wrow = e < E1 ? w_g + static_cast<size_t>(e) * d : w_n + static_cast<size_t>(e - E1) * d;
+      wr[i] = (e < E && col < k1) ? *reinterpret_cast<const float4*>(wrow + col) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   if (k0 < k1) load(k0);
@@ -572,9 +610,13 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
 // Sum of the logit slices (in slice order) plus the router bias, then the
 // fp32 softmax and top-k of each token by one wavefront, and per-block
 // probability column sums (wavefronts added in order) to the workspace.
+// NOISY: the partial rows hold 2 E logits per token, the clean ones then the
+// noise projection's; the noisy logit is clean + b_g + draw * (softplus(
+// projection + b_n) + eps).
 constexpr int kFnTok = 16;                    // tokens per block
 constexpr int kFnWaves = 8;
 
+template <bool NOISY>
 __global__ __launch_bounds__(64 * kFnWaves) void router_finish_kernel(RouterArgs a, const float* __restrict__ part,
                                                                        int nslice) {
   __shared__ float lg[kFnTok * kRtMaxE];
@@ -588,22 +630,39 @@ __global__ __launch_bounds__(64 * kFnWaves) void router_finish_kernel(RouterArgs
   // wavefront per token
   constexpr int kPer = kFnTok * kRtMaxE / (64 * kFnWaves);   // entries per thread at most
   const int n_ent = min(kFnTok, a.T - t0) * a.E;             // the block's tokens are contiguous
-  const float* src = part + static_cast<size_t>(t0) * a.E;
-  float z[kPer];
+  const int PE = NOISY ? 2 * a.E : a.E;                      // partial logits per token
+  const float* src = part + static_cast<size_t>(t0) * PE;
+  float z[kPer], zn[kPer];
+  int off[kPer];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) z[u] = 0.f;
-  // unconditional loads (clamped index) so that they are all in flight at
-  // once; entries past the block's tokens are not stored
+  for (int u = 0; u < kPer; ++u) {
+    // unconditional loads (clamped index) so that they are all in flight at
+    // once; entries past the block's tokens are not stored
+    const int j = min(tid + 64 * kFnWaves * u, n_ent - 1);
+    off[u] = NOISY ? (j / a.E) * PE + j % a.E : j;
+    z[u] = 0.f;
+    zn[u] = 0.f;
+  }
   for (int sl = 0; sl < nslice; ++sl) {
+    const float* ps = src + static_cast<size_t>(sl) * a.T * PE;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int j = min(tid + 64 * kFnWaves * u, n_ent - 1);
-      z[u] += src[static_cast<size_t>(sl) * a.T * a.E + j];
+      z[u] += ps[off[u]];
+      if constexpr (NOISY) zn[u] += ps[off[u] + a.E];
     }
   }
   if (a.b_g) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) z[u] += a.b_g[min(tid + 64 * kFnWaves * u, n_ent - 1) % a.E];
+  }
+  if constexpr (NOISY) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = min(tid + 64 * kFnWaves * u, n_ent - 1);
+      float v = zn[u];
+      if (a.b_n) v += a.b_n[j % a.E];
+      z[u] += a.noise[static_cast<size_t>(t0) * a.E + j] * (softplus_f(v) + a.eps);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
@@ -681,6 +740,91 @@ inline size_t logit_ws_offset(int T, int E) {
   return align_up(static_cast<size_t>(router_max_blocks(T)) * E * sizeof(float), kWsAlign);
 }
 
+// the launches of both entry points; arguments already validated.  noise ==
+// nullptr: the clean router.  bf16: MFMA kernels (clean with up to 8
+// experts: whole rows per block, one launch; otherwise the tiled logits GEMM,
+// then the finishing kernel); fp32 activations: the generic kernel.
+int router_run(const void* x, int x_dt, const float* w_g, const float* b_g, const float* w_n, const float* b_n,
+               const float* noise, float eps, int T, int d, int E, int k, int gate_mode, int32_t* topk_idx,
+               float* topk_gate, float* prob_colsum, float* logits_dbg, void* workspace, hipStream_t stream) {
+  const bool noisy = noise != nullptr;
+  const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE && !noisy;
+  const bool mf = x_dt == MOE_BF16 && !m8;
+  float* part = static_cast<float*>(workspace);
+  int kw8 = 1, tg8 = 1;
+  mf8_shape(T, d, kw8, tg8);
+  const int nb = m8 ? (T + 16 * tg8 - 1) / (16 * tg8) : (mf ? (T + kFnTok - 1) / kFnTok : router_blocks(T));
+  RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg, w_n, b_n, noise, eps};
+  if (T > 0 && m8) {
+    hipLaunchKernelGGL(router_mf8_kernel, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+  }
+  if (T > 0 && mf) {
+    // noisy: the logits GEMM runs over W_g stacked on W_n (2 E rows)
+    const int EL = noisy ? 2 * E : E;
+    float* lgp = reinterpret_cast<float*>(static_cast<char*>(workspace) + logit_ws_offset(T, E));
+    const int bm = logit_bm(T), ks = logit_slices(T, d, EL), kslice = logit_kslice(d, ks);
+    const dim3 grid((T + bm - 1) / bm, (EL + kLgBN - 1) / kLgBN, ks);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const float* wn = noisy ? w_n : w_g;
+    if (bm == 128)
+      hipLaunchKernelGGL(router_logits_kernel<128>, grid, dim3(kLgThreads), 0, stream, xb, w_g, wn, E, T, d, EL,
+                         kslice, lgp);
+    else
+      hipLaunchKernelGGL(router_logits_kernel<64>, grid, dim3(kLgThreads), 0, stream, xb, w_g, wn, E, T, d, EL,
+                         kslice, lgp);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+    if (noisy)
+      hipLaunchKernelGGL(router_finish_kernel<true>, dim3(nb), dim3(64 * kFnWaves), 0, stream, a,
+                         static_cast<const float*>(lgp), ks);
+    else
+      hipLaunchKernelGGL(router_finish_kernel<false>, dim3(nb), dim3(64 * kFnWaves), 0, stream, a,
+                         static_cast<const float*>(lgp), ks);
+    st = check_launch();
+    if (st != MOE_OK) return st;
+  }
+  if (T > 0 && !mf && !m8) {
+    size_t lds = (static_cast<size_t>(kRtDc) * kRtTok + static_cast<size_t>(kRtDc) * kRtExp +
+                  static_cast<size_t>(kRtTok) * E + 4 * static_cast<size_t>(E)) * sizeof(float);
+    if (noisy)
+      hipLaunchKernelGGL((router_generic_kernel<float, true>), dim3(nb), dim3(kRtThreads), lds, stream, a);
+    else
+      hipLaunchKernelGGL((router_generic_kernel<float, false>), dim3(nb), dim3(kRtThreads), lds, stream, a);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+  }
+  if (prob_colsum) {
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(E), dim3(256), 0, stream,
+                       static_cast<const float*>(part), nb, E, prob_colsum);
+    int st = check_launch();
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+// argument checks shared by both entry points (workspace excluded)
+int router_check(const void* x, int x_dt, const float* w_g, const float* b_g, int T, int d, int E, int k,
+                 int gate_mode, int32_t* topk_idx, float* topk_gate, float* prob_colsum, float* logits_dbg) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kRtMaxE || k > kRtMaxK) return MOE_ERR_UNSUPPORTED;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (x_dt == MOE_BF16 && d % 8 != 0) return MOE_ERR_INVALID_ARG;   // 16-byte row pieces
+  if (gate_mode != MOE_GATE_PROB && gate_mode != MOE_GATE_RENORM) return MOE_ERR_INVALID_ARG;
+  if (!w_g || !aligned16(w_g) || (b_g && !aligned16(b_g))) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (topk_idx && !aligned16(topk_idx)) || (topk_gate && !aligned16(topk_gate)) ||
+      (prob_colsum && !aligned16(prob_colsum)) || (logits_dbg && !aligned16(logits_dbg)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+inline bool workspace_ok(int T, const float* prob_colsum, const void* workspace, size_t have, size_t need) {
+  if ((T > 0 || prob_colsum) && (!workspace || have < need || !aligned16(workspace))) return false;
+  return true;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -700,70 +844,37 @@ size_t moe_router_workspace_size(int T, int d, int E, int x_dt) {
 int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g, int T, int d, int E,
                     int k, int gate_mode, int32_t* topk_idx, float* topk_gate, float* prob_colsum,
                     float* logits_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
-  if (E > kRtMaxE || k > kRtMaxK) return MOE_ERR_UNSUPPORTED;
-  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (x_dt == MOE_BF16 && d % 8 != 0) return MOE_ERR_INVALID_ARG;   // 16-byte row pieces
-  if (gate_mode != MOE_GATE_PROB && gate_mode != MOE_GATE_RENORM) return MOE_ERR_INVALID_ARG;
-  if (!w_g || !aligned16(w_g) || (b_g && !aligned16(b_g))) return MOE_ERR_INVALID_ARG;
-  if (T > 0 && (!x || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
-  if ((x && !aligned16(x)) || (topk_idx && !aligned16(topk_idx)) || (topk_gate && !aligned16(topk_gate)) ||
-      (prob_colsum && !aligned16(prob_colsum)) || (logits_dbg && !aligned16(logits_dbg)))
-    return MOE_ERR_INVALID_ARG;
-  const size_t need = moe_router_workspace_size(T, d, E, x_dt);
-  if (prob_colsum && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
-  if (T > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
+  int st = router_check(x, x_dt, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, prob_colsum, logits_dbg);
+  if (st != MOE_OK) return st;
+  if (!workspace_ok(T, prob_colsum, workspace, workspace_bytes, moe_router_workspace_size(T, d, E, x_dt)))
+    return MOE_ERR_WORKSPACE;
+  return router_run(x, x_dt, w_g, b_g, nullptr, nullptr, nullptr, 0.f, T, d, E, k, gate_mode, topk_idx, topk_gate,
+                    prob_colsum, logits_dbg, workspace, stream);
+}
 
-  // bf16: MFMA kernels (up to 8 experts: whole rows per block, one launch;
-  // beyond: the tiled logits GEMM, then the finishing kernel); fp32
-  // activations: the generic kernel
-  const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE;
-  const bool mf = x_dt == MOE_BF16 && !m8;
-  float* part = static_cast<float*>(workspace);
-  int kw8 = 1, tg8 = 1;
-  mf8_shape(T, d, kw8, tg8);
-  const int nb = m8 ? (T + 16 * tg8 - 1) / (16 * tg8) : (mf ? (T + kFnTok - 1) / kFnTok : router_blocks(T));
-  if (T > 0 && m8) {
-    RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
-    hipLaunchKernelGGL(router_mf8_kernel, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
-    int st = check_launch();
-    if (st != MOE_OK) return st;
-  }
-  if (T > 0 && mf) {
-    RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
-    float* lgp = reinterpret_cast<float*>(static_cast<char*>(workspace) + logit_ws_offset(T, E));
-    const int bm = logit_bm(T), ks = logit_slices(T, d, E), kslice = logit_kslice(d, ks);
-    const dim3 grid((T + bm - 1) / bm, (E + kLgBN - 1) / kLgBN, ks);
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (bm == 128)
-      hipLaunchKernelGGL(router_logits_kernel<128>, grid, dim3(kLgThreads), 0, stream, xb, w_g, T, d, E, kslice, lgp);
-    else
-      hipLaunchKernelGGL(router_logits_kernel<64>, grid, dim3(kLgThreads), 0, stream, xb, w_g, T, d, E, kslice, lgp);
-    int st = check_launch();
-    if (st != MOE_OK) return st;
-    hipLaunchKernelGGL(router_finish_kernel, dim3(nb), dim3(64 * kFnWaves), 0, stream, a,
-                       static_cast<const float*>(lgp), ks);
-    st = check_launch();
-    if (st != MOE_OK) return st;
-  }
-  if (T > 0 && !mf && !m8) {
-    RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg};
-    size_t lds = (static_cast<size_t>(kRtDc) * kRtTok + static_cast<size_t>(kRtDc) * kRtExp +
-                  static_cast<size_t>(kRtTok) * E + 4 * static_cast<size_t>(E)) * sizeof(float);
-    if (x_dt == MOE_F32)
-      hipLaunchKernelGGL(router_generic_kernel<float>, dim3(nb), dim3(kRtThreads), lds, stream, a);
-    else
-      hipLaunchKernelGGL(router_generic_kernel<uint16_t>, dim3(nb), dim3(kRtThreads), lds, stream, a);
-    int st = check_launch();
-    if (st != MOE_OK) return st;
-  }
-  if (prob_colsum) {
-    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(E), dim3(256), 0, stream,
-                       static_cast<const float*>(part), nb, E, prob_colsum);
-    int st = check_launch();
-    if (st != MOE_OK) return st;
-  }
-  return MOE_OK;
+size_t moe_router_noisy_workspace_size(int T, int d, int E, int x_dt) {
+  if (T < 0 || E < 1) return 0;
+  size_t s = logit_ws_offset(T, E);
+  // partial logits of the tiled GEMM over W_g and W_n (2 E rows)
+  if (x_dt == MOE_BF16 && d > 0)
+    s += align_up(static_cast<size_t>(logit_slices(T, d, 2 * E)) * T * 2 * E * sizeof(float), kWsAlign);
+  return s;
+}
+
+int moe_router_topk_noisy(const void* x, int x_dt, const float* w_g, const float* b_g, const float* w_n,
+                          const float* b_n, const float* noise, float noise_eps, int T, int d, int E, int k,
+                          int gate_mode, int32_t* topk_idx, float* topk_gate, float* prob_colsum,
+                          float* logits_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = router_check(x, x_dt, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, prob_colsum, logits_dbg);
+  if (st != MOE_OK) return st;
+  if (!w_n || !aligned16(w_n) || (b_n && !aligned16(b_n))) return MOE_ERR_INVALID_ARG;
+  if ((T > 0 && !noise) || (noise && !aligned16(noise))) return MOE_ERR_INVALID_ARG;
+  if (!(noise_eps >= 0.f) || noise_eps > 3.0e38f) return MOE_ERR_INVALID_ARG;   // NaN, negative or infinite
+  if (!workspace_ok(T, prob_colsum, workspace, workspace_bytes, moe_router_noisy_workspace_size(T, d, E, x_dt)))
+    return MOE_ERR_WORKSPACE;
+  // no tokens: only the (zero) column sums, as the clean router writes them
+  return router_run(x, x_dt, w_g, b_g, w_n, b_n, T > 0 ? noise : nullptr, noise_eps, T, d, E, k, gate_mode,
+                    topk_idx, topk_gate, prob_colsum, logits_dbg, workspace, stream);
 }
 
 }  // extern "C"

@@ -63,6 +63,15 @@ class MoELayer:
         L.router_topk(x, self.w["w_g"], self.w.get("b_g"), self.k, self.gate, self.topk_idx, self.topk_gate,
                       self.prob_colsum, None, self.ws_router)
 
+    def router_noisy(self, x, w_n, b_n, noise, eps=1e-2):
+        """Training-mode router with noisy gating: the same outputs as router(),
+        from logits with noise[t, e] * (softplus(x W_n^T + b_n) + eps) added."""
+        if getattr(self, "ws_router_noisy", None) is None:
+            act = L.F32 if self.act_dtype == torch.float32 else L.BF16
+            self.ws_router_noisy = self._ws(L.router_noisy_workspace_size(self.T, self.d, self.E, act), x.device)
+        L.router_topk_noisy(x, self.w["w_g"], self.w.get("b_g"), w_n, b_n, noise, eps, self.k, self.gate,
+                            self.topk_idx, self.topk_gate, self.prob_colsum, None, self.ws_router_noisy)
+
     def dispatch(self, x, topk_idx=None):
         L.dispatch_permute(self.topk_idx if topk_idx is None else topk_idx, self.E, self.capacity, x, self.x_perm,
                            self.counts_routed, self.counts_kept, self.offsets, self.dest_pos, self.perm_token,

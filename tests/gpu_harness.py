@@ -63,6 +63,36 @@ def act_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def compare_router(name, z, k, gate_mode, idx_g, gate_g, colsum_g):
+    """GPU router outputs against the oracle's logits z (float64 [T, E]).
+
+    Top-k ids bit-exact on tokens without a near-tie; everywhere a valid
+    top-k set in descending order; gates and column sums within 1e-5
+    relative.  Returns the near-tie mask and the two errors."""
+    T, E = z.shape
+    p = O.softmax(z)
+    idx_o = O.topk_select(z, k)
+    tie = O.near_tie_mask(z, k, GAP)
+    ok = ~tie
+    mism = int(np.sum(np.any(idx_g[ok] != idx_o[ok], axis=1)))
+    assert mism == 0, f"{name}: {mism} untied tokens differ in top-k ids"
+    # validity everywhere (near-tied tokens may pick another valid set)
+    assert np.all((idx_g >= 0) & (idx_g < E))
+    srt = np.sort(idx_g, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1]) if k > 1 else True
+    if T:
+        sel = np.take_along_axis(z, idx_g.astype(np.int64), axis=1)
+        kth = -np.sort(-z, axis=1)[:, k - 1]
+        assert np.all(sel >= kth[:, None] - GAP)
+        assert np.all(np.diff(sel, axis=1) <= GAP)
+    g_ref = O.gates(p, idx_g, gate_mode)
+    eg = rel_err(gate_g, g_ref, floor_frac=1e-30)
+    assert eg <= 1e-5, f"{name}: gate rel err {eg:.3e}"
+    ec = rel_err(colsum_g, p.sum(axis=0))
+    assert ec <= 1e-5, f"{name}: prob_colsum rel err {ec:.3e}"
+    return tie, eg, ec
+
+
 class Run:
     """One workload uploaded to the GPU with its oracle-side float64 views."""
 
@@ -111,26 +141,7 @@ class Run:
         idx_g = self.layer.topk_idx.cpu().numpy()
         gate_g = self.layer.topk_gate.cpu().numpy().astype(np.float64)
         colsum_g = self.layer.prob_colsum.cpu().numpy().astype(np.float64)
-        z = self.z
-        p = O.softmax(z)
-        idx_o = O.topk_select(z, cfg.k)
-        tie = O.near_tie_mask(z, cfg.k, GAP)
-        ok = ~tie
-        mism = int(np.sum(np.any(idx_g[ok] != idx_o[ok], axis=1)))
-        assert mism == 0, f"{cfg.name}: {mism} untied tokens differ in top-k ids"
-        # validity everywhere (near-tied tokens may pick another valid set)
-        assert np.all((idx_g >= 0) & (idx_g < cfg.E))
-        srt = np.sort(idx_g, axis=1)
-        assert np.all(srt[:, 1:] != srt[:, :-1]) if cfg.k > 1 else True
-        sel = np.take_along_axis(z, idx_g.astype(np.int64), axis=1)
-        kth = -np.sort(-z, axis=1)[:, cfg.k - 1]
-        assert np.all(sel >= kth[:, None] - GAP)
-        assert np.all(np.diff(sel, axis=1) <= GAP)
-        g_ref = O.gates(p, idx_g, cfg.gate)
-        eg = rel_err(gate_g, g_ref, floor_frac=1e-30)
-        assert eg <= 1e-5, f"{cfg.name}: gate rel err {eg:.3e}"
-        ec = rel_err(colsum_g, p.sum(axis=0))
-        assert ec <= 1e-5, f"{cfg.name}: prob_colsum rel err {ec:.3e}"
+        tie, eg, ec = compare_router(cfg.name, self.z, cfg.k, cfg.gate, idx_g, gate_g, colsum_g)
         self.idx_g, self.gate_g, self.colsum_g, self.tie = idx_g, gate_g, colsum_g, tie
         say(f"router {cfg.name}: T={cfg.T} E={cfg.E} k={cfg.k} near-tied {int(tie.sum())} "
             f"gate err {eg:.2e} colsum err {ec:.2e}")

@@ -81,6 +81,34 @@ def test_router_validation_before_launch():
     assert lib.moe_router_topk(fake, L.BF16, fake, None, 8, 16, 512, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_UNSUPPORTED
 
 
+def test_noisy_router_validation_before_launch():
+    lib = L.lib()
+    fake = 1 << 20    # never dereferenced: validation fails first
+    f = lib.moe_router_topk_noisy
+
+    def call(x=fake, dt=L.BF16, wg=fake, wn=fake, bn=None, noise=fake, eps=1e-2, T=8, d=16, E=4, k=2, mode=0,
+             ws=fake, wsb=1 << 20):
+        return f(x, dt, wg, None, wn, bn, noise, eps, T, d, E, k, mode, fake, fake, None, None, ws, wsb, None)
+
+    assert call(k=5) == L.ERR_INVALID_ARG
+    assert call(wn=None) == L.ERR_INVALID_ARG
+    assert call(wn=fake + 4) == L.ERR_INVALID_ARG
+    assert call(bn=fake + 4) == L.ERR_INVALID_ARG
+    assert call(noise=None) == L.ERR_INVALID_ARG
+    assert call(noise=fake + 4) == L.ERR_INVALID_ARG
+    assert call(eps=-1e-3) == L.ERR_INVALID_ARG
+    assert call(eps=float("nan")) == L.ERR_INVALID_ARG
+    assert call(eps=float("inf")) == L.ERR_INVALID_ARG
+    assert call(d=12) == L.ERR_INVALID_ARG
+    assert call(ws=None, wsb=0) == L.ERR_WORKSPACE
+    assert call(wsb=L.router_noisy_workspace_size(8, 16, 4, L.BF16) - 16) == L.ERR_WORKSPACE
+    assert call(E=512) == L.ERR_UNSUPPORTED
+    # the noisy logits GEMM stacks W_g on W_n: twice the partial logits of
+    # the clean router's tiled path, and room for them also at 8 experts
+    assert L.router_noisy_workspace_size(4096, 4096, 8, L.BF16) > L.router_workspace_size(4096, 4096, 8, L.BF16)
+    assert L.router_noisy_workspace_size(64, 32, 4, L.F32) == L.router_workspace_size(64, 32, 4, L.F32)
+
+
 def test_dispatch_validation_before_launch():
     lib = L.lib()
     f = 1 << 20

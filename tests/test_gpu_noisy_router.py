@@ -1,0 +1,107 @@
+"""GPU parity of the noisy-gating router (moe_router_topk_noisy) against the
+oracle's noisy_router on the same seeded inputs and normal draws.
+
+Noisy logits: P2 §2.1 (Noisy Top-k 门控; no floor) and P5 代码实战
+(NoisyTop1Gate in training mode: bias on the noise projection, floor 1e-2,
+top-1 with the probability as its gate).  The comparison protocol is the
+clean router's: ids bit-exact on tokens without a near-tie (gap 1e-5),
+gates and probability column sums within 1e-5 relative; the returned noisy
+logits within 1e-5 of the oracle's, relative to max(1, |z|) of the row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_harness import compare_router, say
+from sparse_mixture_experts_atomic_amd import _lib as L
+from workloads.device import to_tensor
+
+pytestmark = pytest.mark.gpu
+
+# name -> (workload, noise floor eps, bias on the noise projection)
+CASES = {
+    # Mixtral-shaped router with P2's noisy top-2 (no floor, no bias)
+    "mixtral_p2": (W.MIXTRAL, 0.0, False),
+    # Switch-shaped top-1 router with P5's gate (bias, floor 1e-2)
+    "switch_p5_top1": (W.SWITCH, 1e-2, True),
+    # DeepSeekMoE-shaped router: 64 experts, top-6, router bias
+    "deepseek": (W.DEEPSEEK, 1e-2, True),
+    # fp32 activations (the generic kernel), the small workload
+    "tiny_f32": (W.TINY, 1e-2, True),
+    # fp32, two 64-expert groups with a ragged second one, ragged tokens
+    "f32_ragged": (W.TINY.scaled(name="f32_ragged", T=333, d=40, d_out=40, E=70, k=5, seed=21), 0.0, True),
+    # bf16: partial 64-column chunk, 2 E = 40 rows in one expert block
+    "bf16_tails": (W.MIXTRAL.scaled(name="bf16_tails", T=77, d=72, d_out=72, E=20, k=3, gate="prob",
+                                    wg_dist=("normal", 1.0 / 72), bg_var=0.5, seed=22), 1e-2, True),
+    # bf16 at the largest expert count: 2 E = 512 rows in 8 expert blocks
+    "bf16_e256": (W.MIXTRAL.scaled(name="bf16_e256", T=300, d=256, d_out=256, E=256, k=8, gate="renorm",
+                                   wg_dist=("normal", 1.0 / 256), seed=23), 0.0, True),
+    # bf16 split over K slices with a partial last chunk
+    "bf16_kslices": (W.MIXTRAL.scaled(name="bf16_kslices", T=300, d=1544, d_out=1544, E=70, k=5, gate="prob",
+                                      wg_dist=("normal", 1.0 / 1544), seed=24), 1e-2, False),
+    # bf16 with 128-token blocks (T >= 8192), narrow rows
+    "bf16_bm128": (W.MIXTRAL.scaled(name="bf16_bm128", T=8200, d=64, d_out=64, E=8, k=2,
+                                    wg_dist=("normal", 1.0 / 64), seed=25), 1e-2, True),
+}
+
+
+def _run(x, w_g, b_g, w_n, b_n, noise, eps, k, gate, T, d, E, dt):
+    dev = "cuda"
+    t = lambda a: to_tensor(a, dev)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    gte = torch.full((T, k), -7.0, dtype=torch.float32, device=dev)
+    colsum = torch.full((E,), -7.0, dtype=torch.float32, device=dev)
+    lg = torch.full((T, E), -7.0, dtype=torch.float32, device=dev)
+    ws_bytes = max(L.router_noisy_workspace_size(T, d, E, dt), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    L.router_topk_noisy(t(x), t(w_g), t(b_g), t(w_n), t(b_n), t(noise), eps, k, L.GATE_MODES[gate],
+                        idx, gte, colsum, lg, ws)
+    torch.cuda.synchronize()
+    return (idx.cpu().numpy(), gte.cpu().numpy().astype(np.float64), colsum.cpu().numpy().astype(np.float64),
+            lg.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_noisy_router_matches_oracle(name):
+    cfg, eps, bias = CASES[name]
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    say(f"noisy router {name}: T={T} d={d} E={E} k={k} x {cfg.act_dtype} gate {cfg.gate} eps={eps} bias_n={bias}")
+    x = W.gen_x(cfg)
+    w_g, b_g = W.gen_router(cfg)
+    w_n, b_n, noise = W.gen_noisy_gate(cfg, bias)
+    dt = L.F32 if cfg.act_dtype == "f32" else L.BF16
+    idx_g, gate_g, colsum_g, lg_g = _run(x, w_g, b_g, w_n, b_n, noise, eps, k, cfg.gate, T, d, E, dt)
+
+    f64 = lambda a: None if a is None else a.astype(np.float64)
+    z = O.noisy_router_logits(O.to_f64(x, cfg.act_dtype), f64(w_g), f64(b_g), f64(w_n), f64(b_n), f64(noise), eps)
+    tie, eg, ec = compare_router(name, z, k, cfg.gate, idx_g, gate_g, colsum_g)
+    zerr = float(np.max(np.abs(lg_g - z) / np.maximum(1.0, np.max(np.abs(z), axis=1, keepdims=True))))
+    assert zerr <= 1e-5, f"{name}: noisy logit err {zerr:.3e}"
+    # the noise decides: the clean router picks another set for many tokens
+    clean = O.topk_select(O.router_logits(O.to_f64(x, cfg.act_dtype), f64(w_g), f64(b_g)), k)
+    changed = int(np.sum(np.any(np.sort(clean, axis=1) != np.sort(idx_g, axis=1), axis=1)))
+    assert changed > 0
+    # same inputs, same draws: the same bits
+    again = _run(x, w_g, b_g, w_n, b_n, noise, eps, k, cfg.gate, T, d, E, dt)
+    for a, b in zip((idx_g, gate_g, colsum_g, lg_g), again):
+        np.testing.assert_array_equal(a, b)
+    say(f"  near-tied {int(tie.sum())}, tokens whose set the noise changed {changed}, "
+        f"gate err {eg:.2e}, colsum err {ec:.2e}, logit err {zerr:.2e}")
+
+
+def test_noisy_router_zero_tokens_writes_zero_column_sums():
+    cfg = W.MIXTRAL.scaled(name="t0", T=0, d=64, d_out=64, E=8, k=2)
+    say("noisy router T=0: only the column sums are written")
+    dev = "cuda"
+    w_g = torch.zeros((8, 64), dtype=torch.float32, device=dev)
+    colsum = torch.full((8,), -7.0, dtype=torch.float32, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev)
+    idx = torch.zeros((0, 2), dtype=torch.int32, device=dev)
+    g = torch.zeros((0, 2), dtype=torch.float32, device=dev)
+    noise = torch.zeros((0, 8), dtype=torch.float32, device=dev)
+    L.router_topk_noisy(x, w_g, None, w_g, None, noise, 1e-2, cfg.k, L.GATE_RENORM, idx, g, colsum, None, ws)
+    torch.cuda.synchronize()
+    assert torch.all(colsum.cpu() == 0)

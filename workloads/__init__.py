@@ -8,12 +8,14 @@ from .configs import (CANONICAL, CONFIGS, DEEPSEEK, MIXTRAL, STRESS, SWITCH,
                       SWITCH_DROP, TINY, MoEConfig, get_config, shrink)
 from .encode import (bf16_bits_to_f32, e4m3_scales, f32_to_bf16_bits,
                      f32_to_e4m3, quantize_rows_e4m3)
-from .gen import gen_expert, gen_experts, gen_router, gen_x, generate
+from .gen import (gen_expert, gen_experts, gen_noisy_gate, gen_router, gen_x,
+                  generate)
 
 __all__ = [
     "CANONICAL", "CONFIGS", "DEEPSEEK", "MIXTRAL", "STRESS", "SWITCH",
     "SWITCH_DROP", "TINY", "MoEConfig", "get_config", "shrink",
     "bf16_bits_to_f32", "e4m3_scales", "f32_to_bf16_bits", "f32_to_e4m3",
-    "quantize_rows_e4m3", "gen_expert", "gen_experts", "gen_router", "gen_x",
+    "quantize_rows_e4m3", "gen_expert", "gen_experts", "gen_noisy_gate",
+    "gen_router", "gen_x",
     "generate",
 ]

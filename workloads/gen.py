@@ -26,7 +26,8 @@ from .configs import MoEConfig
 from .encode import f32_to_bf16_bits, quantize_rows_e4m3
 
 _TAGS = {"x": 1, "w_g": 2, "b_g": 3, "w1": 4, "w3": 5, "w2": 6, "b1": 7,
-         "b2": 8, "sw1": 9, "sw3": 10, "sw2": 11, "sb1": 12, "sb2": 13}
+         "b2": 8, "sw1": 9, "sw3": 10, "sw2": 11, "sb1": 12, "sb2": 13,
+         "w_n": 14, "b_n": 15, "noise": 16}
 
 
 def _threads() -> int:
@@ -128,6 +129,18 @@ def gen_router(cfg: MoEConfig):
     if cfg.bg_var is not None:
         b_g = _draw(_rng(cfg.seed, "b_g"), (cfg.E,), ("normal", cfg.bg_var))
     return w_g, b_g
+
+
+def gen_noisy_gate(cfg: MoEConfig, bias: bool = True):
+    """Inputs of the noisy gate in training mode: the noise projection W_n
+    [E, d] and its bias b_n [E] (or None), both uniform in +-1/sqrt(d) as a
+    freshly initialised linear layer draws them, and the standard normal
+    draws noise [T, E], all float32."""
+    h = 1.0 / math.sqrt(cfg.d)
+    w_n = _draw(_rng(cfg.seed, "w_n"), (cfg.E, cfg.d), ("uniform", h))
+    b_n = _draw(_rng(cfg.seed, "b_n"), (cfg.E,), ("uniform", h)) if bias else None
+    noise = _draw(_rng(cfg.seed, "noise"), (cfg.T, cfg.E), ("normal", 1.0))
+    return w_n, b_n, noise
 
 
 def generate(cfg: MoEConfig, with_experts: bool = True) -> Dict[str, Optional[np.ndarray]]:
