@@ -363,15 +363,21 @@ __device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x
 // The W_g loads go out before the x loads and are split while x is in
 // flight: moving W_g from L2 costs more than the split.  The wavefronts'
 // partial logits are added in LDS in wavefront order; 8 lanes per token do
-// the fp32 softmax and top-k.
+// the fp32 softmax and top-k.  NOISY: the noise projection W_n goes through
+// the same steps into a second accumulator (one chunk per wavefront and
+// round, so that both fit in registers), and the noisy logit is formed
+// before the softmax.
 constexpr int kM8MaxE = 8;
 constexpr int kM8Cpw = 2;                     // chunks per wavefront and round
 constexpr int kM8Waves = 16;                  // at most, per block
 constexpr int kM8Tok = 16 * kM8Waves;         // at most, per block
 constexpr int kCUs = 256;                     // compute units of an MI355X
 
+template <bool NOISY>
 __global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a, int kw, int tg) {
-  __shared__ float part[kM8Waves][16][16];
+  constexpr int CPW = NOISY ? 1 : kM8Cpw;     // chunks per wavefront and round
+  constexpr int NM = NOISY ? 2 : 1;           // matrices: W_g (and W_n)
+  __shared__ float part[NM][kM8Waves][16][16];
   __shared__ float lg[kM8Tok][kM8MaxE];
   __shared__ float pr[kM8Tok][kM8MaxE];
   const int tid = threadIdx.x;
@@ -393,23 +399,29 @@ __global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a,
   // can wait for them one by one; W_g columns past d and rows past E are
   // zeroed after the load, rows of x past T only feed discarded logits
   const uint16_t* xr = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(tv ? t : a.T - 1) * a.d;
-  const float* wr = a.w_g + static_cast<size_t>(ev ? e : a.E - 1) * a.d;
-  f32x4_mf acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < a.d; c0 += 2 * kw * 128) {
-    float4 wb[kM8Cpw][4];                     // columns 0-3 (lanes < 8) or 4-7 of the lane's eight
-    uint4 xb[kM8Cpw][4];
-    bool ok[kM8Cpw][4];
+  const size_t wrow = static_cast<size_t>(ev ? e : a.E - 1) * a.d;
+  const float* wr[NM];
+  wr[0] = a.w_g + wrow;
+  if constexpr (NOISY) wr[NM - 1] = a.w_n + wrow;
+  f32x4_mf acc[NM];
 #pragma unroll
-    for (int i = 0; i < kM8Cpw; ++i)
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4_mf{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.d; c0 += CPW * kw * 128) {
+    float4 wb[NM][CPW][4];                    // columns 0-3 (lanes < 8) or 4-7 of the lane's eight
+    uint4 xb[CPW][4];
+    bool ok[CPW][4];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int col = c0 + (kv + i * kw) * 128 + s * 32 + kq;
         ok[i][s] = ev && col < a.d;           // d % 8 == 0: a lane's 8 columns are all in or all out
         const int cc = col < a.d ? col : a.d - 8;
-        wb[i][s] = *reinterpret_cast<const float4*>(wr + cc + (hl ? 0 : 4));
+#pragma unroll
+        for (int m = 0; m < NM; ++m) wb[m][i][s] = *reinterpret_cast<const float4*>(wr[m] + cc + (hl ? 0 : 4));
       }
 #pragma unroll
-    for (int i = 0; i < kM8Cpw; ++i)
+    for (int i = 0; i < CPW; ++i)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int col = c0 + (kv + i * kw) * 128 + s * 32 + kq;
@@ -417,39 +429,46 @@ __global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a,
       }
     // every load of the round is in flight before the first use
     __builtin_amdgcn_sched_barrier(0);
-    uint4 b1[kM8Cpw][4], b2[kM8Cpw][4];
+    uint4 b1[NM][CPW][4], b2[NM][CPW][4];
 #pragma unroll
-    for (int i = 0; i < kM8Cpw; ++i)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        // lanes n and n + 8 hold the two halves of the same eight W_g values
-        const float4 mine = wb[i][s];
-        const float4 other = make_float4(dpp_swap8(mine.x), dpp_swap8(mine.y), dpp_swap8(mine.z), dpp_swap8(mine.w));
-        bf16x8_t hi, mid, lo;
-        split3(hl ? mine : other, hl ? other : mine, hi, mid, lo);
-        const uint4 h = __builtin_bit_cast(uint4, hi), m = __builtin_bit_cast(uint4, mid),
-                    l = __builtin_bit_cast(uint4, lo);
-        // a mask rather than a select of the loaded values, which the
-        // compiler would turn into a conditional load waited for at once
-        const uint32_t m1 = ok[i][s] ? ~0u : 0u, m2 = (ok[i][s] && hl) ? ~0u : 0u;
-        b1[i][s] = hl ? h : m;
-        b1[i][s].x &= m1; b1[i][s].y &= m1; b1[i][s].z &= m1; b1[i][s].w &= m1;
-        b2[i][s] = make_uint4(l.x & m2, l.y & m2, l.z & m2, l.w & m2);
-      }
+      for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          // lanes n and n + 8 hold the two halves of the same eight W_g values
+          const float4 mine = wb[m][i][s];
+          const float4 other = make_float4(dpp_swap8(mine.x), dpp_swap8(mine.y), dpp_swap8(mine.z), dpp_swap8(mine.w));
+          bf16x8_t hi, mid, lo;
+          split3(hl ? mine : other, hl ? other : mine, hi, mid, lo);
+          const uint4 h = __builtin_bit_cast(uint4, hi), mm = __builtin_bit_cast(uint4, mid),
+                      l = __builtin_bit_cast(uint4, lo);
+          // a mask rather than a select of the loaded values, which the
+          // compiler would turn into a conditional load waited for at once
+          const uint32_t m1 = ok[i][s] ? ~0u : 0u, m2 = (ok[i][s] && hl) ? ~0u : 0u;
+          b1[m][i][s] = hl ? h : mm;
+          b1[m][i][s].x &= m1; b1[m][i][s].y &= m1; b1[m][i][s].z &= m1; b1[m][i][s].w &= m1;
+          b2[m][i][s] = make_uint4(l.x & m2, l.y & m2, l.z & m2, l.w & m2);
+        }
     // the planes are ready before the first wait for x
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kM8Cpw; ++i)
+    for (int i = 0; i < CPW; ++i)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8_t xv = __builtin_bit_cast(bf16x8_t, xb[i][s]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8_t, b1[i][s]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8_t, b2[i][s]), acc, 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8_t, b1[m][i][s]), acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8_t, b2[m][i][s]), acc[m], 0, 0, 0);
+        }
       }
   }
   // lane holds column r16 of tokens 4 (lane / 16) + q of its group
 #pragma unroll
-  for (int q = 0; q < 4; ++q) part[wave][(lane >> 4) * 4 + q][r16] = acc[q];
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part[m][wave][(lane >> 4) * 4 + q][r16] = acc[m][q];
   __syncthreads();
   for (int j = tid; j < tpb * kM8MaxE; j += nthr) {
     const int tl = j / kM8MaxE, ee = j % kM8MaxE;
@@ -457,10 +476,20 @@ __global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a,
     if (ee < a.E) {
       const int gg = tl / 16, tr = tl % 16;
       for (int w = 0; w < kw; ++w) {
-        const float* pp = part[gg * kw + w][tr];
+        const float* pp = part[0][gg * kw + w][tr];
         z += pp[ee] + pp[ee + 8];
       }
       if (a.b_g) z += a.b_g[ee];
+      if constexpr (NOISY) {
+        float zn = 0.f;
+        for (int w = 0; w < kw; ++w) {
+          const float* pp = part[NM - 1][gg * kw + w][tr];
+          zn += pp[ee] + pp[ee + 8];
+        }
+        if (a.b_n) zn += a.b_n[ee];
+        const int t = t0 + tl;
+        if (t < a.T) z += a.noise[static_cast<size_t>(t) * a.E + ee] * (softplus_f(zn) + a.eps);
+      }
     }
     lg[tl][ee] = z;
   }
@@ -612,13 +641,19 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
 // probability column sums (wavefronts added in order) to the workspace.
 // NOISY: the partial rows hold 2 E logits per token, the clean ones then the
 // noise projection's; the noisy logit is clean + b_g + draw * (softplus(
-// projection + b_n) + eps).
+// projection + b_n) + eps).  PER: logits per thread, 16 E / 512 rounded up
+// to a power of two.  Every load of a group of four slices, and the bias and
+// draws, is in flight before the first wait: at one block per CU the kernel
+// is a chain of memory round trips otherwise.
 constexpr int kFnTok = 16;                    // tokens per block
 constexpr int kFnWaves = 8;
+constexpr int kFnThreads = 64 * kFnWaves;
+constexpr int kFnGroup = 4;                   // slices per round of loads
 
-template <bool NOISY>
-__global__ __launch_bounds__(64 * kFnWaves) void router_finish_kernel(RouterArgs a, const float* __restrict__ part,
-                                                                       int nslice) {
+template <bool NOISY, int PER>
+__global__ __launch_bounds__(kFnThreads) void router_finish_kernel(RouterArgs a, const float* __restrict__ part,
+                                                                    int nslice) {
+  // launch_finish picks PER with PER * kFnThreads >= kFnTok * E
   __shared__ float lg[kFnTok * kRtMaxE];
   __shared__ float wcol[kFnWaves * kRtMaxE];
   const int tid = threadIdx.x;
@@ -626,47 +661,69 @@ __global__ __launch_bounds__(64 * kFnWaves) void router_finish_kernel(RouterArgs
   const int wave = tid >> 6;
   const int t0 = blockIdx.x * kFnTok;
   for (int e = lane; e < a.E; e += 64) wcol[wave * a.E + e] = 0.f;
-  // the block's logits first (all loads in flight together), then one
-  // wavefront per token
-  constexpr int kPer = kFnTok * kRtMaxE / (64 * kFnWaves);   // entries per thread at most
   const int n_ent = min(kFnTok, a.T - t0) * a.E;             // the block's tokens are contiguous
   const int PE = NOISY ? 2 * a.E : a.E;                      // partial logits per token
   const float* src = part + static_cast<size_t>(t0) * PE;
-  float z[kPer], zn[kPer];
-  int off[kPer];
+  // unconditional loads (clamped index); entries past the block's tokens
+  // are not stored
+  int jj[PER], off[PER];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    // unconditional loads (clamped index) so that they are all in flight at
-    // once; entries past the block's tokens are not stored
-    const int j = min(tid + 64 * kFnWaves * u, n_ent - 1);
-    off[u] = NOISY ? (j / a.E) * PE + j % a.E : j;
-    z[u] = 0.f;
-    zn[u] = 0.f;
+  for (int u = 0; u < PER; ++u) {
+    jj[u] = min(tid + kFnThreads * u, n_ent - 1);
+    off[u] = NOISY ? (jj[u] / a.E) * PE + jj[u] % a.E : jj[u];
   }
-  for (int sl = 0; sl < nslice; ++sl) {
-    const float* ps = src + static_cast<size_t>(sl) * a.T * PE;
+  float bg[PER], dr[PER], bn[PER];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      z[u] += ps[off[u]];
-      if constexpr (NOISY) zn[u] += ps[off[u] + a.E];
-    }
+  for (int u = 0; u < PER; ++u) {
+    bg[u] = 0.f;
+    dr[u] = 0.f;
+    bn[u] = 0.f;
   }
   if (a.b_g) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) z[u] += a.b_g[min(tid + 64 * kFnWaves * u, n_ent - 1) % a.E];
+    for (int u = 0; u < PER; ++u) bg[u] = a.b_g[jj[u] % a.E];
   }
   if constexpr (NOISY) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int j = min(tid + 64 * kFnWaves * u, n_ent - 1);
-      float v = zn[u];
-      if (a.b_n) v += a.b_n[j % a.E];
-      z[u] += a.noise[static_cast<size_t>(t0) * a.E + j] * (softplus_f(v) + a.eps);
+    for (int u = 0; u < PER; ++u) dr[u] = a.noise[static_cast<size_t>(t0) * a.E + jj[u]];
+    if (a.b_n) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) bn[u] = a.b_n[jj[u] % a.E];
+    }
+  }
+  float z[PER], zn[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    z[u] = 0.f;
+    zn[u] = 0.f;
+  }
+  for (int s0 = 0; s0 < nslice; s0 += kFnGroup) {
+    float v[kFnGroup][PER], vn[kFnGroup][PER];
+#pragma unroll
+    for (int q = 0; q < kFnGroup; ++q) {
+      const float* ps = src + static_cast<size_t>(min(s0 + q, nslice - 1)) * a.T * PE;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        v[q][u] = ps[off[u]];
+        if constexpr (NOISY) vn[q][u] = ps[off[u] + a.E];
+      }
+    }
+    // slices past the last are added as 0 * v (the partials are finite)
+#pragma unroll
+    for (int q = 0; q < kFnGroup; ++q) {
+      const float m = s0 + q < nslice ? 1.f : 0.f;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        z[u] += m * v[q][u];
+        if constexpr (NOISY) zn[u] += m * vn[q][u];
+      }
     }
   }
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int j = tid + 64 * kFnWaves * u;
+  for (int u = 0; u < PER; ++u) {
+    z[u] += bg[u];
+    if constexpr (NOISY) z[u] += dr[u] * (softplus_f(zn[u] + bn[u]) + a.eps);
+    const int j = tid + kFnThreads * u;
     if (j < n_ent) lg[j] = z[u];
   }
   __syncthreads();
@@ -676,12 +733,26 @@ __global__ __launch_bounds__(64 * kFnWaves) void router_finish_kernel(RouterArgs
     token_softmax_topk(lg + tl * a.E, t, a, wcol + wave * a.E, lane);
   }
   __syncthreads();
-  for (int e = tid; e < a.E; e += 64 * kFnWaves) {
+  for (int e = tid; e < a.E; e += kFnThreads) {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kFnWaves; ++w) v += wcol[w * a.E + e];
     a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + e] = v;
   }
+}
+
+// finishing kernel for E experts: logits per thread as a template argument
+template <bool NOISY>
+void launch_finish(const RouterArgs& a, const float* part, int nslice, int nb, hipStream_t stream) {
+  const dim3 grid(nb), block(kFnThreads);
+  if (a.E <= 32)
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 1>), grid, block, 0, stream, a, part, nslice);
+  else if (a.E <= 64)
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 2>), grid, block, 0, stream, a, part, nslice);
+  else if (a.E <= 128)
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 4>), grid, block, 0, stream, a, part, nslice);
+  else
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 8>), grid, block, 0, stream, a, part, nslice);
 }
 
 // prob_colsum[e] = sum over blocks of the partial sums.  One block per
@@ -712,13 +783,13 @@ inline int router_max_blocks(int T) {
 }
 
 
-// wavefronts per token group (two 128-column chunks each per round) and token
-// groups per block of router_mf8_kernel: whole rows in one round up to 4096
-// columns; more tokens per block for narrow rows while the grid keeps at
-// least one block per CU
-inline void mf8_shape(int T, int d, int& kw, int& tg) {
+// wavefronts per token group (cpw 128-column chunks each per round) and token
+// groups per block of router_mf8_kernel: whole rows in one round up to
+// 16 cpw chunks; more tokens per block for narrow rows while the grid keeps
+// at least one block per CU
+inline void mf8_shape(int T, int d, int cpw, int& kw, int& tg) {
   const int nch = (d + 127) / 128;
-  kw = (nch + kM8Cpw - 1) / kM8Cpw;
+  kw = (nch + cpw - 1) / cpw;
   if (kw > kM8Waves) kw = kM8Waves;
   tg = T / (16 * kCUs);
   if (tg > kM8Waves / kw) tg = kM8Waves / kw;
@@ -741,22 +812,25 @@ inline size_t logit_ws_offset(int T, int E) {
 }
 
 // the launches of both entry points; arguments already validated.  noise ==
-// nullptr: the clean router.  bf16: MFMA kernels (clean with up to 8
-// experts: whole rows per block, one launch; otherwise the tiled logits GEMM,
-// then the finishing kernel); fp32 activations: the generic kernel.
+// nullptr: the clean router.  bf16: MFMA kernels (up to 8 experts: whole
+// rows per block, one launch; otherwise the tiled logits GEMM, then the
+// finishing kernel); fp32 activations: the generic kernel.
 int router_run(const void* x, int x_dt, const float* w_g, const float* b_g, const float* w_n, const float* b_n,
                const float* noise, float eps, int T, int d, int E, int k, int gate_mode, int32_t* topk_idx,
                float* topk_gate, float* prob_colsum, float* logits_dbg, void* workspace, hipStream_t stream) {
   const bool noisy = noise != nullptr;
-  const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE && !noisy;
+  const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE;
   const bool mf = x_dt == MOE_BF16 && !m8;
   float* part = static_cast<float*>(workspace);
   int kw8 = 1, tg8 = 1;
-  mf8_shape(T, d, kw8, tg8);
+  mf8_shape(T, d, noisy ? 1 : kM8Cpw, kw8, tg8);
   const int nb = m8 ? (T + 16 * tg8 - 1) / (16 * tg8) : (mf ? (T + kFnTok - 1) / kFnTok : router_blocks(T));
   RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg, w_n, b_n, noise, eps};
   if (T > 0 && m8) {
-    hipLaunchKernelGGL(router_mf8_kernel, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
+    if (noisy)
+      hipLaunchKernelGGL(router_mf8_kernel<true>, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
+    else
+      hipLaunchKernelGGL(router_mf8_kernel<false>, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
     int st = check_launch();
     if (st != MOE_OK) return st;
   }
@@ -777,11 +851,9 @@ int router_run(const void* x, int x_dt, const float* w_g, const float* b_g, cons
     int st = check_launch();
     if (st != MOE_OK) return st;
     if (noisy)
-      hipLaunchKernelGGL(router_finish_kernel<true>, dim3(nb), dim3(64 * kFnWaves), 0, stream, a,
-                         static_cast<const float*>(lgp), ks);
+      launch_finish<true>(a, lgp, ks, nb, stream);
     else
-      hipLaunchKernelGGL(router_finish_kernel<false>, dim3(nb), dim3(64 * kFnWaves), 0, stream, a,
-                         static_cast<const float*>(lgp), ks);
+      launch_finish<false>(a, lgp, ks, nb, stream);
     st = check_launch();
     if (st != MOE_OK) return st;
   }

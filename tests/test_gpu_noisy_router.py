@@ -41,7 +41,12 @@ CASES = {
     # bf16 split over K slices with a partial last chunk
     "bf16_kslices": (W.MIXTRAL.scaled(name="bf16_kslices", T=300, d=1544, d_out=1544, E=70, k=5, gate="prob",
                                       wg_dist=("normal", 1.0 / 1544), seed=24), 1e-2, False),
-    # bf16 with 128-token blocks (T >= 8192), narrow rows
+    # bf16, at most 8 experts (the single-launch MFMA router with a second
+    # accumulator): seven experts, rows over several rounds of chunks with a
+    # last chunk of 8 columns, router bias
+    "bf16_e7_wide": (W.MIXTRAL.scaled(name="bf16_e7_wide", T=300, d=4360, d_out=16, E=7, k=3, gate="prob",
+                                      wg_dist=("normal", 1.0 / 4360), bg_var=0.5, seed=26), 1e-2, True),
+    # bf16, at most 8 experts, several token groups per block (narrow rows)
     "bf16_bm128": (W.MIXTRAL.scaled(name="bf16_bm128", T=8200, d=64, d_out=64, E=8, k=2,
                                     wg_dist=("normal", 1.0 / 64), seed=25), 1e-2, True),
 }
