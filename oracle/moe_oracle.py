@@ -12,8 +12,8 @@ Sources (web pages on the method; cited by page and section):
   P4  "混合专家 MOE 是什么" (dgblog.top)
   P5  "MoE 混合专家模型串讲：从 Switch Transformer 到 DeepSeekMoE" (uestc.de5.net)
 
-Every step is written the plain way, in float64, with numpy matmul as the
-only library primitive.  Readings taken where the pages are silent or
+Every step is written the plain way, in float64, with numpy matmul (and
+scipy's erf for GELU) as the only library primitives.  Readings taken where the pages are silent or
 disagree are listed next to the function that takes them.
 
 Parity status: every function here is pinned by a CPU test (worked example,
@@ -26,6 +26,7 @@ import math
 from typing import Dict, Optional
 
 import numpy as np
+import scipy.special
 
 # ---------------------------------------------------------------------------
 # stored-value decoding
@@ -290,6 +291,14 @@ def silu(u: np.ndarray) -> np.ndarray:
     return u / (1.0 + np.exp(-u))
 
 
+def gelu(u: np.ndarray) -> np.ndarray:
+    """GELU in its exact form u * Phi(u) = u/2 * (1 + erf(u / sqrt 2)): the
+    experts of P1 §3.2 and P3 §3.1 use torch's nn.GELU, whose default is this
+    form (not the tanh approximation)."""
+    u = np.asarray(u, np.float64)
+    return 0.5 * u * (1.0 + scipy.special.erf(u / math.sqrt(2.0)))
+
+
 def expert_ffn(kind: str, rows: np.ndarray, w1: np.ndarray, w3: Optional[np.ndarray] = None,
                w2: Optional[np.ndarray] = None, b1: Optional[np.ndarray] = None,
                b2: Optional[np.ndarray] = None) -> np.ndarray:
@@ -301,6 +310,8 @@ def expert_ffn(kind: str, rows: np.ndarray, w1: np.ndarray, w3: Optional[np.ndar
               workload).
     'swiglu': W2 (silu(W1 x) * (W3 x)) (not on the pages; the standard
               gated-linear form is the reading taken).
+    'gelu'  : W2 gelu(W1 x + b1) + b2, the two-layer FFN of P1 §3.2 and
+              P3 §3.1 with their GELU activation.
     Weights are [out, in]; rows are [n, in].
     """
     rows = np.asarray(rows, np.float64)
@@ -311,6 +322,8 @@ def expert_ffn(kind: str, rows: np.ndarray, w1: np.ndarray, w3: Optional[np.ndar
         return h
     if kind == "relu":
         h = np.maximum(h, 0.0)
+    elif kind == "gelu":
+        h = gelu(h)
     elif kind == "swiglu":
         h = silu(h) * (rows @ w3.T)
     else:

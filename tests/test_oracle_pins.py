@@ -274,7 +274,7 @@ def test_expert_ffn_matches_torch_functional():
     assert np.allclose(O.silu(u), F.silu(torch.from_numpy(u)).numpy(), rtol=1e-13)
 
 
-@pytest.mark.parametrize("kind", ["linear", "relu", "swiglu"])
+@pytest.mark.parametrize("kind", ["linear", "relu", "swiglu", "gelu"])
 @pytest.mark.parametrize("mode", ["renorm", "prob"])
 def test_dense_equals_sparse_at_k_equal_E(kind, mode):
     """P4 稠密 vs 稀疏: the sparse layer only adds a top-k step."""
@@ -562,3 +562,38 @@ def test_noisy_top1_matches_page_gate_module_written_in_torch():
     np.testing.assert_allclose(r["topk_gate"][:, 0], route.sum(dim=-1).numpy(), rtol=1e-12)
     counts = np.bincount(r["topk_idx"][:, 0], minlength=E)
     np.testing.assert_allclose(O.aux_loss(counts, r["prob_colsum"], T, 1, E, 1.0), aux.item(), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# GELU experts (P1 §3.2 and P3 §3.1: nn.GELU, exact form)
+# ---------------------------------------------------------------------------
+
+
+def test_gelu_closed_forms():
+    # u * Phi(u): Phi(0) = 1/2, Phi(1) = 0.8413447460685429 (normal table),
+    # Phi(-u) = 1 - Phi(u) gives gelu(u) - gelu(-u) = u
+    assert O.gelu(0.0) == 0.0
+    assert O.gelu(1.0) == pytest.approx(0.8413447460685429, rel=1e-14)
+    assert O.gelu(-1.0) == pytest.approx(-(1.0 - 0.8413447460685429), rel=1e-13)
+    assert O.gelu(2.0) == pytest.approx(2.0 * 0.9772498680518208, rel=1e-14)
+    u = np.linspace(-9.0, 9.0, 721)
+    np.testing.assert_allclose(O.gelu(u) - O.gelu(-u), u, atol=1e-14)
+    assert O.gelu(40.0) == 40.0 and O.gelu(-40.0) == pytest.approx(0.0, abs=1e-300)
+    # the tanh approximation differs from the exact form by ~1.5e-4 at u = 1
+    tanh_form = 0.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * (1 + 0.044715)))
+    assert abs(O.gelu(1.0) - tanh_form) > 1e-4
+
+
+def test_gelu_expert_matches_torch_functional():
+    rng = np.random.default_rng(30)
+    d, f, o = 7, 12, 5
+    x = rng.standard_normal((9, d)) * 2
+    w = _rand_weights(rng, "relu", 1, d, f, o, bias=True)
+    F = torch.nn.functional
+    tx = torch.from_numpy(x)
+    h = F.gelu(F.linear(tx, torch.from_numpy(w["w1"][0]), torch.from_numpy(w["b1"][0])))
+    ref = F.linear(h, torch.from_numpy(w["w2"][0]), torch.from_numpy(w["b2"][0])).numpy()
+    got = O.expert_ffn("gelu", x, w["w1"][0], None, w["w2"][0], w["b1"][0], w["b2"][0])
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    u = rng.standard_normal(200) * 5
+    np.testing.assert_allclose(O.gelu(u), F.gelu(torch.from_numpy(u)).numpy(), rtol=1e-13, atol=1e-300)
