@@ -37,7 +37,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_traffic_mixtral.json")
 def ffn_flops_per_row(cfg) -> float:
     if cfg.ffn == "linear":
         return 2.0 * cfg.d * cfg.d_out
-    if cfg.ffn == "relu":
+    if cfg.ffn in ("relu", "gelu"):
         return 2.0 * cfg.d * cfg.d_ff + 2.0 * cfg.d_ff * cfg.d_out
     return 4.0 * cfg.d * cfg.d_ff + 2.0 * cfg.d_ff * cfg.d_out
 

@@ -65,8 +65,10 @@ typedef enum {
 
 typedef enum {
   MOE_FFN_LINEAR = 0,        /* y = A x + b                         (P4 公式：三步走, step two) */
-  MOE_FFN_RELU = 1,          /* y = W2 relu(W1 x + b1) + b2         (P1 §3.2, P3 §3.1 two-layer expert) */
-  MOE_FFN_SWIGLU = 2         /* y = W2 (silu(W1 x) * (W3 x))        (not on the pages; standard gated form) */
+  MOE_FFN_RELU = 1,          /* y = W2 relu(W1 x + b1) + b2         (P1 §3.2, P3 §3.1 two-layer expert, with ReLU) */
+  MOE_FFN_SWIGLU = 2,        /* y = W2 (silu(W1 x) * (W3 x))        (not on the pages; standard gated form) */
+  MOE_FFN_GELU = 3           /* y = W2 gelu(W1 x + b1) + b2         (P1 §3.2 and P3 §3.1 experts: nn.GELU,
+                                gelu(u) = u/2 (1 + erf(u/sqrt 2)), the exact form) */
 } moe_ffn_kind;
 
 typedef enum {
@@ -204,7 +206,7 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
  *             offsets[E] <= max_rows
  *   w1        [E, d_ff, d]  (LINEAR: [E, d_out, d])
  *   w3        [E, d_ff, d]  SWIGLU only (up projection), else NULL
- *   w2        [E, d_out, d_ff]  RELU / SWIGLU, else NULL
+ *   w2        [E, d_out, d_ff]  RELU / SWIGLU / GELU, else NULL
  *   w_dt      MOE_F32 (needs act_dt MOE_F32), MOE_BF16 or MOE_FP8_E4M3
  *             (both need act_dt MOE_BF16)
  *   s1,s3,s2  fp32 per-output-row scales for fp8 weights ([E, rows]), else NULL;
@@ -217,7 +219,7 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
  * to bf16 between the two matrix products.
  * Constraints: E <= 1024; with bf16 activations d and d_ff multiples of 8
  * (16 for fp8 weights); no biases with SWIGLU (else MOE_ERR_UNSUPPORTED).
- * w3 must be given exactly for SWIGLU, w2 exactly for RELU / SWIGLU, the
+ * w3 must be given exactly for SWIGLU, w2 exactly for RELU / SWIGLU / GELU, the
  * scales exactly for fp8 weights, no b2 for LINEAR (else
  * MOE_ERR_INVALID_ARG).  max_rows == 0 returns MOE_OK without launching.
  * Products with K % 128 == 0 go through the LDS-DMA kernel, others through

@@ -21,7 +21,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 # moe_gate_mode
 GATE_PROB, GATE_RENORM = 0, 1
 # moe_ffn_kind
-FFN_LINEAR, FFN_RELU, FFN_SWIGLU = 0, 1, 2
+FFN_LINEAR, FFN_RELU, FFN_SWIGLU, FFN_GELU = 0, 1, 2, 3
 # moe_cap_round
 CAP_CEIL, CAP_FLOOR = 0, 1
 # moe_row_mode
@@ -30,7 +30,7 @@ ROWS_PACKED, ROWS_SHARED = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4
 
 GATE_MODES = {"prob": GATE_PROB, "renorm": GATE_RENORM}
-FFN_KINDS = {"linear": FFN_LINEAR, "relu": FFN_RELU, "swiglu": FFN_SWIGLU}
+FFN_KINDS = {"linear": FFN_LINEAR, "relu": FFN_RELU, "swiglu": FFN_SWIGLU, "gelu": FFN_GELU}
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int

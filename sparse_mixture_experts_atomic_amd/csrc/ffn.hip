@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
     }
     if (bias) acc += bias[static_cast<size_t>(e) * N + n];
     float v = acc;
-    if (EPI == EPI_RELU) v = fmaxf(acc, 0.f);
+    v = act1<EPI>(acc);
     if (EPI == EPI_SWIGLU) v = silu_f32(acc) * acc3;
     out[static_cast<size_t>(a) * N + n] = v;
   }
@@ -115,7 +115,7 @@ size_t moe_ffn_workspace_size(int kind, int act_dt, int max_rows, int E, int d, 
   if (max_rows < 0 || E < 1) return 0;
   size_t s = align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), kWsAlign);
   if (act_dt == MOE_BF16) s += align_up(gemm_partial_bytes(current_cu_count()), kWsAlign);
-  if (kind == MOE_FFN_RELU || kind == MOE_FFN_SWIGLU) {
+  if (kind == MOE_FFN_RELU || kind == MOE_FFN_SWIGLU || kind == MOE_FFN_GELU) {
     const size_t esz = act_dt == MOE_F32 ? 4 : 2;
     s += align_up(static_cast<size_t>(max_rows) * static_cast<size_t>(d_ff > 0 ? d_ff : 0) * esz, kWsAlign);
   }
@@ -127,7 +127,8 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
                            const void* w3, const void* w2, int w_dt, const float* s1, const float* s3,
                            const float* s2, const float* b1, const float* b2, void* y_rows, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-  if (kind != MOE_FFN_LINEAR && kind != MOE_FFN_RELU && kind != MOE_FFN_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (kind != MOE_FFN_LINEAR && kind != MOE_FFN_RELU && kind != MOE_FFN_SWIGLU && kind != MOE_FFN_GELU)
+    return MOE_ERR_INVALID_ARG;
   if (act_dt != MOE_F32 && act_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (w_dt != MOE_F32 && w_dt != MOE_BF16 && w_dt != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (row_mode != MOE_ROWS_PACKED && row_mode != MOE_ROWS_SHARED) return MOE_ERR_INVALID_ARG;
@@ -178,11 +179,13 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
       return launch_f32<EPI_PLAIN>(X, shared_in, offsets, E, d, d_out, static_cast<const float*>(w1), nullptr, b1, Y,
                                    max_rows, stream);
     float* Hf = static_cast<float*>(H);
+    const float* W1 = static_cast<const float*>(w1);
     int st = kind == MOE_FFN_RELU
-                 ? launch_f32<EPI_RELU>(X, shared_in, offsets, E, d, d_ff, static_cast<const float*>(w1), nullptr, b1,
-                                        Hf, max_rows, stream)
-                 : launch_f32<EPI_SWIGLU>(X, shared_in, offsets, E, d, d_ff, static_cast<const float*>(w1),
-                                          static_cast<const float*>(w3), nullptr, Hf, max_rows, stream);
+                 ? launch_f32<EPI_RELU>(X, shared_in, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
+             : kind == MOE_FFN_GELU
+                 ? launch_f32<EPI_GELU>(X, shared_in, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
+                 : launch_f32<EPI_SWIGLU>(X, shared_in, offsets, E, d, d_ff, W1, static_cast<const float*>(w3), nullptr,
+                                          Hf, max_rows, stream);
     if (st != MOE_OK) return st;
     return launch_f32<EPI_PLAIN>(Hf, 0, offsets, E, d_ff, d_out, static_cast<const float*>(w2), nullptr, b2, Y,
                                  max_rows, stream);
@@ -210,7 +213,10 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
   p1.partial = partial;
   p1.n_cu = n_cu;
   p1.split_max = kGemmSplitMax;
-  const int epi1 = kind == MOE_FFN_SWIGLU ? EPI_SWIGLU : (kind == MOE_FFN_RELU ? EPI_RELU : EPI_PLAIN);
+  const int epi1 = kind == MOE_FFN_SWIGLU ? EPI_SWIGLU
+                   : kind == MOE_FFN_RELU ? EPI_RELU
+                   : kind == MOE_FFN_GELU ? EPI_GELU
+                                          : EPI_PLAIN;
   st = launch_grouped_gemm(epi1, fp8, p1, max_rows, mtm, stream);
   if (st != MOE_OK || !two) return st;
 

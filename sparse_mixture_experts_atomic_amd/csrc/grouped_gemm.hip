@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
           const int lr = wm * WM + i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
           if (lr < rows_valid) {
             float v = acc[i][j][q] * s + bias;
-            if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+            v = act1<EPI>(v);
             C[static_cast<size_t>(row0 + lr) * N + col] = f32_to_bf16(v);
           }
         }
@@ -513,7 +513,7 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
             v[h] = silu_fast(acc[i][j][q + h] * sg) * (acc[i][j + 2][q + h] * su);
           } else {
             v[h] = acc[i][j][q + h] * sg + bias;
-            if (EPI == EPI_RELU) v[h] = fmaxf(v[h], 0.f);
+            v[h] = act1<EPI>(v[h]);
           }
         }
         const uint32_t pk = pack_bf16x2(v[0], v[1]);
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
         v = silu_fast(acc[jj][q] * sg) * (acc[jj + 2][q] * su);
       } else {
         v = acc[jj][q] * sg + bias;
-        if (EPI == EPI_RELU) v = fmaxf(v, 0.f);
+        v = act1<EPI>(v);
       }
       ep[lr * kEpPitch + lc] = f32_to_bf16(v);
     }
@@ -1125,10 +1125,12 @@ int launch_epi(int epi, bool fp8, const GemmParams& p, int m_tiles_max, hipStrea
   if (fp8) {
     if (epi == EPI_SWIGLU) return launch<BM, BN, NH, EPI_SWIGLU, true>(p, m_tiles_max, stream);
     if (epi == EPI_RELU) return launch<BM, BN, NH, EPI_RELU, true>(p, m_tiles_max, stream);
+    if (epi == EPI_GELU) return launch<BM, BN, NH, EPI_GELU, true>(p, m_tiles_max, stream);
     return launch<BM, BN, NH, EPI_PLAIN, true>(p, m_tiles_max, stream);
   }
   if (epi == EPI_SWIGLU) return launch<BM, BN, NH, EPI_SWIGLU, false>(p, m_tiles_max, stream);
   if (epi == EPI_RELU) return launch<BM, BN, NH, EPI_RELU, false>(p, m_tiles_max, stream);
+  if (epi == EPI_GELU) return launch<BM, BN, NH, EPI_GELU, false>(p, m_tiles_max, stream);
   return launch<BM, BN, NH, EPI_PLAIN, false>(p, m_tiles_max, stream);
 }
 
@@ -1148,11 +1150,13 @@ int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, in
   if (dma_ok && fp8) {
     if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK, true>(p, m_tiles_max, stream);
     if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK, true>(p, m_tiles_max, stream);
+    if (epi == EPI_GELU) return launch_dma<EPI_GELU, kDmaBK, true>(p, m_tiles_max, stream);
     return launch_dma<EPI_PLAIN, kDmaBK, true>(p, m_tiles_max, stream);
   }
   if (dma_ok) {
     if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK, false>(p, m_tiles_max, stream);
     if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK, false>(p, m_tiles_max, stream);
+    if (epi == EPI_GELU) return launch_dma<EPI_GELU, kDmaBK, false>(p, m_tiles_max, stream);
     return launch_dma<EPI_PLAIN, kDmaBK, false>(p, m_tiles_max, stream);
   }
   return launch_epi<kGemmBM, 128, 1>(epi, fp8, p, m_tiles_max, stream);

@@ -79,7 +79,33 @@ __device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + expf(-u)
 
 // ------------------------------------------------- grouped GEMM interface
 
-enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_GELU = 3 };
+
+// GELU in its exact form, u * Phi(u) = u / 2 * (1 + erf(u / sqrt 2)), with
+// erfc(x), x >= 0, from Abramowitz and Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26: t = 1 / (1 + p x), erfc(x) = (a1 t + a2 t^2 +
+// a3 t^3 + a4 t^4 + a5 t^5) e^(-x^2), absolute error below 1.5e-7 (well under
+// the bf16 rounding of the result, and under fp32 tolerances).  Branch-free:
+// one reciprocal, one exp2 and five FMAs, where the library erf branches per
+// element and, unrolled over an epilogue's 128 values per lane, spills.
+__device__ __forceinline__ float gelu_f32(float u) {
+  const float x = fabsf(u) * 0.70710678118654752f;              // |u| / sqrt 2
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  const float y = q * t * __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);   // erfc(x)
+  return 0.5f * u * (u >= 0.f ? 2.0f - y : y);
+}
+
+// activation of a non-gated first layer (identity for EPI_PLAIN)
+template <int EPI>
+__device__ __forceinline__ float act1(float v) {
+  if constexpr (EPI == EPI_RELU) return fmaxf(v, 0.f);
+  if constexpr (EPI == EPI_GELU) return gelu_f32(v);
+  return v;
+}
 
 constexpr int kGemmBM = 256;   // rows per m-tile of the grouped GEMM
 

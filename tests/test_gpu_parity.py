@@ -90,6 +90,16 @@ EDGE = {
                               b1_var=0.1, b2_var=0.1, seed=35),
     "fp8_dma_linear": _cfg("fp8_dma_linear", T=260, d=384, d_out=200, E=5, k=2, ffn="linear", d_ff=0, gate="prob",
                            w_dtype="fp8", wg_dist=("normal", 1 / 384), w1_var=1 / 384, seed=36),
+    # GELU experts with biases: on the register-staged GEMM (K off the
+    # 128-column grid, N off the tiles), on the LDS-DMA GEMM with e4m3
+    # weights, and the from-scratch page's own model shape in bf16 (DMA GEMM)
+    "gelu_bias_tails": _cfg("gelu_bias_tails", T=257, d=136, d_out=72, E=5, k=2, ffn="gelu", d_ff=200,
+                            gate="renorm", wg_dist=("normal", 1 / 136), w1_var=1 / 136, w2_var=1 / 200,
+                            b1_var=0.1, b2_var=0.1, seed=40),
+    "fp8_dma_gelu_bias": _cfg("fp8_dma_gelu_bias", T=300, d=256, E=6, k=2, ffn="gelu", d_ff=384, gate="prob",
+                              w_dtype="fp8", wg_dist=("normal", 1 / 256), w1_var=1 / 256, w2_var=1 / 384,
+                              b1_var=0.1, b2_var=0.1, seed=41),
+    "p1_gelu_bf16": W.P1_GELU.scaled(name="p1_gelu_bf16", act_dtype="bf16", w_dtype="bf16", seed=42),
     # E <= 8 MFMA router: rows wider than one round of chunks, with a last
     # chunk of 8 columns; seven experts, router bias
     "router_e8_wide": _cfg("router_e8_wide", T=300, d=4360, d_out=16, E=7, k=3, ffn="linear", d_ff=0,
@@ -221,6 +231,20 @@ def test_layer_is_deterministic():
 def test_switch_full(name):
     say(f"[case] full {name}")
     r = Run(W.CONFIGS[name])
+    r.run_all(ffn_experts=8, ffn_rows=48, tokens=np.arange(0, r.cfg.T, 7))
+
+
+@pytest.mark.timeout(300)
+def test_p1_gelu_full():
+    """The from-scratch page's GELU model at its own size, fp32, full oracle."""
+    say("[case] full p1_gelu")
+    Run(W.P1_GELU).run_all()
+
+
+@pytest.mark.timeout(300)
+def test_switch_gelu_full():
+    say("[case] full switch_gelu")
+    r = Run(W.SWITCH_GELU)
     r.run_all(ffn_experts=8, ffn_rows=48, tokens=np.arange(0, r.cfg.T, 7))
 
 

@@ -24,7 +24,7 @@ class MoEConfig:
     d_out: int                  # output width
     E: int                      # routed experts
     k: int                      # experts per token
-    ffn: str                    # 'linear' | 'relu' | 'swiglu'
+    ffn: str                    # 'linear' | 'relu' | 'swiglu' | 'gelu'
     d_ff: int                   # hidden width (ignored for 'linear')
     gate: str                   # 'renorm' | 'prob'
     cf: Optional[float]         # capacity factor, None = no capacity limit
@@ -55,7 +55,7 @@ class MoEConfig:
 
     @property
     def has_w2(self) -> bool:
-        return self.ffn in ("relu", "swiglu")
+        return self.ffn in ("relu", "swiglu", "gelu")
 
     def scaled(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -96,7 +96,20 @@ STRESS = MoEConfig(
     wg_dist=("uniform", 1.0 / math.sqrt(7168)),
     w1_var=1.0 / 7168, w3_var=1.0 / 7168, w2_var=1.0 / 2048)
 
-CONFIGS = {c.name: c for c in (TINY, SWITCH, SWITCH_DROP, MIXTRAL, DEEPSEEK, STRESS)}
+# GELU experts (the two-layer nn.GELU experts of the from-scratch MoE page,
+# section 3): that page's own model (input 128, hidden 256, output 128, 8
+# experts, top-2 renormalised, biases everywhere, batch 32 x sequence 64,
+# fp32, linear layers at their default uniform init, given here as the
+# matching variances), and the Switch-shaped layer with GELU experts
+P1_GELU = MoEConfig(
+    name="p1_gelu", T=2048, d=128, d_out=128, E=8, k=2, ffn="gelu", d_ff=256,
+    gate="renorm", cf=None, act_dtype="f32", w_dtype="f32", alpha=1e-2, seed=5,
+    x_dist=("normal", 1.0), wg_dist=("uniform", 1.0 / math.sqrt(128)), bg_var=1.0 / 384,
+    w1_var=1.0 / 384, w2_var=1.0 / 768, b1_var=1.0 / 384, b2_var=1.0 / 768)
+
+SWITCH_GELU = SWITCH.scaled(name="switch_gelu", ffn="gelu", seed=6, b1_var=1e-2, b2_var=1e-2)
+
+CONFIGS = {c.name: c for c in (TINY, SWITCH, SWITCH_DROP, MIXTRAL, DEEPSEEK, STRESS, P1_GELU, SWITCH_GELU)}
 
 # The five workloads in their canonical order (tiny, Switch, Mixtral,
 # DeepSeekMoE, stress).
