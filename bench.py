@@ -143,7 +143,8 @@ def main():
     arr = W.generate(cfg)
     C = O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
     print(f"[bench] generated {cfg.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-    layer = MoELayer(**layer_kwargs(cfg, arr, C, device="cuda"))
+    lkw = layer_kwargs(cfg, arr, C, device="cuda")
+    layer = MoELayer(**lkw)
     x = to_tensor(arr["x"], "cuda")
     torch.cuda.synchronize()
 
@@ -162,6 +163,37 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
+
+    # timed region 1b: whole steps of the same layer with the routed FFN
+    # reading x through the dispatch permutation (no packed copy of x; the
+    # same weight tensors, bit-identical output)
+    glayer = MoELayer(**lkw, gather_rows=True)
+    for _ in range(args.warmup):
+        glayer.forward(x)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        glayer.forward(x)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step_gather = start.elapsed_time(stop) / args.steps
+    gd, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gf = torch.cuda.Event(enable_timing=True)
+    g_disp, g_exp = [], []
+    for _ in range(args.steps):
+        glayer.router(x)
+        gd.record()
+        glayer.dispatch(x)
+        ge.record()
+        glayer.experts()
+        gf.record()
+        torch.cuda.synchronize()
+        g_disp.append(gd.elapsed_time(ge))
+        g_exp.append(ge.elapsed_time(gf))
+    gathered = {"ms_per_step": ms_step_gather, "value": cfg.T / (ms_step_gather * 1e-3),
+                "dispatch_ms": float(np.median(g_disp)), "experts_ms": float(np.median(g_exp)),
+                "note": "routed FFN reads x through perm_token (moe_expert_ffn_gathered); dispatch copies no rows"}
+    del glayer
 
     # timed region 2: the same steps with HIP events between the stages, on
     # the stream the kernels are launched on (per-stage medians, roofline)
@@ -273,6 +305,7 @@ def main():
                      "kernel": "moe_expert_ffn_grouped (routed experts): gate/up GEMM + down GEMM",
                      "flops_per_launch": ffn_flops, "median_ms": st_ms["experts"]},
         "stages_ms": st_ms,
+        "gathered": gathered,
         "stages_hbm_frac": {
             "router": byts["router"] / (st_ms["router"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "dispatch": byts["dispatch"] / (st_ms["dispatch"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,

@@ -236,6 +236,34 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
                            hipStream_t stream);
 
 /*
+ * ---- (c') Grouped expert FFN reading its rows through the dispatch permutation
+ * P1 §2.4 gathers the tokens of an expert into one batch before running it;
+ * here the gather happens inside the first matrix product: packed row p of
+ * segment e is row perm_token[p] of x, read in place, so the packed copy
+ * Xp = x[perm_token] (moe_dispatch_permute with x and x_perm) need not exist.
+ * The result is bit-identical to moe_dispatch_permute followed by
+ * moe_expert_ffn_grouped in MOE_ROWS_PACKED mode.
+ *
+ *   x           [n_src, d]  the unpermuted activations (act_dt)
+ *   n_src       rows of x (T), >= 0
+ *   perm_token  [max_rows] int32 device: source row of each packed row, as
+ *               moe_dispatch_permute writes it; entries below offsets[E] must
+ *               lie in [0, n_src); NULL only when max_rows == 0
+ * Every other argument, the workspace (moe_ffn_workspace_size), the
+ * constraints and the errors are those of moe_expert_ffn_grouped in
+ * MOE_ROWS_PACKED mode; perm_token must be 16-byte aligned.  Rows of x are
+ * read through 32-bit offsets by the LDS-DMA kernel when n_src * d * 2 <
+ * 2^31, otherwise by the register-staged kernel.
+ */
+int moe_expert_ffn_gathered(int kind, const void* x, int act_dt, int n_src, const int32_t* perm_token,
+                            int max_rows, const int32_t* offsets, int E, int d, int d_ff, int d_out,
+                            const void* w1, const void* w3, const void* w2, int w_dt,
+                            const float* s1, const float* s3, const float* s2,
+                            const float* b1, const float* b2,
+                            void* y_rows, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * ---- (d) Combine: gate-weighted gather + shared experts + residual ----------
  * P1 §3.4 and P1 §4.3: weight * expert output accumulated into a
  * zero-initialised output; P3 §3.1: the same weighted sum over the k slots.

@@ -52,6 +52,8 @@ _SIGS = {
     "moe_ffn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn_grouped": (_i, [_i, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_gathered": (_i, [_i, _vp, _i, _i, _vp, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp]),
     "moe_aux_loss": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp]),
 }
@@ -179,6 +181,16 @@ def expert_ffn_grouped(kind, x_rows, max_rows, row_mode, offsets, E, d, d_ff, d_
                                       _p(s1), _p(s3), _p(s2), _p(b1), _p(b2), _p(y_rows), _p(workspace),
                                       ws_bytes, _stream(stream))
     _check("moe_expert_ffn_grouped", st)
+
+
+def expert_ffn_gathered(kind, x, perm_token, max_rows, offsets, E, d, d_ff, d_out, w1, w3, w2,
+                        s1, s3, s2, b1, b2, y_rows, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().moe_expert_ffn_gathered(kind, _p(x), dtype_code(x), x.shape[0], _p(perm_token), max_rows, _p(offsets),
+                                       E, d, d_ff, d_out, _p(w1), _p(w3), _p(w2), dtype_code(w1),
+                                       _p(s1), _p(s3), _p(s2), _p(b1), _p(b2), _p(y_rows), _p(workspace),
+                                       ws_bytes, _stream(stream))
+    _check("moe_expert_ffn_gathered", st)
 
 
 def combine(y_rows, dest_pos, topk_gate, d_out, shared_y, n_shared, residual, y, stream=None):

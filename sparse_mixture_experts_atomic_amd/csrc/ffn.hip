@@ -51,6 +51,7 @@ constexpr int kF32Rows = 4;
 // found by binary search on offsets.
 template <int EPI>
 __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ in, int in_shared,
+                                                     const int32_t* __restrict__ gather,
                                                      const int32_t* __restrict__ offsets, int E, int K, int N,
                                                      const float* __restrict__ W, const float* __restrict__ W3,
                                                      const float* __restrict__ bias, float* __restrict__ out) {
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
       if (offsets[mid] <= a) lo = mid; else hi = mid;
     }
     const int e = lo;
-    const int src = in_shared ? a - offsets[e] : a;
+    const int src = gather ? gather[a] : (in_shared ? a - offsets[e] : a);
     const float* xr = in + static_cast<size_t>(src) * K;
     const float* wr = W + (static_cast<size_t>(e) * N + n) * K;
     float acc = 0.f, acc3 = 0.f;
@@ -82,13 +83,14 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 template <int EPI>
-int launch_f32(const float* in, int in_shared, const int32_t* offsets, int E, int K, int N, const float* W,
-               const float* W3, const float* bias, float* out, int max_rows, hipStream_t stream) {
+int launch_f32(const float* in, int in_shared, const int32_t* gather, const int32_t* offsets, int E, int K, int N,
+               const float* W, const float* W3, const float* bias, float* out, int max_rows, hipStream_t stream) {
   int gy = (max_rows + kF32Rows - 1) / kF32Rows;
   if (gy > 65535) gy = 65535;
   if (gy < 1) gy = 1;
   dim3 grid((N + kF32Cols - 1) / kF32Cols, gy);
-  hipLaunchKernelGGL((ffn_f32_kernel<EPI>), grid, dim3(256), 0, stream, in, in_shared, offsets, E, K, N, W, W3, bias, out);
+  hipLaunchKernelGGL((ffn_f32_kernel<EPI>), grid, dim3(256), 0, stream, in, in_shared, gather, offsets, E, K, N, W,
+                     W3, bias, out);
   return check_launch();
 }
 
@@ -101,6 +103,11 @@ int current_cu_count() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return n;
 }
+
+int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode, const int32_t* gather,
+            int n_src, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1, const void* w3,
+            const void* w2, int w_dt, const float* s1, const float* s3, const float* s2, const float* b1,
+            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace
 }  // namespace moe
@@ -127,6 +134,30 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
                            const void* w3, const void* w2, int w_dt, const float* s1, const float* s3,
                            const float* s2, const float* b1, const float* b2, void* y_rows, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
+  if (row_mode != MOE_ROWS_PACKED && row_mode != MOE_ROWS_SHARED) return MOE_ERR_INVALID_ARG;
+  return ffn_run(kind, x_rows, act_dt, max_rows, row_mode, nullptr, 0, offsets, E, d, d_ff, d_out, w1, w3, w2, w_dt,
+                 s1, s3, s2, b1, b2, y_rows, workspace, workspace_bytes, stream);
+}
+
+int moe_expert_ffn_gathered(int kind, const void* x, int act_dt, int n_src, const int32_t* perm_token,
+                            int max_rows, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1,
+                            const void* w3, const void* w2, int w_dt, const float* s1, const float* s3,
+                            const float* s2, const float* b1, const float* b2, void* y_rows, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (n_src < 0 || (max_rows > 0 && !perm_token) || (perm_token && !aligned16(perm_token))) return MOE_ERR_INVALID_ARG;
+  return ffn_run(kind, x, act_dt, max_rows, MOE_ROWS_PACKED, perm_token, n_src, offsets, E, d, d_ff, d_out, w1, w3,
+                 w2, w_dt, s1, s3, s2, b1, b2, y_rows, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode, const int32_t* gather,
+            int n_src, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1, const void* w3,
+            const void* w2, int w_dt, const float* s1, const float* s3, const float* s2, const float* b1,
+            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (kind != MOE_FFN_LINEAR && kind != MOE_FFN_RELU && kind != MOE_FFN_SWIGLU && kind != MOE_FFN_GELU)
     return MOE_ERR_INVALID_ARG;
   if (act_dt != MOE_F32 && act_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
@@ -176,19 +207,19 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
     const float* X = static_cast<const float*>(x_rows);
     float* Y = static_cast<float*>(y_rows);
     if (kind == MOE_FFN_LINEAR)
-      return launch_f32<EPI_PLAIN>(X, shared_in, offsets, E, d, d_out, static_cast<const float*>(w1), nullptr, b1, Y,
-                                   max_rows, stream);
+      return launch_f32<EPI_PLAIN>(X, shared_in, gather, offsets, E, d, d_out, static_cast<const float*>(w1), nullptr,
+                                   b1, Y, max_rows, stream);
     float* Hf = static_cast<float*>(H);
     const float* W1 = static_cast<const float*>(w1);
     int st = kind == MOE_FFN_RELU
-                 ? launch_f32<EPI_RELU>(X, shared_in, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
+                 ? launch_f32<EPI_RELU>(X, shared_in, gather, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
              : kind == MOE_FFN_GELU
-                 ? launch_f32<EPI_GELU>(X, shared_in, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
-                 : launch_f32<EPI_SWIGLU>(X, shared_in, offsets, E, d, d_ff, W1, static_cast<const float*>(w3), nullptr,
-                                          Hf, max_rows, stream);
+                 ? launch_f32<EPI_GELU>(X, shared_in, gather, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
+                 : launch_f32<EPI_SWIGLU>(X, shared_in, gather, offsets, E, d, d_ff, W1, static_cast<const float*>(w3),
+                                          nullptr, Hf, max_rows, stream);
     if (st != MOE_OK) return st;
-    return launch_f32<EPI_PLAIN>(Hf, 0, offsets, E, d_ff, d_out, static_cast<const float*>(w2), nullptr, b2, Y,
-                                 max_rows, stream);
+    return launch_f32<EPI_PLAIN>(Hf, 0, nullptr, offsets, E, d_ff, d_out, static_cast<const float*>(w2), nullptr, b2,
+                                 Y, max_rows, stream);
   }
 
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, kGemmBM, ts);
@@ -199,6 +230,8 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
   GemmParams p1{};
   p1.A = static_cast<const uint16_t*>(x_rows);
   p1.a_shared = shared_in;
+  p1.gather = gather;
+  p1.a_rows = n_src;
   p1.offsets = offsets;
   p1.ts = ts;
   p1.E = E;
@@ -238,4 +271,5 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
   return launch_grouped_gemm(EPI_PLAIN, fp8, p2, max_rows, mtm, stream);
 }
 
-}  // extern "C"
+}  // namespace
+}  // namespace moe

@@ -140,6 +140,7 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
     a_slot[i] = swz(r, c);
     int rr = row0 + min(r, rows_valid - 1);
     if (p.a_shared) rr -= seg0;
+    if (p.gather) rr = p.gather[rr];
     a_src[i] = p.A + static_cast<size_t>(rr) * K;
   }
   const uint8_t* b_src[B_LD];
@@ -717,11 +718,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     // the same for every i).  Addresses: a uniform base (advanced by 2 BK bytes
     // per stage) plus a 32-bit per-lane byte offset fixed for the whole loop.
     const int cq = (tid & (CH - 1)) ^ ((tid >> 4) & (CH - 1));
-    const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K));
+    // gathered rows (the dispatch permutation read in place): the base is A's
+    // first row and each lane's offset that of its source row (the host
+    // keeps a_rows * K * 2 below 2^31)
+    const bool gat = p.gather != nullptr;
+    const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(
+        gat ? p.A : p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K));
     uint32_t a_vo[LDA];
 #pragma unroll
-    for (int i = 0; i < LDA; ++i)
-      a_vo[i] = static_cast<uint32_t>((min(i * RPI + tid / CH, rows_valid - 1) * K + cq * 8) * 2);
+    for (int i = 0; i < LDA; ++i) {
+      const int r = min(i * RPI + tid / CH, rows_valid - 1);
+      const int src = gat ? p.gather[row0 + r] : r;
+      a_vo[i] = static_cast<uint32_t>((src * K + cq * 8) * 2);
+    }
     const int cqb = (tid & (CHB - 1)) ^ ((tid >> 4) & (CHB - 1));
     const char* b_sb[LDB];
     uint32_t b_vo[LDB];
@@ -1146,7 +1155,8 @@ int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, in
   // expert's weight matrix and one m-tile
   const size_t wbytes = fp8 ? 1 : 2;
   const bool dma_ok = p.K % kDmaKMult == 0 && p.N % 8 == 0 && static_cast<size_t>(p.N) * p.K * wbytes < (size_t(1) << 31) &&
-                      static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31);
+                      static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31) &&
+                      (!p.gather || static_cast<size_t>(p.a_rows) * p.K * 2 < (size_t(1) << 31));
   if (dma_ok && fp8) {
     if (epi == EPI_SWIGLU) return launch_dma<EPI_SWIGLU, kDmaBK, true>(p, m_tiles_max, stream);
     if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK, true>(p, m_tiles_max, stream);

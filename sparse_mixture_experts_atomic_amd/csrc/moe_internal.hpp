@@ -112,6 +112,8 @@ constexpr int kGemmBM = 256;   // rows per m-tile of the grouped GEMM
 struct GemmParams {
   const uint16_t* A;         // bf16 rows [*, K]
   int a_shared;              // 1: segment e reads A rows from 0 (shared experts)
+  const int32_t* gather;     // packed row -> row of A (null: row itself); not with a_shared
+  int a_rows;                // rows of A when gathering (bounds the DMA offsets)
   const int32_t* offsets;    // [E+1] segment bounds
   const int32_t* ts;         // [E+1] m-tile prefix (tiles of kGemmBM rows)
   int E;

@@ -17,7 +17,7 @@ from . import _lib as L
 class MoELayer:
     def __init__(self, *, T: int, d: int, d_out: int, E: int, k: int, kind: str, d_ff: int, gate: str,
                  capacity: int, n_shared: int, alpha: float, act_dtype: torch.dtype,
-                 weights: Dict[str, Optional[torch.Tensor]], device="cuda"):
+                 weights: Dict[str, Optional[torch.Tensor]], device="cuda", gather_rows: bool = False):
         self.T, self.d, self.d_out, self.E, self.k = T, d, d_out, E, k
         self.kind = L.FFN_KINDS[kind]
         self.d_ff = d_ff
@@ -39,7 +39,10 @@ class MoELayer:
         self.offsets = torch.empty((E + 1,), **i32)
         self.dest_pos = torch.empty((T, k), **i32)
         self.perm_token = torch.empty((max(A, 1),), **i32)
-        self.x_perm = torch.empty((max(A, 1), d), dtype=act_dtype, device=dev)
+        # gather_rows: the routed FFN reads x through perm_token (no packed copy)
+        self.gather_rows = gather_rows
+        self._x_src = None
+        self.x_perm = None if gather_rows else torch.empty((max(A, 1), d), dtype=act_dtype, device=dev)
         self.y_rows = torch.empty((max(A, 1), d_out), dtype=act_dtype, device=dev)
         self.y = torch.empty((T, d_out), dtype=act_dtype, device=dev)
         self.loss = torch.empty((1,), **f32)
@@ -73,12 +76,21 @@ class MoELayer:
                             self.topk_idx, self.topk_gate, self.prob_colsum, None, self.ws_router_noisy)
 
     def dispatch(self, x, topk_idx=None):
-        L.dispatch_permute(self.topk_idx if topk_idx is None else topk_idx, self.E, self.capacity, x, self.x_perm,
+        if self.gather_rows:
+            self._x_src = x
+        L.dispatch_permute(self.topk_idx if topk_idx is None else topk_idx, self.E, self.capacity,
+                           None if self.gather_rows else x, self.x_perm,
                            self.counts_routed, self.counts_kept, self.offsets, self.dest_pos, self.perm_token,
                            self.ws_disp)
 
     def experts(self, x_perm=None, offsets=None):
         w = self.w
+        if self.gather_rows and x_perm is None:
+            L.expert_ffn_gathered(self.kind, self._x_src, self.perm_token, self.T * self.k,
+                                  self.offsets if offsets is None else offsets, self.E, self.d, self.d_ff, self.d_out,
+                                  w["w1"], w.get("w3"), w.get("w2"), w.get("s1"), w.get("s3"), w.get("s2"),
+                                  w.get("b1"), w.get("b2"), self.y_rows, self.ws_ffn)
+            return
         L.expert_ffn_grouped(self.kind, self.x_perm if x_perm is None else x_perm, self.T * self.k, L.ROWS_PACKED,
                              self.offsets if offsets is None else offsets, self.E, self.d, self.d_ff, self.d_out,
                              w["w1"], w.get("w3"), w.get("w2"), w.get("s1"), w.get("s3"), w.get("s2"),

@@ -143,6 +143,24 @@ def test_ffn_validation_before_launch():
     assert call(wsb=16) == L.ERR_WORKSPACE
 
 
+def test_gathered_ffn_validation_before_launch():
+    lib = L.lib()
+    fake = 1 << 20    # never dereferenced: validation fails first
+    f = lib.moe_expert_ffn_gathered
+
+    def call(x=fake, n_src=100, perm=fake, kind=L.FFN_SWIGLU, w3=fake, ws=fake, wsb=1 << 30):
+        return f(kind, x, L.BF16, n_src, perm, 200, fake, 8, 128, 256, 128, fake, w3, fake, L.BF16,
+                 None, None, None, None, None, fake, ws, wsb, None)
+
+    assert call(n_src=-1) == L.ERR_INVALID_ARG
+    assert call(perm=None) == L.ERR_INVALID_ARG
+    assert call(perm=fake + 4) == L.ERR_INVALID_ARG
+    assert call(kind=7) == L.ERR_INVALID_ARG
+    assert call(w3=None) == L.ERR_INVALID_ARG            # SwiGLU needs W3
+    assert call(x=fake + 2) == L.ERR_INVALID_ARG
+    assert call(ws=None, wsb=0) == L.ERR_WORKSPACE
+
+
 def test_combine_and_aux_validation_before_launch():
     lib = L.lib()
     f = 1 << 20
