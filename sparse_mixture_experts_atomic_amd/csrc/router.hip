@@ -523,6 +523,7 @@ constexpr int kLgBN = 64;                     // experts per block
 constexpr int kLgBK = 64;                     // columns per LDS chunk
 constexpr int kLgPad = kLgBK + 8;             // LDS row pitch (bf16): 16 rows of a read hit distinct banks
 constexpr int kLgThreads = 256;
+constexpr int kLgFlush = 4;                   // chunks per fp32 run of the logits GEMM
 
 template <int BM>
 __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
@@ -545,11 +546,18 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
   const int e0 = blockIdx.y * kLgBN;
   const int k0 = blockIdx.z * kslice;
   const int k1 = min(d, k0 + kslice);
+  // each run of kLgFlush 64-column chunks is summed in fp32 (MFMA), the
+  // running total in fp64, so that the rounding error does not grow with the
+  // slice width the way one long fp32 chain's does (at d = 7168 that chain's
+  // error reached 1e-5 of a logit)
   f32x4_mf acc[FT][2];
+  double tot[FT][2][4];
 #pragma unroll
   for (int i = 0; i < FT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_mf{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[i][j][q] = 0.0;
   // the next chunk's global loads are in flight while the current one is
   // multiplied out of LDS; d % 8 == 0 and slices are whole chunks, so a
   // piece is all in or all out
@@ -600,6 +608,13 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
     }
     __syncthreads();
     if (kc + kLgBK < k1) load(kc + kLgBK);
+    const int run = ((kc - k0) / kLgBK) % kLgFlush;          // chunk within the fp32 run
+    if (run == 0) {
+#pragma unroll
+      for (int i = 0; i < FT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_mf{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int ks = 0; ks < kLgBK / 32; ++ks) {
       bf16x8_t fa[FT], fb[2][3];
@@ -619,6 +634,14 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
           for (int pl = 0; pl < 3; ++pl)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j][pl], acc[i][j], 0, 0, 0);
     }
+    if (run == kLgFlush - 1 || kc + kLgBK >= k1) {
+#pragma unroll
+      for (int i = 0; i < FT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) tot[i][j][q] += static_cast<double>(acc[i][j][q]);
+    }
     __syncthreads();
   }
   // lane holds expert column r16 of tokens 4 (lane / 16) + q of each fragment
@@ -631,7 +654,7 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = t0 + wm * WT + i * 16 + (lane >> 4) * 4 + q;
-        if (t < T && e < E) out[static_cast<size_t>(t) * E + e] = acc[i][j][q];
+        if (t < T && e < E) out[static_cast<size_t>(t) * E + e] = static_cast<float>(tot[i][j][q]);
       }
     }
 }

@@ -28,6 +28,9 @@ CASES = {
     "switch_p5_top1": (W.SWITCH, 1e-2, True),
     # DeepSeekMoE-shaped router: 64 experts, top-6, router bias
     "deepseek": (W.DEEPSEEK, 1e-2, True),
+    # stress-shaped router at full size: 256 experts, top-8, d = 7168 (the
+    # tiled GEMM over 512 stacked rows, 128-token blocks)
+    "stress": (W.STRESS, 1e-2, True),
     # fp32 activations (the generic kernel), the small workload
     "tiny_f32": (W.TINY, 1e-2, True),
     # fp32, two 64-expert groups with a ragged second one, ragged tokens
@@ -68,6 +71,7 @@ def _run(x, w_g, b_g, w_n, b_n, noise, eps, k, gate, T, d, E, dt):
             lg.cpu().numpy().astype(np.float64))
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("name", list(CASES))
 def test_noisy_router_matches_oracle(name):
     cfg, eps, bias = CASES[name]
