@@ -12,6 +12,10 @@
  * The layer is five calls, run in this order on one stream:
  *   moe_router_topk -> moe_dispatch_permute -> moe_expert_ffn_grouped
  *   (routed experts, then shared experts) -> moe_combine -> moe_aux_loss.
+ * Variants: moe_router_topk_noisy in place of moe_router_topk (noisy gating
+ * in training mode), and moe_dispatch_permute without the row copy followed
+ * by moe_expert_ffn_gathered in place of moe_expert_ffn_grouped for the
+ * routed experts (the FFN reads x through the permutation).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE memory owned by the caller.  The library
