@@ -46,6 +46,11 @@ CASES = {
     "p1_gelu_bf16": W.P1_GELU.scaled(name="p1_gelu_bf16", act_dtype="bf16", w_dtype="bf16", seed=42),
     # fp32 path
     "p1_gelu_f32": W.P1_GELU,
+    # one token; one expert (every row in one segment)
+    "t1": _cfg("t1", T=1, d=128, E=4, k=2, ffn="swiglu", d_ff=128, gate="renorm", wg_dist=("normal", 1 / 128),
+               w1_var=1 / 128, w3_var=1 / 128, w2_var=1 / 128, seed=44),
+    "e1": _cfg("e1", T=300, d=256, E=1, k=1, ffn="gelu", d_ff=256, gate="renorm", wg_dist=("normal", 1 / 256),
+               w1_var=1 / 256, w2_var=1 / 256, b1_var=0.1, b2_var=0.1, seed=45),
     # Mixtral shape at full size
     "mixtral": W.MIXTRAL,
 }
@@ -139,3 +144,22 @@ def test_gathered_ffn_beyond_32bit_row_offsets():
         assert src.max() > cfg.T - 4096
     assert worst <= tol_for(cfg), f"rows vs oracle {worst:.3e}"
     say(f"  last rows of each segment vs oracle {worst:.2e}")
+
+
+def test_gathered_ffn_with_capacity_zero_reads_no_rows():
+    """Capacity 0: no packed row exists, perm_token is never written, and the
+    gathered FFN must not read it; the layer output is 0."""
+    cfg = _cfg("cap0", T=200, d=128, E=4, k=2, ffn="swiglu", d_ff=128, gate="renorm", cf=1e-9,
+               wg_dist=("normal", 1 / 128), w1_var=1 / 128, w3_var=1 / 128, w2_var=1 / 128, seed=46)
+    say("gathered ffn cap0: capacity 0, every assignment dropped")
+    arr = W.generate(cfg)
+    kw = layer_kwargs(cfg, arr, 0, "cuda")
+    g = MoELayer(**kw, gather_rows=True)
+    g.perm_token.fill_(0)                # a valid row: a wrong read would show as written rows
+    g.y_rows.fill_(7.0)
+    x = to_tensor(arr["x"], "cuda")
+    y, _ = g.forward(x)
+    torch.cuda.synchronize()
+    assert int(g.offsets[-1].item()) == 0
+    assert torch.all(g.y_rows.float() == 7.0)       # untouched
+    assert torch.all(y.float() == 0.0)

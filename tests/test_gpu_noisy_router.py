@@ -49,6 +49,11 @@ CASES = {
     # last chunk of 8 columns, router bias
     "bf16_e7_wide": (W.MIXTRAL.scaled(name="bf16_e7_wide", T=300, d=4360, d_out=16, E=7, k=3, gate="prob",
                                       wg_dist=("normal", 1.0 / 4360), bg_var=0.5, seed=26), 1e-2, True),
+    # degenerate shapes: one token, one expert (the gate is 1 whatever the
+    # noise); fp32 with k = E (every expert chosen, ids ordered by noisy logit)
+    "bf16_t1_e1": (W.MIXTRAL.scaled(name="bf16_t1_e1", T=1, d=64, d_out=64, E=1, k=1, gate="renorm",
+                                    wg_dist=("normal", 1.0 / 64), seed=27), 1e-2, True),
+    "f32_k_eq_e": (W.TINY.scaled(name="f32_k_eq_e", T=50, d=24, d_out=24, E=5, k=5, gate="prob", seed=28), 0.0, True),
     # bf16, at most 8 experts, several token groups per block (narrow rows)
     "bf16_bm128": (W.MIXTRAL.scaled(name="bf16_bm128", T=8200, d=64, d_out=64, E=8, k=2,
                                     wg_dist=("normal", 1.0 / 64), seed=25), 1e-2, True),
@@ -91,7 +96,8 @@ def test_noisy_router_matches_oracle(name):
     # the noise decides: the clean router picks another set for many tokens
     clean = O.topk_select(O.router_logits(O.to_f64(x, cfg.act_dtype), f64(w_g), f64(b_g)), k)
     changed = int(np.sum(np.any(np.sort(clean, axis=1) != np.sort(idx_g, axis=1), axis=1)))
-    assert changed > 0
+    if k < E and T > 1:
+        assert changed > 0
     # same inputs, same draws: the same bits
     again = _run(x, w_g, b_g, w_n, b_n, noise, eps, k, cfg.gate, T, d, E, dt)
     for a, b in zip((idx_g, gate_g, colsum_g, lg_g), again):
