@@ -174,7 +174,11 @@ int moe_router_topk_noisy(const void* x, int x_dt, const float* w_g, const float
  * before t; it is kept iff capacity < 0 or r < capacity.
  *
  *   topk_idx      [T, k] int32 in (ids outside [0, E) are treated as dropped
- *                 and not counted)
+ *                 and not counted).  The ids of one token must be distinct,
+ *                 as the router writes them (P1 §3.3: the k largest of E
+ *                 scores are k different experts).  With a repeated id in a
+ *                 token the integer outputs are unspecified, but every write
+ *                 still stays inside the output buffers.
  *   capacity      C >= 0, or -1 for no limit
  *   x             [T, d] in (x_dt MOE_F32 / MOE_BF16), may be NULL together
  *                 with x_perm to skip the row copy
@@ -187,7 +191,10 @@ int moe_router_topk_noisy(const void* x, int x_dt, const float* w_g, const float
  *   perm_token    [T*k] out: source token of each packed row; entries at and
  *                 beyond offsets[E] are left untouched
  * Every integer output is unique given topk_idx and is written
- * deterministically.
+ * deterministically.  Any T, k and d the arguments allow: rows wider than
+ * 64 KB, more than 256 slots per token or more than 64512 assignments take
+ * the count/rank/permute kernels instead of the one-launch kernel, with the
+ * same results.
  */
 size_t moe_dispatch_workspace_size(int T, int k, int E);
 int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capacity,
@@ -252,10 +259,12 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
  *   n_src       rows of x (T), >= 0
  *   perm_token  [max_rows] int32 device: source row of each packed row, as
  *               moe_dispatch_permute writes it; entries below offsets[E] must
- *               lie in [0, n_src); NULL only when max_rows == 0
+ *               lie in [0, n_src) (an entry outside is clamped into that
+ *               range, so no read leaves x); NULL only when max_rows == 0
  * Every other argument, the workspace (moe_ffn_workspace_size), the
  * constraints and the errors are those of moe_expert_ffn_grouped in
- * MOE_ROWS_PACKED mode; perm_token must be 16-byte aligned.  Rows of x are
+ * MOE_ROWS_PACKED mode; perm_token must be 16-byte aligned, and n_src == 0
+ * with max_rows > 0 is MOE_ERR_INVALID_ARG.  Rows of x are
  * read through 32-bit offsets by the LDS-DMA kernel when n_src * d * 2 <
  * 2^31, otherwise by the register-staged kernel.
  */
@@ -281,6 +290,7 @@ int moe_expert_ffn_gathered(int kind, const void* x, int act_dt, int n_src, cons
  *   residual  [T, d_out] dt, or NULL
  *   y         [T, d_out] out, dt.  Summation is fp32 in slot order, then the
  *             shared experts in order, then the residual.
+ * Any T >= 0 (beyond 65535 tokens each row of blocks takes several tokens).
  */
 int moe_combine(const void* y_rows, int dt, const int32_t* dest_pos, const float* topk_gate,
                 int T, int k, int d_out, const void* shared_y, int n_shared,

@@ -43,7 +43,8 @@ template <typename T> struct Vec<T, 1> {
   __device__ __forceinline__ static T pack(const float* f) { T r; Elem<T>::store(&r, 0, f[0]); return r; }
 };
 
-// One thread = one 16-byte output vector of one token (grid y = token).  The gate-weighted
+// One thread = one 16-byte output vector of one token (grid y = token,
+// strided past the grid-y limit).  The gate-weighted
 // rows of the (up to 8 unrolled) slots are loaded together, so a wavefront has
 // k row loads in flight; slot indices and gates are uniform across the
 // wavefront's 64 vectors of the same token.
@@ -55,51 +56,52 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_ro
                                                      const T* __restrict__ shared_y, int n_shared,
                                                      const T* __restrict__ residual, T* __restrict__ y) {
   using V = typename Vec<T, VW>::type;
-  const int t = blockIdx.y;
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= nvec) return;
   const V* yr = reinterpret_cast<const V*>(y_rows);
-  const int32_t* dp = dest_pos + static_cast<size_t>(t) * k;
-  const float* gp = gate + static_cast<size_t>(t) * k;
-  float acc[VW];
+  for (int t = blockIdx.y; t < T_; t += gridDim.y) {
+    const int32_t* dp = dest_pos + static_cast<size_t>(t) * k;
+    const float* gp = gate + static_cast<size_t>(t) * k;
+    float acc[VW];
 #pragma unroll
-  for (int i = 0; i < VW; ++i) acc[i] = 0.f;
-  for (int j0 = 0; j0 < k; j0 += kCbUnroll) {
-    V rv[kCbUnroll];
-    int d[kCbUnroll];
+    for (int i = 0; i < VW; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kCbUnroll) {
+      V rv[kCbUnroll];
+      int d[kCbUnroll];
 #pragma unroll
-    for (int u = 0; u < kCbUnroll; ++u) {
-      d[u] = j0 + u < k ? dp[j0 + u] : -1;
-      if (d[u] >= 0) rv[u] = yr[static_cast<size_t>(d[u]) * nvec + v];
+      for (int u = 0; u < kCbUnroll; ++u) {
+        d[u] = j0 + u < k ? dp[j0 + u] : -1;
+        if (d[u] >= 0) rv[u] = yr[static_cast<size_t>(d[u]) * nvec + v];
+      }
+#pragma unroll
+      for (int u = 0; u < kCbUnroll; ++u) {
+        if (d[u] < 0) continue;
+        const float g = gp[j0 + u];
+        float f[VW];
+        Vec<T, VW>::unpack(rv[u], f);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+      }
     }
-#pragma unroll
-    for (int u = 0; u < kCbUnroll; ++u) {
-      if (d[u] < 0) continue;
-      const float g = gp[j0 + u];
+    const V* sy = reinterpret_cast<const V*>(shared_y);
+    for (int s = 0; s < n_shared; ++s) {
       float f[VW];
-      Vec<T, VW>::unpack(rv[u], f);
+      Vec<T, VW>::unpack(sy[(static_cast<size_t>(s) * T_ + t) * nvec + v], f);
 #pragma unroll
-      for (int i = 0; i < VW; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+      for (int i = 0; i < VW; ++i) acc[i] += f[i];
     }
-  }
-  const V* sy = reinterpret_cast<const V*>(shared_y);
-  for (int s = 0; s < n_shared; ++s) {
-    float f[VW];
-    Vec<T, VW>::unpack(sy[(static_cast<size_t>(s) * T_ + t) * nvec + v], f);
+    if (residual) {
+      float f[VW];
+      Vec<T, VW>::unpack(reinterpret_cast<const V*>(residual)[static_cast<size_t>(t) * nvec + v], f);
 #pragma unroll
-    for (int i = 0; i < VW; ++i) acc[i] += f[i];
+      for (int i = 0; i < VW; ++i) acc[i] += f[i];
+    }
+    reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
   }
-  if (residual) {
-    float f[VW];
-    Vec<T, VW>::unpack(reinterpret_cast<const V*>(residual)[static_cast<size_t>(t) * nvec + v], f);
-#pragma unroll
-    for (int i = 0; i < VW; ++i) acc[i] += f[i];
-  }
-  reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
 }
 
-// k known at compile time (1, 2, 4 or 8): one thread per 16-byte output
-// vector of one token (grid y = token); the K slot rows are loaded together,
+// k known at compile time (1 to 8): one thread per 16-byte output vector of
+// one token (grid y = token, strided past the grid-y limit); the K slot rows are loaded together,
 // then accumulated in slot order (dropped slots skipped), then the shared
 // experts and the residual, as in combine_kernel.
 template <typename T, int VW, int K>
@@ -108,50 +110,55 @@ __global__ __launch_bounds__(256) void combine_kk_kernel(const T* __restrict__ y
                                                         const T* __restrict__ shared_y, int n_shared,
                                                         const T* __restrict__ residual, T* __restrict__ y) {
   using V = typename Vec<T, VW>::type;
-  const int t = blockIdx.y;
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= nvec) return;
   const V* yr = reinterpret_cast<const V*>(y_rows);
-  int d[K];
-  V rv[K];
+  for (int t = blockIdx.y; t < T_; t += gridDim.y) {
+    int d[K];
+    V rv[K];
 #pragma unroll
-  for (int u = 0; u < K; ++u) {
-    d[u] = dest_pos[static_cast<size_t>(t) * K + u];
-    if (d[u] >= 0) rv[u] = yr[static_cast<size_t>(d[u]) * nvec + v];
+    for (int u = 0; u < K; ++u) {
+      d[u] = dest_pos[static_cast<size_t>(t) * K + u];
+      if (d[u] >= 0) rv[u] = yr[static_cast<size_t>(d[u]) * nvec + v];
+    }
+    float acc[VW];
+#pragma unroll
+    for (int c = 0; c < VW; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      if (d[u] < 0) continue;
+      const float g = gate[static_cast<size_t>(t) * K + u];
+      float f[VW];
+      Vec<T, VW>::unpack(rv[u], f);
+#pragma unroll
+      for (int c = 0; c < VW; ++c) acc[c] = fmaf(g, f[c], acc[c]);
+    }
+    const V* sy = reinterpret_cast<const V*>(shared_y);
+    for (int sI = 0; sI < n_shared; ++sI) {
+      float f[VW];
+      Vec<T, VW>::unpack(sy[(static_cast<size_t>(sI) * T_ + t) * nvec + v], f);
+#pragma unroll
+      for (int c = 0; c < VW; ++c) acc[c] += f[c];
+    }
+    if (residual) {
+      float f[VW];
+      Vec<T, VW>::unpack(reinterpret_cast<const V*>(residual)[static_cast<size_t>(t) * nvec + v], f);
+#pragma unroll
+      for (int c = 0; c < VW; ++c) acc[c] += f[c];
+    }
+    reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
   }
-  float acc[VW];
-#pragma unroll
-  for (int c = 0; c < VW; ++c) acc[c] = 0.f;
-#pragma unroll
-  for (int u = 0; u < K; ++u) {
-    if (d[u] < 0) continue;
-    const float g = gate[static_cast<size_t>(t) * K + u];
-    float f[VW];
-    Vec<T, VW>::unpack(rv[u], f);
-#pragma unroll
-    for (int c = 0; c < VW; ++c) acc[c] = fmaf(g, f[c], acc[c]);
-  }
-  const V* sy = reinterpret_cast<const V*>(shared_y);
-  for (int sI = 0; sI < n_shared; ++sI) {
-    float f[VW];
-    Vec<T, VW>::unpack(sy[(static_cast<size_t>(sI) * T_ + t) * nvec + v], f);
-#pragma unroll
-    for (int c = 0; c < VW; ++c) acc[c] += f[c];
-  }
-  if (residual) {
-    float f[VW];
-    Vec<T, VW>::unpack(reinterpret_cast<const V*>(residual)[static_cast<size_t>(t) * nvec + v], f);
-#pragma unroll
-    for (int c = 0; c < VW; ++c) acc[c] += f[c];
-  }
-  reinterpret_cast<V*>(y)[static_cast<size_t>(t) * nvec + v] = Vec<T, VW>::pack(acc);
 }
+
+// grid y: one token per row of blocks up to the device's grid-y limit;
+// beyond it each row of blocks takes every gridDim.y-th token
+constexpr int kCbMaxGridY = 65535;
 
 template <typename T, int VW>
 int launch_combine(const void* y_rows, const int32_t* dest_pos, const float* gate, int T_, int k, int d_out,
                    const void* shared_y, int n_shared, const void* residual, void* y, hipStream_t stream) {
   const int nvec = d_out / VW;
-  const dim3 grid((nvec + 255) / 256, T_);   // (vector blocks of a row, tokens)
+  const dim3 grid((nvec + 255) / 256, T_ < kCbMaxGridY ? T_ : kCbMaxGridY);   // (vector blocks of a row, tokens)
 #define MOE_CB_K(KK)                                                                                          \
   hipLaunchKernelGGL((combine_kk_kernel<T, VW, KK>), grid, dim3(256), 0, stream, static_cast<const T*>(y_rows), \
                      dest_pos, gate, T_, nvec, static_cast<const T*>(shared_y), n_shared,                      \
@@ -160,7 +167,11 @@ int launch_combine(const void* y_rows, const int32_t* dest_pos, const float* gat
   switch (k) {
     case 1: MOE_CB_K(1);
     case 2: MOE_CB_K(2);
+    case 3: MOE_CB_K(3);
     case 4: MOE_CB_K(4);
+    case 5: MOE_CB_K(5);
+    case 6: MOE_CB_K(6);
+    case 7: MOE_CB_K(7);
     case 8: MOE_CB_K(8);
     default: break;
   }

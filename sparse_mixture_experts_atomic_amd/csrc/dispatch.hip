@@ -186,6 +186,7 @@ constexpr int kFusedMaxEntries = 63 * 4 * 256;
 constexpr int kPackedE = 8;                    // register-packed counting for E <= 8
 constexpr int kIdPre = 8;                      // int4 id loads per thread issued before the rows
 constexpr int kFusedThreads = 256;
+constexpr int kFusedMaxVec = 16;               // row vectors per thread (the largest NQ instance)
 
 template <int NQ>
 __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
@@ -462,12 +463,17 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
     return check_launch();
   }
   const size_t row_bytes = copy_rows ? static_cast<size_t>(d) * dtype_bytes(x_dt) : 0;
-  if (static_cast<long>(T) * k <= kFusedMaxEntries && row_bytes % 16 == 0) {
+  // The one-launch kernel holds one entry per thread (so at most kFusedThreads
+  // slots of one token) and at most kFusedMaxVec 16-byte vectors of rows per
+  // thread (so one row of at most kFusedMaxVec * kFusedThreads vectors); wider
+  // rows or more slots per token take the count/rank/permute launches.
+  if (static_cast<long>(T) * k <= kFusedMaxEntries && row_bytes % 16 == 0 && k <= kFusedThreads &&
+      row_bytes / 16 <= static_cast<size_t>(kFusedMaxVec) * kFusedThreads) {
     // tokens per block: at most 16 row vectors per thread, at most 256 entries,
     // and about 1024 blocks when T allows (four per CU: the row loads of one
     // block overlap the index work and stores of the others)
     const int nvec = static_cast<int>(row_bytes / 16);
-    int tpb = nvec > 0 ? (16 * kFusedThreads) / nvec : kFusedThreads;
+    int tpb = nvec > 0 ? (kFusedMaxVec * kFusedThreads) / nvec : kFusedThreads;
     tpb = min(tpb, kFusedThreads / k);
     tpb = min(tpb, max(1, (T + 1023) / 1024));
     tpb = max(tpb, 1);

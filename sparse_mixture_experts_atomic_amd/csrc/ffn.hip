@@ -51,7 +51,7 @@ constexpr int kF32Rows = 4;
 // found by binary search on offsets.
 template <int EPI>
 __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ in, int in_shared,
-                                                     const int32_t* __restrict__ gather,
+                                                     const int32_t* __restrict__ gather, int n_src,
                                                      const int32_t* __restrict__ offsets, int E, int K, int N,
                                                      const float* __restrict__ W, const float* __restrict__ W3,
                                                      const float* __restrict__ bias, float* __restrict__ out) {
@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
       if (offsets[mid] <= a) lo = mid; else hi = mid;
     }
     const int e = lo;
-    const int src = gather ? gather[a] : (in_shared ? a - offsets[e] : a);
+    // gathered rows are clamped into x, so no entry can address outside it
+    const int src = gather ? min(max(gather[a], 0), n_src - 1) : (in_shared ? a - offsets[e] : a);
     const float* xr = in + static_cast<size_t>(src) * K;
     const float* wr = W + (static_cast<size_t>(e) * N + n) * K;
     float acc = 0.f, acc3 = 0.f;
@@ -83,14 +84,15 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 template <int EPI>
-int launch_f32(const float* in, int in_shared, const int32_t* gather, const int32_t* offsets, int E, int K, int N,
-               const float* W, const float* W3, const float* bias, float* out, int max_rows, hipStream_t stream) {
+int launch_f32(const float* in, int in_shared, const int32_t* gather, int n_src, const int32_t* offsets, int E, int K,
+               int N, const float* W, const float* W3, const float* bias, float* out, int max_rows,
+               hipStream_t stream) {
   int gy = (max_rows + kF32Rows - 1) / kF32Rows;
   if (gy > 65535) gy = 65535;
   if (gy < 1) gy = 1;
   dim3 grid((N + kF32Cols - 1) / kF32Cols, gy);
-  hipLaunchKernelGGL((ffn_f32_kernel<EPI>), grid, dim3(256), 0, stream, in, in_shared, gather, offsets, E, K, N, W,
-                     W3, bias, out);
+  hipLaunchKernelGGL((ffn_f32_kernel<EPI>), grid, dim3(256), 0, stream, in, in_shared, gather, n_src, offsets, E, K,
+                     N, W, W3, bias, out);
   return check_launch();
 }
 
@@ -144,7 +146,8 @@ int moe_expert_ffn_gathered(int kind, const void* x, int act_dt, int n_src, cons
                             const void* w3, const void* w2, int w_dt, const float* s1, const float* s3,
                             const float* s2, const float* b1, const float* b2, void* y_rows, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-  if (n_src < 0 || (max_rows > 0 && !perm_token) || (perm_token && !aligned16(perm_token))) return MOE_ERR_INVALID_ARG;
+  if (n_src < 0 || (max_rows > 0 && (!perm_token || n_src == 0)) || (perm_token && !aligned16(perm_token)))
+    return MOE_ERR_INVALID_ARG;
   return ffn_run(kind, x, act_dt, max_rows, MOE_ROWS_PACKED, perm_token, n_src, offsets, E, d, d_ff, d_out, w1, w3,
                  w2, w_dt, s1, s3, s2, b1, b2, y_rows, workspace, workspace_bytes, stream);
 }
@@ -207,18 +210,18 @@ int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode
     const float* X = static_cast<const float*>(x_rows);
     float* Y = static_cast<float*>(y_rows);
     if (kind == MOE_FFN_LINEAR)
-      return launch_f32<EPI_PLAIN>(X, shared_in, gather, offsets, E, d, d_out, static_cast<const float*>(w1), nullptr,
+      return launch_f32<EPI_PLAIN>(X, shared_in, gather, n_src, offsets, E, d, d_out, static_cast<const float*>(w1), nullptr,
                                    b1, Y, max_rows, stream);
     float* Hf = static_cast<float*>(H);
     const float* W1 = static_cast<const float*>(w1);
     int st = kind == MOE_FFN_RELU
-                 ? launch_f32<EPI_RELU>(X, shared_in, gather, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
+                 ? launch_f32<EPI_RELU>(X, shared_in, gather, n_src, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
              : kind == MOE_FFN_GELU
-                 ? launch_f32<EPI_GELU>(X, shared_in, gather, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
-                 : launch_f32<EPI_SWIGLU>(X, shared_in, gather, offsets, E, d, d_ff, W1, static_cast<const float*>(w3),
+                 ? launch_f32<EPI_GELU>(X, shared_in, gather, n_src, offsets, E, d, d_ff, W1, nullptr, b1, Hf, max_rows, stream)
+                 : launch_f32<EPI_SWIGLU>(X, shared_in, gather, n_src, offsets, E, d, d_ff, W1, static_cast<const float*>(w3),
                                           nullptr, Hf, max_rows, stream);
     if (st != MOE_OK) return st;
-    return launch_f32<EPI_PLAIN>(Hf, 0, nullptr, offsets, E, d_ff, d_out, static_cast<const float*>(w2), nullptr, b2,
+    return launch_f32<EPI_PLAIN>(Hf, 0, nullptr, 0, offsets, E, d_ff, d_out, static_cast<const float*>(w2), nullptr, b2,
                                  Y, max_rows, stream);
   }
 

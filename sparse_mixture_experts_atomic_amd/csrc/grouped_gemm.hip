@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, BN == 128 ? 2 : 1) void grouped_gemm_kern
     a_slot[i] = swz(r, c);
     int rr = row0 + min(r, rows_valid - 1);
     if (p.a_shared) rr -= seg0;
-    if (p.gather) rr = p.gather[rr];
+    if (p.gather) rr = min(max(p.gather[rr], 0), p.a_rows - 1);   // clamped: never outside A
     a_src[i] = p.A + static_cast<size_t>(rr) * K;
   }
   const uint8_t* b_src[B_LD];
@@ -728,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
 #pragma unroll
     for (int i = 0; i < LDA; ++i) {
       const int r = min(i * RPI + tid / CH, rows_valid - 1);
-      const int src = gat ? p.gather[row0 + r] : r;
+      const int src = gat ? min(max(p.gather[row0 + r], 0), p.a_rows - 1) : r;   // clamped: never outside A
       a_vo[i] = static_cast<uint32_t>((src * K + cq * 8) * 2);
     }
     const int cqb = (tid & (CHB - 1)) ^ ((tid >> 4) & (CHB - 1));
