@@ -139,13 +139,13 @@ def main():
 
     import workloads as W
     from sparse_mixture_experts_atomic_amd import MoELayer
+    from sparse_mixture_experts_atomic_amd import _lib as L
     from workloads.device import layer_kwargs, to_tensor
-    import oracle as O
 
     cfg = W.CONFIGS[args.workload]
     t0 = time.perf_counter()
     arr = W.generate(cfg)
-    C = O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+    C = L.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
     print(f"[bench] generated {cfg.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     lkw = layer_kwargs(cfg, arr, C, device="cuda")
     layer = MoELayer(**lkw)

@@ -30,6 +30,7 @@ ROWS_PACKED, ROWS_SHARED = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4
 
 GATE_MODES = {"prob": GATE_PROB, "renorm": GATE_RENORM}
+CAP_ROUNDS = {"ceil": CAP_CEIL, "floor": CAP_FLOOR}
 FFN_KINDS = {"linear": FFN_LINEAR, "relu": FFN_RELU, "swiglu": FFN_SWIGLU, "gelu": FFN_GELU}
 
 _vp = ctypes.c_void_p
@@ -119,7 +120,13 @@ def _check(name: str, st: int):
         raise MoEError(name, st)
 
 
-def capacity(T: int, k: int, E: int, cf: Optional[float], round_mode: int = CAP_CEIL) -> int:
+def capacity(T: int, k: int, E: int, cf: Optional[float], round_mode=CAP_CEIL) -> int:
+    """moe_capacity: C >= 0, or -1 (no limit) when cf is None or <= 0.
+    round_mode is CAP_CEIL / CAP_FLOOR or their names 'ceil' / 'floor'."""
+    if isinstance(round_mode, str):
+        round_mode = CAP_ROUNDS[round_mode]
+    if T < 0 or k < 1 or E < 1:
+        raise ValueError("moe_capacity needs T >= 0, k >= 1 and E >= 1")
     return lib().moe_capacity(T, k, E, 0.0 if cf is None else float(cf), round_mode)
 
 

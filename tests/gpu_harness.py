@@ -26,6 +26,7 @@ import torch
 import oracle as O
 import workloads as W
 from sparse_mixture_experts_atomic_amd import MoELayer
+from sparse_mixture_experts_atomic_amd import _lib as L
 from workloads.device import layer_kwargs, to_tensor
 
 GAP = 1e-5
@@ -99,7 +100,9 @@ class Run:
     def __init__(self, cfg: W.MoEConfig, arrays: Optional[Dict] = None, device: str = "cuda"):
         self.cfg = cfg
         self.arr = arrays if arrays is not None else W.generate(cfg)
-        self.C = O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+        # the layer runs with the library's own capacity; the oracle's must agree
+        self.C = L.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+        assert self.C == O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round), cfg.name
         self.layer = MoELayer(**layer_kwargs(cfg, self.arr, self.C, device))
         self.x = to_tensor(self.arr["x"], device)
         self.x64 = O.to_f64(self.arr["x"], cfg.act_dtype)
@@ -107,6 +110,7 @@ class Run:
         self.b_g = None if self.arr["b_g"] is None else self.arr["b_g"].astype(np.float64)
         self._z = None
         self._wcache = {}
+        self._wbytes = 0
 
     # -- oracle pieces --------------------------------------------------------
     @property
@@ -115,18 +119,25 @@ class Run:
             self._z = O.router_logits(self.x64, self.w_g, self.b_g)
         return self._z
 
+    # float64 weights of the experts decoded so far, up to this many bytes
+    # (one Mixtral-shaped expert is 1.4 GB in float64)
+    WCACHE_BYTES = 3 << 30
+
     def expert_w(self, e: int, shared: bool = False):
         key = (e, shared)
         if key not in self._wcache:
-            if len(self._wcache) > 24:
-                self._wcache.clear()
             pre = "sh_" if shared else ""
             sub = {}
             for n in ("w1", "s1", "w3", "s3", "w2", "s2", "b1", "b2"):
                 a = self.arr.get(pre + n)
                 sub[n] = None if a is None else a[e:e + 1]
-            w = O.decode_weights(sub, self.cfg.w_dtype)
-            self._wcache[key] = {k: v[0] for k, v in w.items()}
+            w = {k: v[0] for k, v in O.decode_weights(sub, self.cfg.w_dtype).items()}
+            nbytes = sum(v.nbytes for v in w.values())
+            while self._wcache and self._wbytes + nbytes > self.WCACHE_BYTES:
+                old = next(iter(self._wcache))
+                self._wbytes -= sum(v.nbytes for v in self._wcache.pop(old).values())
+            self._wcache[key] = w
+            self._wbytes += nbytes
         return self._wcache[key]
 
     def ffn64(self, e: int, rows: np.ndarray, shared: bool = False) -> np.ndarray:
@@ -152,29 +163,35 @@ class Run:
         self.layer.dispatch(self.x)
         torch.cuda.synchronize()
         ref = O.dispatch(self.idx_g, cfg.E, self.C)
-        L = self.layer
-        got = {"counts_routed": L.counts_routed, "counts_kept": L.counts_kept, "offsets": L.offsets,
-               "dest_pos": L.dest_pos}
+        ly = self.layer
+        got = {"counts_routed": ly.counts_routed, "counts_kept": ly.counts_kept, "offsets": ly.offsets,
+               "dest_pos": ly.dest_pos}
         for k, t in got.items():
             a = t.cpu().numpy()
             assert np.array_equal(a, ref[k]), f"{cfg.name}: dispatch {k} differs"
         A = int(ref["offsets"][-1])
-        perm = L.perm_token[:A].cpu().numpy()
+        perm = ly.perm_token[:A].cpu().numpy()
         assert np.array_equal(perm, ref["perm_token"]), f"{cfg.name}: perm_token differs"
-        # packed rows are exact copies
+        # packed rows are exact copies: every row (or a sample), compared as
+        # bytes on the host in chunks of about 256 MB
         rows = np.arange(A) if row_sample is None or row_sample >= A else \
             np.unique(np.concatenate([np.random.default_rng(seed).choice(A, row_sample, replace=False),
                                       ref["offsets"][:-1][ref["counts_kept"] > 0], [A - 1]]))
-        xp = L.x_perm[torch.from_numpy(rows).to(L.x_perm.device)].cpu()
-        src = self.x.cpu()[torch.from_numpy(perm[rows].astype(np.int64))]
-        if xp.dtype == torch.bfloat16:
-            assert torch.equal(xp.view(torch.int16), src.view(torch.int16)), f"{cfg.name}: x_perm bytes differ"
-        else:
-            assert torch.equal(xp, src), f"{cfg.name}: x_perm differs"
+        x_host = self.x.cpu()
+        x_host = x_host.view(torch.int16) if x_host.dtype == torch.bfloat16 else x_host.view(torch.int32)
+        step = max(1, (256 << 20) // max(1, x_host.shape[1] * x_host.element_size()))
+        for c0 in range(0, len(rows), step):
+            rc = rows[c0:c0 + step]
+            xp = ly.x_perm[torch.from_numpy(rc).to(ly.x_perm.device)].cpu()
+            xp = xp.view(torch.int16) if xp.dtype == torch.bfloat16 else xp.view(torch.int32)
+            src = x_host[torch.from_numpy(perm[rc].astype(np.int64))]
+            assert torch.equal(xp, src), f"{cfg.name}: x_perm bytes differ in rows {rc[0]}..{rc[-1]}"
+        self.xp_rows_checked = len(rows)
         self.disp = ref
         dropped = int((ref["dest_pos"] < 0).sum())
         say(f"dispatch {cfg.name}: kept {A} dropped {dropped} C={self.C} loads "
-            f"{int(ref['counts_routed'].min())}..{int(ref['counts_routed'].max())}")
+            f"{int(ref['counts_routed'].min())}..{int(ref['counts_routed'].max())}; "
+            f"{len(rows)} packed rows byte-compared")
         return ref
 
     def _segment_rows(self, max_experts: Optional[int], rows_per_expert: Optional[int], seed: int):
@@ -208,15 +225,19 @@ class Run:
         segs = self._segment_rows(max_experts, rows_per_expert, seed)
         worst = 0.0
         n = 0
-        for e, rows in segs.items():
+        for i, (e, rows) in enumerate(segs.items()):
             ridx = torch.from_numpy(rows).to(self.layer.y_rows.device)
             xp = act_to_f64(self.layer.x_perm[ridx])
             yg = act_to_f64(self.layer.y_rows[ridx])
             ref = self.ffn64(e, xp)
             worst = max(worst, rownorm_err(yg, ref))
             n += len(rows)
+            if i % 16 == 15:
+                say(f"  ffn {cfg.name}: {i + 1}/{len(segs)} experts, {n} rows so far, err {worst:.2e}")
         assert worst <= tol_for(cfg), f"{cfg.name}: expert FFN err {worst:.3e}"
-        say(f"ffn {cfg.name}: {len(segs)} experts {n} rows err {worst:.2e}")
+        whole = sum(1 for e, r in segs.items() if len(r) == self.disp["offsets"][e + 1] - self.disp["offsets"][e])
+        say(f"ffn {cfg.name}: {len(segs)} experts ({whole} whole segments) {n} of "
+            f"{int(self.disp['offsets'][-1])} rows err {worst:.2e}")
         return worst
 
     def check_shared(self, rows: Optional[np.ndarray] = None):
@@ -236,13 +257,22 @@ class Run:
         say(f"shared {cfg.name}: {cfg.n_shared} experts {len(rows)} rows err {worst:.2e}")
         return worst
 
-    def check_combine(self, tokens: Optional[np.ndarray] = None, residual: bool = False):
+    def check_combine(self, tokens: Optional[np.ndarray] = None, residual: bool = False, chunk: int = 4096):
         cfg = self.cfg
         res = self.x if residual else None
         self.layer.combine(res)
         torch.cuda.synchronize()
-        T = cfg.T
-        tokens = np.arange(T) if tokens is None else tokens
+        tokens = np.arange(cfg.T) if tokens is None else tokens
+        worst, alldrop = 0.0, 0
+        for c0 in range(0, max(len(tokens), 1), chunk):
+            e, a = self._combine_chunk(tokens[c0:c0 + chunk], residual)
+            worst, alldrop = max(worst, e), alldrop + a
+        assert worst <= tol_for(cfg), f"{cfg.name}: combine err {worst:.3e}"
+        say(f"combine {cfg.name}: {len(tokens)} of {cfg.T} tokens err {worst:.2e} all-dropped {alldrop}")
+        return worst
+
+    def _combine_chunk(self, tokens: np.ndarray, residual: bool):
+        cfg = self.cfg
         dest = self.disp["dest_pos"][tokens]
         used = np.unique(dest[dest >= 0])
         remap = np.full(max(int(self.disp["offsets"][-1]), 1), -1, dtype=np.int64)
@@ -264,9 +294,7 @@ class Run:
         if not cfg.n_shared and alldrop.any():
             want = self.x64[tokens][alldrop] if residual else 0.0
             assert np.all(yg[alldrop] == want), f"{cfg.name}: dropped tokens not exact"
-        assert err <= tol_for(cfg), f"{cfg.name}: combine err {err:.3e}"
-        say(f"combine {cfg.name}: {len(tokens)} tokens err {err:.2e} all-dropped {int(alldrop.sum())}")
-        return err
+        return err, int(alldrop.sum())
 
     def check_aux(self):
         cfg = self.cfg
@@ -304,18 +332,22 @@ class Run:
             for j in range(cfg.k):
                 if disp["dest_pos"][t, j] >= 0:
                     by_e.setdefault(int(idx[t, j]), []).append((i, t, j))
-        for e, lst in by_e.items():
-            rows = self.x64[[t for _, t, _ in lst]]
-            out = self.ffn64(e, rows)
-            for (i, t, j), o in zip(lst, out):
-                ref[i] += g[t, j] * o
+        for n_done, (e, lst) in enumerate(sorted(by_e.items())):
+            ii = np.array([i for i, _, _ in lst], dtype=np.int64)
+            tt = np.array([t for _, t, _ in lst], dtype=np.int64)
+            jj = np.array([j for _, _, j in lst], dtype=np.int64)
+            out = self.ffn64(e, self.x64[tt])
+            np.add.at(ref, ii, g[tt, jj][:, None] * out)
+            if n_done % 32 == 31:
+                say(f"  e2e {cfg.name}: {n_done + 1}/{len(by_e)} experts")
         for s in range(cfg.n_shared):
             ref += self.ffn64(s, self.x64[toks], shared=True)
         yg = act_to_f64(self.layer.y[torch.from_numpy(toks).to(self.layer.y.device)])
         err = rownorm_err(yg, ref)
         assert err <= tol_for(cfg), f"{cfg.name}: end-to-end err {err:.3e}"
         assert good.mean() >= 0.98, f"{cfg.name}: too many tokens excluded ({(~good).sum()})"
-        say(f"e2e {cfg.name}: {len(toks)} tokens err {err:.2e} excluded {int((~good).sum())}")
+        say(f"e2e {cfg.name}: {len(toks)} of {len(tokens)} tokens err {err:.2e} excluded {int((~good).sum())} "
+            f"(near-tied or dropped differently)")
         return err
 
     def run_all(self, ffn_experts=None, ffn_rows=None, tokens=None, e2e_tokens=None, row_sample=None,

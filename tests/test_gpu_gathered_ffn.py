@@ -58,7 +58,8 @@ CASES = {
 
 def _layers(cfg):
     arr = W.generate(cfg)
-    C = O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+    C = L.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+    assert C == O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
     kw = layer_kwargs(cfg, arr, C, "cuda")
     packed = MoELayer(**kw)
     gathered = MoELayer(**kw, gather_rows=True)
@@ -117,7 +118,8 @@ def test_gathered_ffn_beyond_32bit_row_offsets():
                wg_dist=("normal", 1 / 8192), w1_var=1 / 8192, seed=43)
     say(f"gathered ffn {cfg.name}: T={cfg.T} d={cfg.d} ({cfg.T * cfg.d * 2 / 2**30:.3f} GiB of x)")
     arr = W.generate(cfg)
-    C = O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+    C = L.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
+    assert C == O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
     kw = layer_kwargs(cfg, arr, C, "cuda")
     g = MoELayer(**kw, gather_rows=True)
     x = to_tensor(arr["x"], "cuda")

@@ -421,6 +421,70 @@ def test_fp8_weights_decode_with_row_scales():
     assert O.to_f64(q, "fp8", s).tolist() == [[0.5, 1.0], [896.0, 2.0 ** -8]]
 
 
+def test_decode_weights_pairs_each_matrix_with_its_own_scales_and_keeps_biases():
+    # every code decodes to a fixed value (0x38 = 1, 0x40 = 2, 0x30 = 1/2) and
+    # every row scale is a different prime, so a scale taken from the wrong
+    # matrix, the wrong row or the wrong axis, a dropped bias or a routed
+    # tensor returned for the shared prefix changes some value
+    E, R, C = 2, 3, 4
+    s1 = np.array([[2, 3, 5], [7, 11, 13]], np.float32)
+    s3 = np.array([[17, 19, 23], [29, 31, 37]], np.float32)
+    s2 = np.array([[41, 43, 47, 53], [59, 61, 67, 71]], np.float32)
+    raw = {"w1": np.full((E, R, C), 0x38, np.uint8), "s1": s1,
+           "w3": np.full((E, R, C), 0x40, np.uint8), "s3": s3,
+           "w2": np.full((E, C, R), 0x30, np.uint8), "s2": s2,
+           "b1": np.array([[0.25, -0.5, 1.5], [2.0, -4.0, 8.0]], np.float32),
+           "b2": np.array([[1.0, 2.0, 3.0, 4.0], [-1.0, -2.0, -3.0, -4.0]], np.float32),
+           "sh_w1": np.full((1, R, C), 0x40, np.uint8), "sh_s1": np.array([[73, 79, 83]], np.float32),
+           "sh_w3": np.full((1, R, C), 0x38, np.uint8), "sh_s3": np.array([[89, 97, 101]], np.float32),
+           "sh_w2": np.full((1, C, R), 0x38, np.uint8), "sh_s2": np.array([[103, 107, 109, 113]], np.float32),
+           "sh_b1": None, "sh_b2": None}
+    w = O.decode_weights(raw, "fp8")
+    assert sorted(w) == ["b1", "b2", "w1", "w2", "w3"]
+    for e in range(E):
+        for r in range(R):
+            assert w["w1"][e, r].tolist() == [float(s1[e, r])] * C
+            assert w["w3"][e, r].tolist() == [2.0 * float(s3[e, r])] * C
+        for c in range(C):
+            assert w["w2"][e, c].tolist() == [0.5 * float(s2[e, c])] * R
+    assert w["b1"].tolist() == raw["b1"].astype(np.float64).tolist()
+    assert w["b2"].tolist() == raw["b2"].astype(np.float64).tolist()
+    sh = O.decode_weights(raw, "fp8", prefix="sh_")
+    assert sorted(sh) == ["w1", "w2", "w3"]
+    assert sh["w1"][0, :, 0].tolist() == [146.0, 158.0, 166.0]
+    assert sh["w3"][0, :, 0].tolist() == [89.0, 97.0, 101.0]
+    assert sh["w2"][0, :, 0].tolist() == [103.0, 107.0, 109.0, 113.0]
+
+
+@pytest.mark.parametrize("w_dtype", ["fp8", "bf16"])
+def test_decode_weights_returns_the_generators_draws_within_half_a_step(w_dtype):
+    # the workload generator's own float32 draws, drawn again from the same
+    # streams, against the decoded stored weights of each matrix (routed and
+    # shared): within half a step of the storage format at each value
+    import workloads as W
+    from workloads.gen import _draw, _rng
+
+    cfg = W.MoEConfig(name="dec", T=4, d=48, d_out=48, E=3, k=1, ffn="swiglu", d_ff=32, gate="prob", cf=None,
+                      n_shared=1, w_dtype=w_dtype, seed=7, w1_var=1 / 48, w3_var=4 / 48, w2_var=9 / 32)
+    arr = W.generate(cfg)
+    shapes = {"w1": (cfg.d_ff, cfg.d, cfg.w1_var), "w3": (cfg.d_ff, cfg.d, cfg.w3_var),
+              "w2": (cfg.d_out, cfg.d_ff, cfg.w2_var)}
+    for prefix, tag, n in (("", "", cfg.E), ("sh_", "s", cfg.n_shared)):
+        w = O.decode_weights(arr, w_dtype, prefix=prefix)
+        for name, (rows, cols, var) in shapes.items():
+            for e in range(n):
+                ref = _draw(_rng(cfg.seed, tag + name, e), (rows, cols), ("normal", var)).astype(np.float64)
+                got = w[name][e]
+                if w_dtype == "bf16":
+                    bound = np.abs(ref) * 2.0 ** -8          # half a bf16 step (8 significant bits)
+                else:
+                    s = np.max(np.abs(ref), axis=1, keepdims=True) / 448.0
+                    # e4m3 keeps 4 significant bits; below 2^-6 (times the
+                    # scale) the step is 2^-9: half of either
+                    bound = np.maximum(np.abs(ref) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-6)
+                assert np.all(np.abs(got - ref) <= bound), (prefix, name, e)
+
+
 def test_aux_loss_counts_assignments_before_capacity_drops():
     """P1 §3.4 takes the selection frequency from the top-k indices
     themselves, so capacity drops do not change f."""
@@ -535,33 +599,49 @@ def test_noisy_scale_is_the_floor_when_the_projection_is_very_negative():
     np.testing.assert_allclose(z - O.router_logits(x, w_g), noise * 1e-2, rtol=1e-12, atol=1e-24)
 
 
-def test_noisy_top1_matches_page_gate_module_written_in_torch():
-    # P5 代码实战, NoisyTop1Gate in training mode, with the normal draws
-    # passed in: softplus scale + 1e-2 times the draw added to the gate
-    # logits; softmax; arg-max as the expert; probs times its one-hot as the
-    # routing weights; balance loss E * sum(load * importance)
+def test_noisy_top1_gate_and_balance_loss_from_the_equations_by_scalar_loops():
+    # P2 §2.1: the noisy logit of expert e is the clean logit plus a standard
+    # normal draw times softplus of a second projection; P5 代码实战 gives that
+    # projection a bias and a 1e-2 floor, keeps the arg-max expert with its
+    # softmax probability as the weight (top-1, 'prob' gates); P5
+    # 负载均衡损失函数: loss = N * sum_i f_i P_i with f_i the share of tokens
+    # sent to i and P_i the mean router probability of i.  Every quantity is
+    # formed here one scalar at a time with the math module (dot products,
+    # ln(1 + e^u), exp, arg-max by comparison), independently of numpy.
     rng = np.random.default_rng(13)
-    T, d, E = 64, 16, 6
+    T, d, E = 12, 5, 4
     x = rng.standard_normal((T, d))
     w_g, b_g = rng.standard_normal((E, d)), rng.standard_normal(E)
     w_n, b_n = rng.standard_normal((E, d)) * 0.5, rng.standard_normal(E)
     noise = rng.standard_normal((T, E))
-    F = torch.nn.functional
-    xt = torch.from_numpy(x)
-    logits = F.linear(xt, torch.from_numpy(w_g), torch.from_numpy(b_g))
-    std = F.softplus(F.linear(xt, torch.from_numpy(w_n), torch.from_numpy(b_n)), threshold=50.0) + 1e-2
-    logits = logits + torch.from_numpy(noise) * std
-    probs = F.softmax(logits, dim=-1)
-    top = torch.argmax(logits, dim=-1)
-    mask = F.one_hot(top, num_classes=E).double()
-    route = probs * mask
-    aux = E * torch.sum(mask.mean(dim=0) * probs.mean(dim=0))
+    eps = 1e-2
+    want_idx, want_gate, prob_sum, load = [], [], [0.0] * E, [0] * E
+    for t in range(T):
+        z = []
+        for e in range(E):
+            clean = b_g[e] + sum(float(x[t, c]) * float(w_g[e, c]) for c in range(d))
+            u = b_n[e] + sum(float(x[t, c]) * float(w_n[e, c]) for c in range(d))
+            z.append(clean + float(noise[t, e]) * (math.log(1.0 + math.exp(u)) + eps))
+        best = 0
+        for e in range(1, E):
+            if z[e] > z[best]:
+                best = e
+        den = sum(math.exp(v) for v in z)
+        probs = [math.exp(v) / den for v in z]
+        want_idx.append(best)
+        want_gate.append(probs[best])
+        load[best] += 1
+        for e in range(E):
+            prob_sum[e] += probs[e]
+    want_loss = E * sum((load[e] / T) * (prob_sum[e] / T) for e in range(E))
 
-    r = O.noisy_router(x, w_g, b_g, w_n, b_n, noise, 1e-2, 1, "prob")
-    np.testing.assert_array_equal(r["topk_idx"][:, 0], top.numpy())
-    np.testing.assert_allclose(r["topk_gate"][:, 0], route.sum(dim=-1).numpy(), rtol=1e-12)
+    r = O.noisy_router(x, w_g, b_g, w_n, b_n, noise, eps, 1, "prob")
+    assert not r["near_tie"].any()
+    assert r["topk_idx"][:, 0].tolist() == want_idx
+    np.testing.assert_allclose(r["topk_gate"][:, 0], want_gate, rtol=1e-12)
+    np.testing.assert_allclose(r["prob_colsum"], prob_sum, rtol=1e-12)
     counts = np.bincount(r["topk_idx"][:, 0], minlength=E)
-    np.testing.assert_allclose(O.aux_loss(counts, r["prob_colsum"], T, 1, E, 1.0), aux.item(), rtol=1e-12)
+    assert O.aux_loss(counts, r["prob_colsum"], T, 1, E, 1.0) == pytest.approx(want_loss, rel=1e-12)
 
 
 # ---------------------------------------------------------------------------
