@@ -52,7 +52,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1,  /* bad shape, dtype, NULL or misaligned pointer, k outside [1, E] */
   MOE_ERR_UNSUPPORTED = -2,  /* valid combination that the library does not implement */
   MOE_ERR_HIP = -3,          /* a HIP launch failed; see moe_last_hip_error() */
-  MOE_ERR_WORKSPACE = -4     /* workspace NULL or smaller than *_workspace_size() */
+  MOE_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than *_workspace_size() */
+  MOE_ERR_SCRATCH_LIMIT = -5 /* the allocation-free call needs more than MOE_NOALLOC_SCRATCH_BYTES */
 } moe_status;
 
 typedef enum {
@@ -132,6 +133,27 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
                     int32_t* topk_idx, float* topk_gate, float* prob_colsum,
                     float* logits_dbg, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * ---- (a'') Router without a workspace, for callers that cannot allocate --------
+ * For callers that cannot call hipMalloc or pass a workspace (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same operation, arguments, outputs and errors as moe_router_topk, with its
+ * scratch (what moe_router_workspace_size reports) in a fixed device array
+ * of MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  The call allocates nothing.  A call whose scratch
+ * would exceed that size returns MOE_ERR_SCRATCH_LIMIT before any launch
+ * (the Mixtral-shaped router needs 8 KB, the DeepSeekMoE-shaped one about
+ * 4 MB; the 32768-token, 256-expert one does not fit).  Every call on one GPU
+ * shares that GPU's array: two calls that overlap in time on the same GPU
+ * (other streams or host threads) race; calls ordered on one stream do not.
+ * The first call on a device looks up the array's address on it.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int moe_router_topk_noalloc(const void* x, int x_dt, const float* w_g, const float* b_g,
+                            int T, int d, int E, int k, int gate_mode,
+                            int32_t* topk_idx, float* topk_gate, float* prob_colsum,
+                            float* logits_dbg, hipStream_t stream);
 
 /*
  * ---- (a') Router with noisy gating (training mode) ---------------------------

@@ -27,7 +27,9 @@ CAP_CEIL, CAP_FLOOR = 0, 1
 # moe_row_mode
 ROWS_PACKED, ROWS_SHARED = 0, 1
 # moe_status
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE, ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5
+# fixed scratch of the allocation-free router (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 GATE_MODES = {"prob": GATE_PROB, "renorm": GATE_RENORM}
 CAP_ROUNDS = {"ceil": CAP_CEIL, "floor": CAP_FLOOR}
@@ -45,6 +47,7 @@ _SIGS = {
     "moe_capacity": (_i, [_i, _i, _i, ctypes.c_double, _i]),
     "moe_router_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_router_topk": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_router_topk_noalloc": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "moe_router_noisy_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_router_topk_noisy": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
@@ -151,6 +154,17 @@ def router_topk(x, w_g, b_g, k, gate_mode, topk_idx, topk_gate, prob_colsum=None
                                _p(topk_idx), _p(topk_gate), _p(prob_colsum), _p(logits_dbg),
                                _p(workspace), ws_bytes, _stream(stream))
     _check("moe_router_topk", st)
+
+
+def router_topk_noalloc(x, w_g, b_g, k, gate_mode, topk_idx, topk_gate, prob_colsum=None, logits_dbg=None,
+                        stream=None):
+    """moe_router_topk_noalloc: moe_router_topk with the library's fixed scratch."""
+    T, d = x.shape
+    E = w_g.shape[0]
+    st = lib().moe_router_topk_noalloc(_p(x), dtype_code(x), _p(w_g), _p(b_g), T, d, E, k, gate_mode,
+                                       _p(topk_idx), _p(topk_gate), _p(prob_colsum), _p(logits_dbg),
+                                       _stream(stream))
+    _check("moe_router_topk_noalloc", st)
 
 
 def router_noisy_workspace_size(T, d, E, x_dt) -> int:

@@ -19,6 +19,9 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid but unimplemented combination";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed (see moe_last_hip_error)";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "MOE_ERR_SCRATCH_LIMIT: the call needs more scratch than the allocation-free entry point's fixed "
+             "MOE_NOALLOC_SCRATCH_BYTES";
     default: return "unknown moe_status";
   }
 }

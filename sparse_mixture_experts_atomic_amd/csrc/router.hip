@@ -6,7 +6,16 @@
 // P3 §3.1 (keep the k largest, optionally renormalised).
 #include <math.h>
 
+#include <mutex>
+
 #include "moe_internal.hpp"
+
+// Scratch of moe_router_topk_noalloc: the per-block probability column sums
+// and (more than 8 experts) the partial logits, in a fixed device array
+// instead of a caller workspace.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code this name is only a stand-in
+// for the symbol: the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace moe {
 namespace {
@@ -920,6 +929,34 @@ inline bool workspace_ok(int T, const float* prob_colsum, const void* workspace,
   return true;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept for later calls.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return MOE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      record_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return MOE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -945,6 +982,22 @@ int moe_router_topk(const void* x, int x_dt, const float* w_g, const float* b_g,
     return MOE_ERR_WORKSPACE;
   return router_run(x, x_dt, w_g, b_g, nullptr, nullptr, nullptr, 0.f, T, d, E, k, gate_mode, topk_idx, topk_gate,
                     prob_colsum, logits_dbg, workspace, stream);
+}
+
+int moe_router_topk_noalloc(const void* x, int x_dt, const float* w_g, const float* b_g, int T, int d, int E,
+                            int k, int gate_mode, int32_t* topk_idx, float* topk_gate, float* prob_colsum,
+                            float* logits_dbg, hipStream_t stream) {
+  int st = router_check(x, x_dt, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, prob_colsum, logits_dbg);
+  if (st != MOE_OK) return st;
+  // the scratch this call needs is what moe_router_topk takes as workspace;
+  // every byte the kernels read from it is written first in the same call
+  if (moe_router_workspace_size(T, d, E, x_dt) > static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES))
+    return MOE_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != MOE_OK) return st;
+  return router_run(x, x_dt, w_g, b_g, nullptr, nullptr, nullptr, 0.f, T, d, E, k, gate_mode, topk_idx, topk_gate,
+                    prob_colsum, logits_dbg, ws, stream);
 }
 
 size_t moe_router_noisy_workspace_size(int T, int d, int E, int x_dt) {

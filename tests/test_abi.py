@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     lib = L.lib()
     assert lib.moe_abi_version() == 1
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert lib.moe_status_string(st).decode().startswith("MOE_")
     assert lib.moe_last_hip_error() == 0
 
@@ -79,6 +79,28 @@ def test_router_validation_before_launch():
     assert lib.moe_router_topk(fake, L.BF16, fake, None, 8, 12, 4, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_INVALID_ARG
     assert lib.moe_router_topk(fake, L.BF16, fake, None, 8, 16, 4, 2, 0, fake, fake, None, None, None, 0, None) == L.ERR_WORKSPACE
     assert lib.moe_router_topk(fake, L.BF16, fake, None, 8, 16, 512, 2, 0, fake, fake, None, None, fake, 1 << 20, None) == L.ERR_UNSUPPORTED
+
+
+def test_noalloc_router_validation_and_scratch_limit_before_launch():
+    lib = L.lib()
+    fake = 1 << 20    # never dereferenced: validation fails first
+    f = lib.moe_router_topk_noalloc
+
+    def call(x=fake, dt=L.BF16, wg=fake, T=8, d=16, E=4, k=2, mode=0):
+        return f(x, dt, wg, None, T, d, E, k, mode, fake, fake, fake, None, None)
+
+    assert call(k=5) == L.ERR_INVALID_ARG
+    assert call(wg=None) == L.ERR_INVALID_ARG
+    assert call(x=fake + 4) == L.ERR_INVALID_ARG
+    assert call(d=12) == L.ERR_INVALID_ARG
+    assert call(E=512) == L.ERR_UNSUPPORTED
+    # the 32768-token, 256-expert router needs more than the fixed scratch:
+    # refused on the host, before any device call
+    assert L.router_workspace_size(32768, 7168, 256, L.BF16) > L.NOALLOC_SCRATCH_BYTES
+    assert call(T=32768, d=7168, E=256, k=8) == L.ERR_SCRATCH_LIMIT
+    # the Mixtral- and DeepSeekMoE-shaped routers fit
+    assert L.router_workspace_size(4096, 4096, 8, L.BF16) <= L.NOALLOC_SCRATCH_BYTES
+    assert L.router_workspace_size(4096, 2048, 64, L.BF16) <= L.NOALLOC_SCRATCH_BYTES
 
 
 def test_noisy_router_validation_before_launch():
