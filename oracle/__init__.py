@@ -1,4 +1,5 @@
-"""CPU oracle (float64) for the sparse MoE layer forward pass.
+"""CPU oracle (float64) for the sparse MoE layer: the forward pass
+(moe_oracle) and its gradients (moe_backward, imported as a submodule).
 
 TEST INFRASTRUCTURE ONLY: imported by tests, by the smoke check and by the
 CPU-baseline leg of the benchmark, never by the product library.
