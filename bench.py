@@ -117,6 +117,7 @@ def main():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training-step (forward + backward) leg")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration) and exit")
     args = ap.parse_args()
@@ -281,6 +282,57 @@ def main():
                 "note": "routed FFN reads x through perm_token (moe_expert_ffn_gathered); dispatch copies no rows"}
     del glayer
 
+    # timed region 5 (last): training steps, forward + backward of a layer
+    # instance that keeps the router logits; dy is a fixed seeded draw.  The
+    # FFN backward's algorithmic FLOPs are twice the forward's per kept row
+    # (dgrad and wgrad of every matrix); the fp32 recompute of the first
+    # layer's pre-activations is not counted.
+    backward = None
+    if not args.no_backward and cfg.act_dtype == "bf16" and cfg.w_dtype == "bf16":
+        blayer = MoELayer(**lkw)
+        blayer.enable_backward()
+        gen = torch.Generator(device="cpu").manual_seed(1234)
+        dy = torch.randn((cfg.T, cfg.d_out), generator=gen).to(torch.bfloat16).to("cuda")
+        for _ in range(min(args.warmup, 5)):
+            blayer.forward(x)
+            blayer.backward(x, dy)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            blayer.forward(x)
+            blayer.backward(x, dy)
+        stop.record()
+        torch.cuda.synchronize()
+        ms_train = start.elapsed_time(stop) / args.steps
+        bst = ["combine", "experts", "shared", "router", "permute"]
+        bev = {s_: [] for s_ in bst}
+        for _ in range(args.steps):
+            blayer.forward(x)
+            m = [torch.cuda.Event(enable_timing=True) for _ in range(len(bst) + 1)]
+            m[0].record()
+            blayer.backward_combine(dy)
+            m[1].record()
+            blayer.backward_experts()
+            m[2].record()
+            blayer.backward_shared(x, dy)
+            m[3].record()
+            blayer.backward_router(x)
+            m[4].record()
+            blayer.backward_permute(dy)
+            m[5].record()
+            for i, s_ in enumerate(bst):
+                bev[s_].append((m[i], m[i + 1]))
+        torch.cuda.synchronize()
+        bms = {s_: float(np.median([a_.elapsed_time(b_) for a_, b_ in bev[s_]])) for s_ in bst}
+        kept = int(blayer.offsets[-1].item())
+        bwd_flops = 2.0 * ffn_flops_per_row(cfg) * kept
+        backward = {"ms_per_train_step": ms_train, "train_tokens_per_s": cfg.T / (ms_train * 1e-3),
+                    "stages_ms": bms, "ffn_bwd_flops": bwd_flops,
+                    "ffn_bwd_tflops": bwd_flops / (bms["experts"] * 1e-3) / 1e12,
+                    "note": "forward + backward (moe_combine_backward, moe_expert_ffn_grouped_backward, "
+                            "moe_router_backward, moe_permute_backward); stage medians with HIP events between them"}
+        del blayer
+
     a_kept = int(layer.offsets[-1].item())
     ffn_flops = ffn_flops_per_row(cfg) * a_kept
     sh_flops = ffn_flops_per_row(cfg) * cfg.T * cfg.n_shared
@@ -320,6 +372,7 @@ def main():
         "stages_hbm_frac_loop": {k_: byts[k_] / (loop_st_ms[k_] * 1e-3) / 1e9 / PEAK_HBM_GBPS
                                  for k_ in ("router", "dispatch", "combine", "router_noisy")},
         "shared_tflops": (sh_flops / (st_ms["shared"] * 1e-3) / 1e12) if cfg.n_shared else None,
+        "backward": backward,
         "kept_rows": a_kept,
         "cold": {
             "note": "median step with a 512 MB scratch write before each step (no input in the last-level cache)",

@@ -331,6 +331,111 @@ int moe_combine(const void* y_rows, int dt, const int32_t* dest_pos, const float
 int moe_aux_loss(const int32_t* counts_routed, const float* prob_colsum, int T, int k, int E,
                  float alpha, float* loss, hipStream_t stream);
 
+/*
+ * ==== Backward pass (training) ==================================================
+ * Gradients of L = <dy, y> + daux * aux for the forward layer above, given
+ * the layer-output gradient dy [T, d_out] and the aux-loss gradient daux.
+ * P1 §4.3: the output is accumulated into zeros (index_add_), so each token's
+ * gradient goes back to exactly the expert rows it came from, and the top-k
+ * weight normalisation stays inside the graph; P1 §3.5: the training step
+ * differentiates task loss + coef * aux loss; P3 §2.2: the router's gradient
+ * comes back through the selected experts only; P5 负载均衡损失函数: f_i is
+ * discrete and carries no gradient, P_i does.  The top-k selection and the
+ * capacity drops are piecewise constant and pass no gradient.
+ * Order of the calls: moe_combine_backward -> moe_expert_ffn_grouped_backward
+ * (routed experts on the packed rows with the dYe rows; shared experts on x
+ * with dy itself, MOE_ROWS_SHARED) -> moe_router_backward ->
+ * moe_permute_backward.  Same conventions as the forward calls (device
+ * pointers, caller workspaces, asynchronous, validated before any launch).
+ * Reductions run in a fixed order: results are reproducible bit for bit.
+ */
+
+/*
+ * Combine backward.  For each kept slot (dest_pos[t,j] >= 0):
+ *   dy_rows[dest_pos[t,j]] = topk_gate[t,j] * dy[t]       (dt, rounded once)
+ *   dgate[t,j]             = sum_c dy[t,c] * y_rows[dest_pos[t,j],c]  (fp32)
+ * and dgate[t,j] = 0 for a dropped slot.  The gradient of each shared
+ * expert's output and of the residual is dy itself.
+ *   dy, y_rows  [T, d_out], [*, d_out] in dt (MOE_F32 or MOE_BF16)
+ *   dy_rows     [*, d_out] out, dt: rows not referenced are left untouched
+ *   dgate       [T, k] fp32 out
+ * d_out must be a multiple of 8 (bf16) or 4 (fp32), else MOE_ERR_UNSUPPORTED.
+ */
+int moe_combine_backward(const void* dy, int dt, const void* y_rows, const int32_t* dest_pos,
+                         const float* topk_gate, int T, int k, int d_out, void* dy_rows, float* dgate,
+                         hipStream_t stream);
+
+/*
+ * Grouped expert FFN backward: for each segment (the rows routed to expert
+ * e; MOE_ROWS_SHARED as in moe_expert_ffn_grouped), with X the segment's
+ * input rows and dY their output gradients:
+ *   LINEAR  y = W1 x + b1:             dX = dY W1, dW1 = dY^T X, db1 = sum dY
+ *   RELU / GELU  h = W1 x + b1, a = act(h), y = W2 a + b2:
+ *           dW2 = dY^T a, db2 = sum dY, dh = (dY W2) act'(h), dW1 = dh^T X,
+ *           db1 = sum dh, dX = dh W1
+ *   SWIGLU  h1 = W1 x, h3 = W3 x, a = silu(h1) h3, y = W2 a:
+ *           da = dY W2, dh1 = da h3 silu'(h1), dh3 = da silu(h1),
+ *           dW2 = dY^T a, dW1 = dh1^T X, dW3 = dh3^T X, dX = dh1 W1 + dh3 W3
+ * h1, h3 (h) are recomputed from X and kept in fp32 (the derivatives of
+ * SiLU and GELU have roots, where a bf16 pre-activation would only be
+ * absolutely accurate); dh1, dh3 and a are rounded to bf16 between the
+ * matrix products; the weight gradients accumulate in fp32 over the
+ * segment's rows.
+ *   x_rows   [max_rows, d] (PACKED) or [T, d] (SHARED), bf16
+ *   dy_rows  [max_rows, d_out] (PACKED: the dy_rows of moe_combine_backward)
+ *            or [T, d_out] (SHARED: dy), bf16
+ *   dx_rows  [max_rows, d] out, bf16 (PACKED and SHARED alike: row r of the
+ *            packed batch; shared expert s writes rows s T .. s T + T - 1)
+ *   dw1      [E, rows of w1, d] fp32 out; dw3 [E, d_ff, d] (SWIGLU only);
+ *   dw2      [E, d_out, d_ff] (two-layer kinds); db1, db2 [E, *] fp32, given
+ *            exactly when b1, b2 are
+ * bf16 activations and weights only (else MOE_ERR_UNSUPPORTED); d, d_ff and
+ * d_out multiples of 8.  An expert with no rows gets zero gradients.
+ */
+size_t moe_ffn_backward_workspace_size(int kind, int max_rows, int E, int d, int d_ff, int d_out);
+int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
+                                    const int32_t* offsets, int E, int d, int d_ff, int d_out,
+                                    const void* w1, const void* w3, const void* w2, int w_dt,
+                                    const float* b1, const float* b2, const void* dy_rows, void* dx_rows,
+                                    float* dw1, float* dw3, float* dw2, float* db1, float* db2,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Router backward.  From the forward's fp32 logits z [T, E] (logits_dbg of
+ * moe_router_topk), its top-k ids and gates and the gate gradients dgate of
+ * moe_combine_backward, per token in fp32: p = softmax(z); the gate
+ * gradient dp (MOE_GATE_PROB: dp[S_j] += dgate_j; MOE_GATE_RENORM: dp[S_j]
+ * += (dgate_j - sum_i dgate_i gate_i) / sum_i p[S_i]); the balance loss
+ * alpha E sum_e f_e P_e adds daux alpha E f_e / T to dp[e] of every token
+ * (f_e = counts_routed[e] / (T k), constant); dz = p (dp - sum_e p dp).
+ * Then dW_g = dz^T x and db_g = sum_t dz (token slices summed in fp32, the
+ * slices in fp64, in order).  The input gradient dz W_g is added by
+ * moe_permute_backward.
+ *   dz    [T, E] fp32 out;  dw_g [E, d] fp32 out;  db_g [E] fp32 out or NULL
+ * E <= 256 (else MOE_ERR_UNSUPPORTED).  T == 0 writes zero dw_g and db_g.
+ */
+size_t moe_router_backward_workspace_size(int T, int d, int E);
+int moe_router_backward(const void* x, int x_dt, const float* logits, const int32_t* topk_idx,
+                        const float* topk_gate, const float* dgate, const int32_t* counts_routed,
+                        int T, int d, int E, int k, int gate_mode, float alpha, float daux,
+                        float* dz, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * Permute backward (the transpose of Xp[dest_pos[t,j]] = x[t]) plus the other
+ * paths into x, summed in fp32 in this order:
+ *   dx[t] = sum_{j kept} dx_rows[dest_pos[t,j]] + sum_{s < n_shared} dx_shared[s, t]
+ *           + dres[t] + sum_e dz[t,e] w_g[e, :]
+ *   dx_rows    [*, d] dt (moe_expert_ffn_grouped_backward of the routed experts)
+ *   dx_shared  [n_shared, T, d] dt or NULL (the shared experts' dx_rows)
+ *   dres       [T, d] dt or NULL (dy when the layer adds the residual)
+ *   dz, w_g    [T, E], [E, d] fp32, or dz NULL (no router term)
+ *   dx         [T, d] out, dt
+ */
+int moe_permute_backward(const void* dx_rows, int dt, const int32_t* dest_pos, int T, int k, int d,
+                         const void* dx_shared, int n_shared, const void* dres, const float* dz,
+                         const float* w_g, int E, void* dx, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

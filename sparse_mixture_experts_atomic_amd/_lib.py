@@ -60,6 +60,14 @@ _SIGS = {
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp]),
     "moe_aux_loss": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp]),
+    "moe_combine_backward": (_i, [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_ffn_backward_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "moe_expert_ffn_grouped_backward": (_i, [_i, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_router_backward_workspace_size": (_sz, [_i, _i, _i]),
+    "moe_router_backward": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _vp, _vp, _vp,
+                                 _vp, _sz, _vp]),
+    "moe_permute_backward": (_i, [_vp, _i, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp]),
 }
 
 _lib = None
@@ -225,3 +233,51 @@ def aux_loss(counts_routed, prob_colsum, T, k, E, alpha, loss, stream=None):
     st = lib().moe_aux_loss(_p(counts_routed), _p(prob_colsum), T, k, E, float(alpha), _p(loss),
                             _stream(stream))
     _check("moe_aux_loss", st)
+
+
+# ---------------------------------------------------------------- backward
+
+
+def combine_backward(dy, y_rows, dest_pos, topk_gate, dy_rows, dgate, stream=None):
+    T, k = dest_pos.shape
+    st = lib().moe_combine_backward(_p(dy), dtype_code(dy), _p(y_rows), _p(dest_pos), _p(topk_gate), T, k,
+                                    dy.shape[1], _p(dy_rows), _p(dgate), _stream(stream))
+    _check("moe_combine_backward", st)
+
+
+def ffn_backward_workspace_size(kind, max_rows, E, d, d_ff, d_out) -> int:
+    return lib().moe_ffn_backward_workspace_size(kind, max_rows, E, d, d_ff, d_out)
+
+
+def expert_ffn_grouped_backward(kind, x_rows, max_rows, row_mode, offsets, E, d, d_ff, d_out, w1, w3, w2, b1, b2,
+                                dy_rows, dx_rows, dw1, dw3, dw2, db1, db2, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().moe_expert_ffn_grouped_backward(kind, _p(x_rows), dtype_code(x_rows), max_rows, row_mode, _p(offsets),
+                                               E, d, d_ff, d_out, _p(w1), _p(w3), _p(w2), dtype_code(w1), _p(b1),
+                                               _p(b2), _p(dy_rows), _p(dx_rows), _p(dw1), _p(dw3), _p(dw2), _p(db1),
+                                               _p(db2), _p(workspace), ws_bytes, _stream(stream))
+    _check("moe_expert_ffn_grouped_backward", st)
+
+
+def router_backward_workspace_size(T, d, E) -> int:
+    return lib().moe_router_backward_workspace_size(T, d, E)
+
+
+def router_backward(x, logits, topk_idx, topk_gate, dgate, counts_routed, gate_mode, alpha, daux, dz, dw_g, db_g,
+                    workspace, stream=None):
+    T, d = x.shape
+    E = logits.shape[1]
+    k = topk_idx.shape[1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().moe_router_backward(_p(x), dtype_code(x), _p(logits), _p(topk_idx), _p(topk_gate), _p(dgate),
+                                   _p(counts_routed), T, d, E, k, gate_mode, float(alpha), float(daux), _p(dz),
+                                   _p(dw_g), _p(db_g), _p(workspace), ws_bytes, _stream(stream))
+    _check("moe_router_backward", st)
+
+
+def permute_backward(dx_rows, dest_pos, d, dx_shared, n_shared, dres, dz, w_g, dx, stream=None):
+    T, k = dest_pos.shape
+    E = w_g.shape[0] if w_g is not None else 0
+    st = lib().moe_permute_backward(_p(dx_rows), dtype_code(dx_rows), _p(dest_pos), T, k, d, _p(dx_shared), n_shared,
+                                    _p(dres), _p(dz), _p(w_g), E, _p(dx), _stream(stream))
+    _check("moe_permute_backward", st)

@@ -98,7 +98,13 @@ int launch_f32(const float* in, int in_shared, const int32_t* gather, int n_src,
 
 inline int m_tiles_max(int max_rows, int E) { return (max_rows + kGemmBM - 1) / kGemmBM + E; }
 
-// compute units of the current device (0 if it cannot be queried)
+int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode, const int32_t* gather,
+            int n_src, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1, const void* w3,
+            const void* w2, int w_dt, const float* s1, const float* s3, const float* s2, const float* b1,
+            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+}  // namespace
+
 int current_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -106,12 +112,11 @@ int current_cu_count() {
   return n;
 }
 
-int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode, const int32_t* gather,
-            int n_src, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1, const void* w3,
-            const void* w2, int w_dt, const float* s1, const float* s3, const float* s2, const float* b1,
-            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* ts, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, bm, ts);
+  return check_launch();
+}
 
-}  // namespace
 }  // namespace moe
 
 using namespace moe;
@@ -225,8 +230,7 @@ int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode
                                  Y, max_rows, stream);
   }
 
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, kGemmBM, ts);
-  int st = check_launch();
+  int st = launch_tile_map(offsets, E, kGemmBM, ts, stream);
   if (st != MOE_OK) return st;
   const int mtm = m_tiles_max(max_rows, E);
 

@@ -137,4 +137,58 @@ constexpr int kGemmSplitMax = 4;
 // Enqueues C = epi(A B^T) per segment.  m_tiles_max bounds ts[E] from above.
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream);
 
+// ts[e] = sum over e' < e of ceil(segment length / bm), ts[E] the total (one
+// block, E <= 1024)
+int launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* ts, hipStream_t stream);
+
+// compute units of the current device (0 if it cannot be queried)
+int current_cu_count();
+
+// ------------------------------------------- backward grouped GEMMs
+
+enum { BWD_EPI_STORE = 0, BWD_EPI_SWIGLU = 1, BWD_EPI_RELU = 2, BWD_EPI_GELU = 3 };
+enum { BWD_DGRAD = 0, BWD_WGRAD = 1, BWD_FWD = 2 };
+
+// One grouped GEMM of the FFN backward (bwd_gemm.hip).  C(m, n) = sum_k
+// A(m, k) B(n, k) with
+//   dgrad (segments on M, rows of the packed batch; tile map ts of 128-row
+//          tiles): A(m, k) = A[m * lda + k] (k < K1) or A2[m * lda + k - K1],
+//          B(n, k) = B_e[k * ldb + n] (k < K1) or B2_e[(k - K1) * ldb + n],
+//          B_e = B + e * b_estride; epilogue per BWD_EPI_* into O1/O2/O3
+//          (bf16 [rows, N], row pitch ldc), reading H1/H3 at the same place;
+//   wgrad (segments on K, one M x N output per expert): A(m, k) =
+//          A[k * lda + m], B(n, k) = B[k * ldb + n], k over the segment's
+//          rows; fp32 output Cf + e * c_estride, row pitch ldc;
+//   fwd    (segments on M, forward layout): A(m, k) = A[m * lda + k],
+//          B(n, k) = B_e[n * ldb + k]; fp32 output Cf (+ bias[e, n]).
+// a_shared / b_shared: the operand's segment e starts at row 0 (shared
+// experts: every segment is the same token batch).
+struct BwdGemmParams {
+  const uint16_t* A;
+  const uint16_t* A2;
+  long lda;
+  int a_shared;
+  const uint16_t* B;
+  const uint16_t* B2;
+  long ldb;
+  long b_estride;
+  int b_shared;
+  int M, N, K, K1;
+  const int32_t* offsets;
+  const int32_t* ts;
+  int E;
+  float* Cf;
+  long ldc;
+  long c_estride;
+  const float* bias;
+  const float* H1;
+  const float* H3;
+  uint16_t* O1;
+  uint16_t* O2;
+  uint16_t* O3;
+};
+constexpr int kBwdBM = 128;   // rows per m-tile of the dgrad tile map
+
+int launch_bwd_gemm(int mode, int epi, const BwdGemmParams& p, int m_tiles_max, hipStream_t stream);
+
 }  // namespace moe

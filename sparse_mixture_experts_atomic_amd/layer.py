@@ -46,6 +46,8 @@ class MoELayer:
         self.y_rows = torch.empty((max(A, 1), d_out), dtype=act_dtype, device=dev)
         self.y = torch.empty((T, d_out), dtype=act_dtype, device=dev)
         self.loss = torch.empty((1,), **f32)
+        # training: the router keeps its fp32 logits for the backward pass
+        self.logits = None
         act = L.F32 if act_dtype == torch.float32 else L.BF16
         self.ws_router = self._ws(L.router_workspace_size(T, d, E, act), dev)
         self.ws_disp = self._ws(L.dispatch_workspace_size(T, k, E), dev)
@@ -64,7 +66,7 @@ class MoELayer:
     # individual stages (the tests drive them one at a time) ----------------
     def router(self, x):
         L.router_topk(x, self.w["w_g"], self.w.get("b_g"), self.k, self.gate, self.topk_idx, self.topk_gate,
-                      self.prob_colsum, None, self.ws_router)
+                      self.prob_colsum, self.logits, self.ws_router)
 
     def router_noisy(self, x, w_n, b_n, noise, eps=1e-2):
         """Training-mode router with noisy gating: the same outputs as router(),
@@ -112,6 +114,74 @@ class MoELayer:
 
     def aux(self):
         L.aux_loss(self.counts_routed, self.prob_colsum, self.T, self.k, self.E, self.alpha, self.loss)
+
+    # ---------------------------------------------------------------- training
+    def enable_backward(self):
+        """Allocate what the backward pass needs (the forward then also keeps
+        the router logits); gradients land in self.grad after backward()."""
+        if self.logits is not None:
+            return
+        dev = self.topk_idx.device
+        T, d, E, k, A = self.T, self.d, self.E, self.k, self.T * self.k
+        f32 = dict(dtype=torch.float32, device=dev)
+        act = self.act_dtype
+        self.logits = torch.empty((T, E), **f32)
+        self.dgate = torch.empty((T, k), **f32)
+        self.dz = torch.empty((T, E), **f32)
+        self.dy_rows = torch.empty((max(A, 1), self.d_out), dtype=act, device=dev)
+        self.dx_rows = torch.empty((max(A, 1), d), dtype=act, device=dev)
+        self.dx = torch.empty((T, d), dtype=act, device=dev)
+        self.ws_rbwd = self._ws(L.router_backward_workspace_size(T, d, E), dev)
+        self.ws_fbwd = self._ws(L.ffn_backward_workspace_size(self.kind, A, E, d, self.d_ff, self.d_out), dev)
+        g = {"w_g": torch.empty((E, d), **f32), "b_g": torch.empty((E,), **f32)}
+        for pre in ("", "sh_"):
+            for n in ("w1", "w3", "w2", "b1", "b2"):
+                t = self.w.get(pre + n)
+                if t is not None:
+                    g[pre + n] = torch.empty(t.shape, **f32)
+        self.grad = g
+        if self.n_shared:
+            self.dx_shared = torch.empty((self.n_shared, T, d), dtype=act, device=dev)
+            self.ws_sbwd = self._ws(L.ffn_backward_workspace_size(self.kind, self.n_shared * T, self.n_shared, d,
+                                                                  self.d_ff, self.d_out), dev)
+
+    def backward_combine(self, dy):
+        L.combine_backward(dy, self.y_rows, self.dest_pos, self.topk_gate, self.dy_rows, self.dgate)
+
+    def backward_experts(self):
+        w, g = self.w, self.grad
+        L.expert_ffn_grouped_backward(self.kind, self.x_perm, self.T * self.k, L.ROWS_PACKED, self.offsets, self.E,
+                                      self.d, self.d_ff, self.d_out, w["w1"], w.get("w3"), w.get("w2"), w.get("b1"),
+                                      w.get("b2"), self.dy_rows, self.dx_rows, g["w1"], g.get("w3"), g.get("w2"),
+                                      g.get("b1"), g.get("b2"), self.ws_fbwd)
+
+    def backward_shared(self, x, dy):
+        if not self.n_shared:
+            return
+        w, g = self.w, self.grad
+        L.expert_ffn_grouped_backward(self.kind, x, self.n_shared * self.T, L.ROWS_SHARED, self.sh_offsets,
+                                      self.n_shared, self.d, self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"),
+                                      w.get("sh_w2"), w.get("sh_b1"), w.get("sh_b2"), dy, self.dx_shared, g["sh_w1"],
+                                      g.get("sh_w3"), g.get("sh_w2"), g.get("sh_b1"), g.get("sh_b2"), self.ws_sbwd)
+
+    def backward_router(self, x, daux=1.0):
+        L.router_backward(x, self.logits, self.topk_idx, self.topk_gate, self.dgate, self.counts_routed, self.gate,
+                          self.alpha, daux, self.dz, self.grad["w_g"], self.grad["b_g"], self.ws_rbwd)
+
+    def backward_permute(self, dy=None, residual=False):
+        L.permute_backward(self.dx_rows, self.dest_pos, self.d, self.dx_shared if self.n_shared else None,
+                           self.n_shared, dy if residual else None, self.dz, self.w["w_g"], self.dx)
+
+    def backward(self, x, dy, daux=1.0, residual=False):
+        """Gradients of <dy, y> + daux * aux for the last forward(x) (which
+        must have run after enable_backward()); returns dx, fills self.grad.
+        The gradient of b_g is kept whether or not the router has a bias."""
+        self.backward_combine(dy)
+        self.backward_experts()
+        self.backward_shared(x, dy)
+        self.backward_router(x, daux)
+        self.backward_permute(dy, residual)
+        return self.dx
 
     def forward(self, x, residual=None):
         """Whole layer; returns (y, aux loss tensor).  Asynchronous."""
