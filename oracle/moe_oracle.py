@@ -436,6 +436,81 @@ def dense_moe(x: np.ndarray, w_g: np.ndarray, b_g: Optional[np.ndarray], kind: s
 
 
 # ---------------------------------------------------------------------------
+# fp8 activations (expert inputs and hidden layer quantised per row)
+# ---------------------------------------------------------------------------
+# P2's deployment paragraph quantises the expert weights to int8; P3 §4.2
+# runs the experts in INT4 and keeps the router in FP16.  The pages fix the
+# principle (quantise the experts, keep the router precise), not a format.
+# Readings taken: the e4m3 format of the stored weights (OCP E4M3FN) for the
+# expert inputs too, one fp32 scale per row (per token) set so that the row's
+# largest magnitude maps to 448, the format's largest finite value, exactly
+# as the weights are scaled per output row; the hidden layer of a two-layer
+# expert is rounded to bf16 (the kernel's precision for that value) and then
+# quantised per row the same way before the second matrix.
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Values rounded to fp32, then to bf16 (nearest, ties to the even
+    pattern), returned as float64."""
+    u = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32)).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+_E4M3_POS = E4M3_TABLE[:127]          # codes 0x00..0x7E: 0 .. 448, increasing
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """fp32 values -> OCP E4M3FN codes: the nearest finite value, ties to the
+    code with an even mantissa, magnitudes past 448 to 448; the sign bit is
+    that of the input (so -0.0 and negatives that round to 0 give 0x80)."""
+    v = np.asarray(v, np.float32).astype(np.float64)
+    mag = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, mag, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = mag - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - mag
+    code = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(hi % 2 == 0, hi, lo)))
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_rows_e4m3(x: np.ndarray):
+    """Per-row quantisation of fp32-representable values: scale s = amax / 448
+    in fp32 (1 for an all-zero row), codes = e4m3_round(x / s) with the
+    division in fp32.  Returns (codes [rows, cols] uint8, s [rows] fp32)."""
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return e4m3_round(x32 / s[:, None]), s
+
+
+def dequantize_rows_e4m3(codes: np.ndarray, s: np.ndarray) -> np.ndarray:
+    return e4m3_to_f64(codes) * np.asarray(s, np.float32).astype(np.float64)[:, None]
+
+
+def expert_ffn_fp8(kind: str, codes: np.ndarray, s: np.ndarray, w1: np.ndarray, w3: Optional[np.ndarray] = None,
+                   w2: Optional[np.ndarray] = None) -> np.ndarray:
+    """One expert on per-row e4m3 inputs (codes, scales), float64 weights:
+    the first matrix on the dequantised rows, the activation, the hidden
+    layer rounded to bf16 and quantised per row, the second matrix on the
+    dequantised hidden rows.  No biases."""
+    xh = dequantize_rows_e4m3(codes, s)
+    h = xh @ w1.T
+    if kind == "linear":
+        return h
+    if kind == "relu":
+        h = np.maximum(h, 0.0)
+    elif kind == "gelu":
+        h = gelu(h)
+    elif kind == "swiglu":
+        h = silu(h) * (xh @ w3.T)
+    else:
+        raise ValueError(kind)
+    hq, hs = quantize_rows_e4m3(bf16_round(h))
+    return dequantize_rows_e4m3(hq, hs) @ w2.T
+
+
+# ---------------------------------------------------------------------------
 # whole layer
 # ---------------------------------------------------------------------------
 

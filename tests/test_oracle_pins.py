@@ -677,3 +677,106 @@ def test_gelu_expert_matches_torch_functional():
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
     u = rng.standard_normal(200) * 5
     np.testing.assert_allclose(O.gelu(u), F.gelu(torch.from_numpy(u)).numpy(), rtol=1e-13, atol=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# fp8 activations: per-row e4m3 quantisation (readings in the oracle)
+# ---------------------------------------------------------------------------
+
+
+def _e4m3_probe_values():
+    rng = np.random.default_rng(51)
+    pos = O.E4M3_TABLE[:127]
+    mids = (pos[1:] + pos[:-1]) / 2                     # every tie between neighbours
+    near = np.concatenate([mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20)])
+    rand = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 4000))
+    v = np.concatenate([pos, mids, near, rand, [0.0, 2.0 ** -10, 3 * 2.0 ** -10, 447.9, 448.0]])
+    v = np.concatenate([v, -v]).astype(np.float32)
+    return v
+
+
+def test_e4m3_rounding_matches_torch_conversion():
+    v = _e4m3_probe_values()
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_round(v)
+    assert np.array_equal(got, ref)
+    # past the largest finite value: saturation (torch's fn format has no inf)
+    assert O.e4m3_round(np.array([449.0, 1e6, -3e4], np.float32)).tolist() == [0x7E, 0x7E, 0xFE]
+
+
+def test_e4m3_rounding_is_the_nearest_code_by_brute_force():
+    v = _e4m3_probe_values()[::7].astype(np.float64)
+    codes = O.e4m3_round(v)
+    finite = np.array([c for c in range(256) if not np.isnan(O.E4M3_TABLE[c])])
+    vals = O.E4M3_TABLE[finite]
+    for x, c in zip(v, codes):
+        d = np.abs(vals - min(max(x, -448.0), 448.0))
+        best = [int(b) for b in finite[d == d.min()]]
+        # equally near codes: the one carrying the input's sign (the two
+        # zeros), then the one with the even mantissa
+        best = [b for b in best if (b >> 7) == int(np.signbit(x))] or best
+        if len(best) > 1:
+            best = [b for b in best if b % 2 == 0]
+        assert int(c) in best, (x, c, best)
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(52)
+    v = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-20, 20, 5000), [0.0, -0.0, 1.0]])
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(v), ref)
+
+
+def test_row_quantisation_scale_error_and_idempotence():
+    rng = np.random.default_rng(53)
+    x = (rng.standard_normal((40, 96)) * np.exp(rng.uniform(-8, 8, (40, 1)))).astype(np.float32)
+    x[3] = 0.0
+    q, s = O.quantize_rows_e4m3(x)
+    amax = np.max(np.abs(x), axis=1)
+    assert s[3] == 1.0 and np.all(q[3] == 0)
+    np.testing.assert_array_equal(s[amax > 0], (amax[amax > 0] / np.float32(448)).astype(np.float32))
+    # the largest magnitude of each row lands on +-448 (codes 0x7E / 0xFE)
+    for r in np.nonzero(amax > 0)[0]:
+        c = q[r, np.argmax(np.abs(x[r]))]
+        assert c & 0x7F == 0x7E
+    # each value within half a step: 1/16 relative (3 mantissa bits), or
+    # 2^-10 s below 2^-6 s (subnormals)
+    xh = O.dequantize_rows_e4m3(q, s)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, s[:, None].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(np.abs(xh - x) <= bound)
+    # quantising dequantised rows again returns the same codes and scales
+    q2, s2 = O.quantize_rows_e4m3(xh)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+
+
+def test_fp8_expert_ffn_linear_is_exact_on_the_dequantised_rows():
+    rng = np.random.default_rng(54)
+    x = rng.standard_normal((20, 32)).astype(np.float32)
+    w = rng.standard_normal((24, 32)) / 6
+    q, s = O.quantize_rows_e4m3(x)
+    got = O.expert_ffn_fp8("linear", q, s, w)
+    xh = O.e4m3_to_f64(q) * s[:, None].astype(np.float64)
+    np.testing.assert_allclose(got, O.expert_ffn("linear", xh, w), rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("kind", ["swiglu", "relu", "gelu"])
+def test_fp8_expert_ffn_stays_within_the_quantisation_error_of_the_exact_ffn(kind):
+    # inputs and hidden values each carry at most 1/16 relative error; with
+    # random weights the output rows then differ from the exact FFN by a few
+    # percent, and a planted mistake (a scale inverted, a hidden layer left
+    # unquantised, the wrong scale row) fails one of the checks below
+    rng = np.random.default_rng(55)
+    d, f, n = 64, 96, 48
+    x = rng.standard_normal((30, d)).astype(np.float32) * np.float32(3.0)
+    w1 = rng.standard_normal((f, d)) / np.sqrt(d)
+    w3 = rng.standard_normal((f, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((d, f)) / np.sqrt(f)
+    q, s = O.quantize_rows_e4m3(x)
+    got = O.expert_ffn_fp8(kind, q, s, w1, w3 if kind == "swiglu" else None, w2)
+    exact = O.expert_ffn(kind, x.astype(np.float64), w1, w3 if kind == "swiglu" else None, w2)
+    rel = np.max(np.abs(got - exact), axis=1) / np.max(np.abs(exact), axis=1)
+    assert np.all(rel < 0.12) and np.median(rel) < 0.06
+    # the hidden layer is quantised (not just the input)
+    xh = O.dequantize_rows_e4m3(q, s)
+    no_hidden_q = O.expert_ffn(kind, xh, w1, w3 if kind == "swiglu" else None, w2)
+    assert np.max(np.abs(got - no_hidden_q)) > 0
