@@ -60,6 +60,10 @@ _SIGS = {
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp]),
     "moe_aux_loss": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp]),
+    "moe_quantize_rows_e4m3": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_ffn_fp8_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "moe_expert_ffn_fp8": (_i, [_i, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _sz, _vp]),
     "moe_combine_backward": (_i, [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "moe_ffn_backward_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn_grouped_backward": (_i, [_i, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i,
@@ -281,3 +285,25 @@ def permute_backward(dx_rows, dest_pos, d, dx_shared, n_shared, dres, dz, w_g, d
     st = lib().moe_permute_backward(_p(dx_rows), dtype_code(dx_rows), _p(dest_pos), T, k, d, _p(dx_shared), n_shared,
                                     _p(dres), _p(dz), _p(w_g), E, _p(dx), _stream(stream))
     _check("moe_permute_backward", st)
+
+
+# ---------------------------------------------------------------- fp8 activations
+
+
+def quantize_rows_e4m3(x, q, scale, stream=None):
+    rows, cols = x.shape
+    st = lib().moe_quantize_rows_e4m3(_p(x), dtype_code(x), rows, cols, _p(q), _p(scale), _stream(stream))
+    _check("moe_quantize_rows_e4m3", st)
+
+
+def ffn_fp8_workspace_size(kind, max_rows, E, d_ff) -> int:
+    return lib().moe_ffn_fp8_workspace_size(kind, max_rows, E, d_ff)
+
+
+def expert_ffn_fp8(kind, xq, x_scale, gather, row_mode, max_rows, offsets, E, d, d_ff, d_out, w1, w3, w2, s1, s3, s2,
+                   y_rows, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().moe_expert_ffn_fp8(kind, _p(xq), _p(x_scale), xq.shape[0], _p(gather), row_mode, max_rows, _p(offsets),
+                                  E, d, d_ff, d_out, _p(w1), _p(w3), _p(w2), _p(s1), _p(s3), _p(s2), _p(y_rows),
+                                  _p(workspace), ws_bytes, _stream(stream))
+    _check("moe_expert_ffn_fp8", st)

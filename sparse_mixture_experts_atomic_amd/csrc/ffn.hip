@@ -157,6 +157,94 @@ int moe_expert_ffn_gathered(int kind, const void* x, int act_dt, int n_src, cons
                  w2, w_dt, s1, s3, s2, b1, b2, y_rows, workspace, workspace_bytes, stream);
 }
 
+size_t moe_ffn_fp8_workspace_size(int kind, int max_rows, int E, int d_ff) {
+  if (max_rows < 0 || E < 1) return 0;
+  size_t s = align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), kWsAlign);
+  if (kind == MOE_FFN_RELU || kind == MOE_FFN_SWIGLU || kind == MOE_FFN_GELU) {
+    const size_t ff = static_cast<size_t>(max_rows) * static_cast<size_t>(d_ff > 0 ? d_ff : 0);
+    s += align_up(ff * 2, kWsAlign) + align_up(ff, kWsAlign) + align_up(static_cast<size_t>(max_rows) * 4, kWsAlign);
+  }
+  return s;
+}
+
+int moe_expert_ffn_fp8(int kind, const void* xq, const float* x_scale, int n_src, const int32_t* gather, int row_mode,
+                       int max_rows, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1,
+                       const void* w3, const void* w2, const float* s1, const float* s3, const float* s2, void* y_rows,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (kind != MOE_FFN_LINEAR && kind != MOE_FFN_RELU && kind != MOE_FFN_SWIGLU && kind != MOE_FFN_GELU)
+    return MOE_ERR_INVALID_ARG;
+  if (row_mode != MOE_ROWS_PACKED && row_mode != MOE_ROWS_SHARED) return MOE_ERR_INVALID_ARG;
+  if (gather && row_mode != MOE_ROWS_PACKED) return MOE_ERR_INVALID_ARG;
+  if (max_rows < 0 || E < 1 || d < 1 || d_out < 1 || n_src < 0) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  const bool two = kind != MOE_FFN_LINEAR;
+  if (two && d_ff < 1) return MOE_ERR_INVALID_ARG;
+  if (d % 128 != 0 || (two && d_ff % 128 != 0) || d_out % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!offsets || !w1 || !s1 || (max_rows > 0 && (!xq || !x_scale || !y_rows))) return MOE_ERR_INVALID_ARG;
+  if (gather && max_rows > 0 && n_src == 0) return MOE_ERR_INVALID_ARG;
+  if ((kind == MOE_FFN_SWIGLU) != (w3 != nullptr) || (kind == MOE_FFN_SWIGLU) != (s3 != nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (two != (w2 != nullptr) || two != (s2 != nullptr)) return MOE_ERR_INVALID_ARG;
+  const void* p16[] = {xq, offsets, w1, w3, w2, y_rows, gather};
+  for (const void* ptr : p16)
+    if (ptr && !aligned16(ptr)) return MOE_ERR_INVALID_ARG;
+  const void* p4[] = {x_scale, s1, s3, s2};
+  for (const void* ptr : p4)
+    if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 3u)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < moe_ffn_fp8_workspace_size(kind, max_rows, E, d_ff) || !aligned16(workspace))
+    return MOE_ERR_WORKSPACE;
+  if (max_rows == 0) return MOE_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ts = reinterpret_cast<int32_t*>(ws);
+  ws += align_up(static_cast<size_t>(E + 1) * sizeof(int32_t), kWsAlign);
+  const size_t ff = static_cast<size_t>(max_rows) * static_cast<size_t>(two ? d_ff : 0);
+  uint16_t* H = two ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+  uint8_t* Hq = two ? reinterpret_cast<uint8_t*>(ws + align_up(ff * 2, kWsAlign)) : nullptr;
+  float* sh = two ? reinterpret_cast<float*>(ws + align_up(ff * 2, kWsAlign) + align_up(ff, kWsAlign)) : nullptr;
+
+  int st = launch_tile_map(offsets, E, kGemmBM, ts, stream);
+  if (st != MOE_OK) return st;
+  const int mtm = m_tiles_max(max_rows, E);
+  GemmParams p1{};
+  p1.A = static_cast<const uint16_t*>(xq);
+  p1.a_shared = row_mode == MOE_ROWS_SHARED ? 1 : 0;
+  p1.gather = gather;
+  p1.a_rows = n_src;
+  p1.offsets = offsets;
+  p1.ts = ts;
+  p1.E = E;
+  p1.B1 = w1;
+  p1.B3 = w3;
+  p1.s1 = s1;
+  p1.s3 = s3;
+  p1.C = two ? H : static_cast<uint16_t*>(y_rows);
+  p1.N = two ? d_ff : d_out;
+  p1.K = d;
+  p1.split_max = 1;
+  p1.row_scale = x_scale;
+  const int epi1 = kind == MOE_FFN_SWIGLU ? EPI_SWIGLU : kind == MOE_FFN_RELU ? EPI_RELU
+                   : kind == MOE_FFN_GELU ? EPI_GELU : EPI_PLAIN;
+  st = launch_grouped_gemm_f8(epi1, p1, mtm, stream);
+  if (st != MOE_OK || !two) return st;
+  // the hidden layer (bf16) quantised per row, rows below offsets[E] only
+  st = launch_quant_rows(H, MOE_BF16, max_rows, d_ff, offsets + E, Hq, sh, stream);
+  if (st != MOE_OK) return st;
+  GemmParams p2{};
+  p2.A = reinterpret_cast<const uint16_t*>(Hq);
+  p2.offsets = offsets;
+  p2.ts = ts;
+  p2.E = E;
+  p2.B1 = w2;
+  p2.s1 = s2;
+  p2.C = static_cast<uint16_t*>(y_rows);
+  p2.N = d_out;
+  p2.K = d_ff;
+  p2.split_max = 1;
+  p2.row_scale = sh;
+  return launch_grouped_gemm_f8(EPI_PLAIN, p2, mtm, stream);
+}
+
 }  // extern "C"
 
 namespace moe {

@@ -482,9 +482,11 @@ __device__ __forceinline__ SplitPlan split_plan(int V, int KT, int R, int n_cu, 
 // (may be <= 0), col0: first output column (pieces at col0 + c >= N are
 // skipped; N % 8 == 0).  st must hold 32 FM x (OC + 8) bf16 of LDS that no
 // other wavefront uses.
-template <int EPI, int FM>
+// RS: fp8 activations; rsl[r] (LDS) is the scale of the wavefront's row r,
+// applied with the column scale before the activation.
+template <int EPI, int FM, bool RS = false>
 __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint16_t* st, const GemmParams& p, int e,
-                                              int row0, int rows_valid, int col0) {
+                                              int row0, int rows_valid, int col0, const float* rsl = nullptr) {
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
   constexpr int PITCH = OC + 8;           // the two lane halves of a write land 16 banks apart
   constexpr int PR = OC / 8;              // 16-byte pieces per row
@@ -510,10 +512,12 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
         float v[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          float rs = 1.f;
+          if constexpr (RS) rs = rsl[i * 32 + ((q + h) >> 2) * 8 + fc * 4 + ((q + h) & 3)];
           if (EPI == EPI_SWIGLU) {
-            v[h] = silu_fast(acc[i][j][q + h] * sg) * (acc[i][j + 2][q + h] * su);
+            v[h] = silu_fast(acc[i][j][q + h] * (rs * sg)) * (acc[i][j + 2][q + h] * (rs * su));
           } else {
-            v[h] = acc[i][j][q + h] * sg + bias;
+            v[h] = acc[i][j][q + h] * (rs * sg) + bias;
             v[h] = act1<EPI>(v[h]);
           }
         }
@@ -1095,6 +1099,171 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     tile(std::integral_constant<int, 4>{});
 }
 
+// ---------------------------------------------------------------------------
+// e4m3 activations x e4m3 weights on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+// scales; the per-row scales of both operands multiply the fp32
+// accumulators in the epilogue).  One byte per value, so a stage of 128 K
+// values has the byte geometry of a bf16 stage of 64: rows of 128 bytes,
+// eight 16-byte chunks in the same LDS swizzle, DMA'd global -> LDS by
+// global_load_lds_dwordx4 with per-lane offsets fixed for the whole loop
+// (gathered rows: the offset of the source row).  Tile 256 x 256, four
+// wavefronts of 128 x 128 (4 x 4 fragments, 256 accumulator registers).  A
+// k-step is 64 values: a lane supplies 32 bytes of its row (row lane % 32,
+// k-half lane / 32), read as two 16-byte chunks; A and B use the same lane
+// to k mapping, which is all the product needs.  Two LDS stages of 64 KB:
+//   k-step 0 of stage s: 16 MFMAs, reading k-step 1's fragments meanwhile;
+//   wait for stage s + 1's DMAs, barrier (every wavefront is done with
+//   stage s's buffer);
+//   k-step 1: 16 MFMAs, issuing stage s + 2's DMAs into the freed buffer
+//   (one per MFMA) and reading stage s + 1's k-step 0 fragments.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+constexpr int kF8BK = 128;         // K values (bytes) per stage
+constexpr int kF8Stage = 256 * kF8BK / 16;   // uint4 per operand and stage
+// LDS: two stages of A and B (128 KB), reused after the loop by the
+// epilogue's staging (four wavefronts of 128 rows x 136 bf16 = 136 KB)
+constexpr int kF8Lds = 4 * 128 * (128 + 8) * 2 / 16 > 4 * kF8Stage ? 4 * 128 * (128 + 8) * 2 / 16 : 4 * kF8Stage;
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams p) {
+  constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
+  constexpr int CH = 8;                      // 16-byte chunks per LDS row
+  constexpr int ND = 256 * CH / kThreads;    // DMA instructions per operand and stage (8)
+  __shared__ uint4 ldsm[kF8Lds];             // [buffer][A, B][256 rows x 8 chunks], then the epilogue staging
+  __shared__ float rsl[4][128];              // row scales of each wavefront's rows
+  static_assert(kF8Lds * 16 + 4 * 128 * 4 <= 160 * 1024, "LDS");
+  auto lds = [&](int buf, int op) __attribute__((always_inline)) { return ldsm + (buf * 2 + op) * kF8Stage; };
+
+  const int n_tiles = (p.N + HC - 1) / HC;
+  const int m_total = p.ts[p.E];
+  const int V = m_total * n_tiles;
+  const int per = (V + kXcds - 1) / kXcds;
+  const int b = blockIdx.x;
+  if (b / kXcds >= per) return;
+  const int L = (b % kXcds) * per + b / kXcds;   // blocks of one XCD take a contiguous range
+  if (L >= V) return;
+  const TileCoord tc = tile_coord(p, L, m_total, n_tiles, 256);
+  const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
+  const int K = p.K, N = p.N;
+  const int KT = K / kF8BK;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fc = lane >> 5;
+
+  // per-lane DMA offsets: instruction i fills rows 32 i + tid / 8, stored
+  // chunk tid % 8, which holds the global chunk (tid % 8) ^ ((tid >> 4) % 8)
+  const int cq = (tid & (CH - 1)) ^ ((tid >> 4) & (CH - 1));
+  const bool gat = p.gather != nullptr;
+  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(p.A);
+  const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(
+      gat ? A8 : A8 + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K));
+  uint32_t a_vo[ND], b_vo[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    const int r = min(i * 32 + tid / CH, rows_valid - 1);
+    const int src = gat ? min(max(p.gather[row0 + r], 0), p.a_rows - 1) : r;
+    a_vo[i] = static_cast<uint32_t>(src * K + cq * 16);
+    const int rb = i * 32 + tid / CH;
+    int n;
+    if (EPI == EPI_SWIGLU) n = nt * HC + (rb >> 7) * 64 + (rb & 63);
+    else n = nt * 256 + rb;
+    n = min(n, N - 1);
+    b_vo[i] = static_cast<uint32_t>(n * K + cq * 16);
+  }
+  const char* b_sb1 = uniform_ptr(static_cast<const char*>(p.B1) + static_cast<size_t>(e) * N * K);
+  const char* b_sb3 = EPI == EPI_SWIGLU ? uniform_ptr(static_cast<const char*>(p.B3) + static_cast<size_t>(e) * N * K)
+                                        : b_sb1;
+  const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
+  auto issue = [&](int st, int buf, int q) __attribute__((always_inline)) {
+    // q < ND: A instruction q; else B instruction q - ND (SwiGLU: rows 64..127
+    // of each 128-row half are up rows)
+    if (q < ND) {
+      dma16(a_sb + st * kF8BK, a_vo[q], lds_addr(lds(buf, 0) + q * 256) + wave_lds);
+    } else {
+      const int i = q - ND;
+      const char* bb = (EPI == EPI_SWIGLU && ((i * 32) & 64)) ? b_sb3 : b_sb1;
+      dma16(bb + st * kF8BK, b_vo[i], lds_addr(lds(buf, 1) + i * 256) + wave_lds);
+    }
+  };
+  // fragment of k-step ks: rows rb + fr, chunks 4 ks + 2 fc (+ 1)
+  auto read_frag = [&](const uint4* S, int row, int ks) __attribute__((always_inline)) {
+    const uint4 lo = S[dma_swz<CH>(row, 4 * ks + 2 * fc)];
+    const uint4 hi = S[dma_swz<CH>(row, 4 * ks + 2 * fc + 1)];
+    return i32x8_t{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                   static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  };
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  // a wavefront whose rows all lie past the segment's end skips its MFMAs
+  const bool wave_rows = wm * 128 < rows_valid;
+  i32x8_t f0[8], f1[8];                      // fragments: A 0..3, B 4..7
+  auto read_all = [&](i32x8_t (&f)[8], int buf, int ks, int r) __attribute__((always_inline)) {
+    if (r < 4) f[r] = read_frag(lds(buf, 0), wm * 128 + r * 32 + fr, ks);
+    else f[r] = read_frag(lds(buf, 1), wn * 128 + (r - 4) * 32 + fr, ks);
+  };
+  auto mma = [&](const i32x8_t (&f)[8], int q) __attribute__((always_inline)) {
+    const int i = q >> 2, j = q & 3;
+    if (wave_rows)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[i], f[4 + j], acc[i][j], 0, 0, 0, 127, 0, 127);
+  };
+
+  // prologue: stages 0 and 1 in flight, wait for stage 0
+#pragma unroll
+  for (int q = 0; q < 2 * ND; ++q) issue(0, 0, q);
+  if (KT > 1) {
+#pragma unroll
+    for (int q = 0; q < 2 * ND; ++q) issue(1, 1, q);
+    wait_vmcnt<2 * ND>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+#pragma unroll
+  for (int r = 0; r < 8; ++r) read_all(f0, 0, 0, r);
+  for (int s = 0; s < KT; ++s) {
+    const int buf = s & 1;
+    // k-step 0 on f0; k-step 1's fragments into f1
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma(f0, q);
+      if (q < 8) read_all(f1, buf, 1, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // stage s + 1 landed (this wavefront's DMAs) and every wavefront is done
+    // with stage s's buffer
+    wait_vmcnt<0>();
+    lds_barrier();
+    const bool next = s + 1 < KT, next2 = s + 2 < KT;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma(f1, q);
+      if (next2) issue(s + 2, buf, q);
+      if (next && q < 8) read_all(f0, buf ^ 1, 0, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // epilogue: the buffers are free (no DMA in flight, the last reads came
+  // before the last barrier); row scales of the wavefront's rows into LDS
+  lds_barrier();
+  for (int r = lane; r < 128; r += 64) {
+    const int lr = min(wm * 128 + r, rows_valid - 1);
+    const int grow = row0 + lr;
+    const int src = gat ? min(max(p.gather[grow], 0), p.a_rows - 1) : (p.a_shared ? grow - seg0 : grow);
+    rsl[wave][r] = p.row_scale[src];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
+  const int col0 = EPI == EPI_SWIGLU ? nt * HC + wn * 64 : nt * 256 + wn * 128;
+  wave_epilogue<EPI, 4, true>(acc, reinterpret_cast<uint16_t*>(ldsm) + wave * 128 * (OC + 8), p, e,
+                              row0 + wm * 128, rows_valid - wm * 128, col0, rsl[wave]);
+}
+
 template <int EPI, int BK, bool FP8>
 int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
@@ -1144,6 +1313,27 @@ int launch_epi(int epi, bool fp8, const GemmParams& p, int m_tiles_max, hipStrea
 }
 
 }  // namespace
+
+int launch_grouped_gemm_f8(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  if (p.K % kF8BK != 0 || p.N % 8 != 0 || !p.row_scale) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<size_t>(p.N) * p.K >= (size_t(1) << 31) || static_cast<size_t>(kGemmBM) * p.K >= (size_t(1) << 31) ||
+      (p.gather && static_cast<size_t>(p.a_rows) * p.K >= (size_t(1) << 31)))
+    return MOE_ERR_UNSUPPORTED;
+  const long HC = epi == EPI_SWIGLU ? 128 : 256;
+  const long n_tiles = (p.N + HC - 1) / HC;
+  long blocks = n_tiles * m_tiles_max;
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+  if (blocks <= 0) return MOE_OK;
+  if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  switch (epi) {
+    case EPI_SWIGLU: hipLaunchKernelGGL(grouped_gemm_f8_kernel<EPI_SWIGLU>, grid, block, 0, stream, p); break;
+    case EPI_RELU: hipLaunchKernelGGL(grouped_gemm_f8_kernel<EPI_RELU>, grid, block, 0, stream, p); break;
+    case EPI_GELU: hipLaunchKernelGGL(grouped_gemm_f8_kernel<EPI_GELU>, grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL(grouped_gemm_f8_kernel<EPI_PLAIN>, grid, block, 0, stream, p); break;
+  }
+  return check_launch();
+}
 
 // 256-row tiles throughout (one tile map serves both GEMMs of an FFN); the
 // weight-row width is 256 unless that leaves too few tiles to fill 256 CUs

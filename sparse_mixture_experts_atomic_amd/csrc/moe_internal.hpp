@@ -128,6 +128,7 @@ struct GemmParams {
   float* partial;            // split-tail partial sums: n_cu x 256 x 256 fp32 (or null)
   int n_cu;                  // compute units (one block of the DMA kernel each)
   int split_max;             // most K parts of a split tile (1: no split)
+  const float* row_scale;    // fp8 activations: scale of each source row of A (or null)
 };
 
 // Bytes of the split-tail partial buffer for n_cu compute units.
@@ -136,6 +137,18 @@ constexpr int kGemmSplitMax = 4;
 
 // Enqueues C = epi(A B^T) per segment.  m_tiles_max bounds ts[E] from above.
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream);
+
+// Both operands e4m3 (A: codes, one byte per value, rows scaled by
+// p.row_scale of their source row; B: codes with per-row scales p.s1/p.s3):
+// C = epi(diag(row scales) A B^T diag(column scales)) per segment, bf16 out.
+// K % 128 == 0, N % 8 == 0.
+int launch_grouped_gemm_f8(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
+
+// Per-row e4m3 quantisation (quant.hip): scale[r] = max |x[r, :]| / 448 (1
+// for a zero row), q = e4m3(x / scale); rows_dev (device, or null) bounds the
+// rows; cols % 8 == 0.
+int launch_quant_rows(const void* x, int x_dt, int rows, int cols, const int32_t* rows_dev, uint8_t* q, float* scale,
+                      hipStream_t stream);
 
 // ts[e] = sum over e' < e of ceil(segment length / bm), ts[E] the total (one
 // block, E <= 1024)

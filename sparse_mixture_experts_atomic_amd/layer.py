@@ -17,7 +17,8 @@ from . import _lib as L
 class MoELayer:
     def __init__(self, *, T: int, d: int, d_out: int, E: int, k: int, kind: str, d_ff: int, gate: str,
                  capacity: int, n_shared: int, alpha: float, act_dtype: torch.dtype,
-                 weights: Dict[str, Optional[torch.Tensor]], device="cuda", gather_rows: bool = False):
+                 weights: Dict[str, Optional[torch.Tensor]], device="cuda", gather_rows: bool = False,
+                 fp8_act: bool = False):
         self.T, self.d, self.d_out, self.E, self.k = T, d, d_out, E, k
         self.kind = L.FFN_KINDS[kind]
         self.d_ff = d_ff
@@ -40,6 +41,16 @@ class MoELayer:
         self.dest_pos = torch.empty((T, k), **i32)
         self.perm_token = torch.empty((max(A, 1),), **i32)
         # gather_rows: the routed FFN reads x through perm_token (no packed copy)
+        # fp8_act: the experts run on e4m3 activations (x quantised per row,
+        # read through perm_token; e4m3 weights required)
+        self.fp8_act = fp8_act
+        if fp8_act:
+            if weights.get("s1") is None or act_dtype != torch.bfloat16:
+                raise ValueError("fp8 activations need e4m3 expert weights and bf16 x")
+            gather_rows = True
+            self.xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((max(T, 1),), dtype=torch.float32, device=dev)
+            self.ws_f8 = self._ws(L.ffn_fp8_workspace_size(self.kind, A, E, d_ff), dev)
         self.gather_rows = gather_rows
         self._x_src = None
         self.x_perm = None if gather_rows else torch.empty((max(A, 1), d), dtype=act_dtype, device=dev)
@@ -56,6 +67,8 @@ class MoELayer:
             self.shared_y = torch.empty((n_shared, T, d_out), dtype=act_dtype, device=dev)
             self.sh_offsets = torch.arange(0, (n_shared + 1) * T, T, **i32)
             self.ws_sh = self._ws(L.ffn_workspace_size(self.kind, act, n_shared * T, n_shared, d, d_ff, d_out), dev)
+            if fp8_act:
+                self.ws_sh_f8 = self._ws(L.ffn_fp8_workspace_size(self.kind, n_shared * T, n_shared, d_ff), dev)
         else:
             self.shared_y = None
 
@@ -85,8 +98,19 @@ class MoELayer:
                            self.counts_routed, self.counts_kept, self.offsets, self.dest_pos, self.perm_token,
                            self.ws_disp)
 
+    def quantize(self, x):
+        """fp8 activations: x quantised per row (codes and scales)."""
+        if self.fp8_act:
+            L.quantize_rows_e4m3(x, self.xq, self.xs)
+
     def experts(self, x_perm=None, offsets=None):
         w = self.w
+        if self.fp8_act:
+            L.expert_ffn_fp8(self.kind, self.xq, self.xs, self.perm_token, L.ROWS_PACKED, self.T * self.k,
+                             self.offsets if offsets is None else offsets, self.E, self.d, self.d_ff, self.d_out,
+                             w["w1"], w.get("w3"), w.get("w2"), w.get("s1"), w.get("s3"), w.get("s2"), self.y_rows,
+                             self.ws_f8)
+            return
         if self.gather_rows and x_perm is None:
             L.expert_ffn_gathered(self.kind, self._x_src, self.perm_token, self.T * self.k,
                                   self.offsets if offsets is None else offsets, self.E, self.d, self.d_ff, self.d_out,
@@ -102,6 +126,11 @@ class MoELayer:
         if not self.n_shared:
             return
         w = self.w
+        if self.fp8_act:
+            L.expert_ffn_fp8(self.kind, self.xq, self.xs, None, L.ROWS_SHARED, self.n_shared * self.T, self.sh_offsets,
+                             self.n_shared, self.d, self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"), w.get("sh_w2"),
+                             w.get("sh_s1"), w.get("sh_s3"), w.get("sh_s2"), self.shared_y, self.ws_sh_f8)
+            return
         L.expert_ffn_grouped(self.kind, x, self.n_shared * self.T, L.ROWS_SHARED, self.sh_offsets, self.n_shared,
                              self.d, self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"), w.get("sh_w2"),
                              w.get("sh_s1"), w.get("sh_s3"), w.get("sh_s2"), w.get("sh_b1"), w.get("sh_b2"),
@@ -187,6 +216,7 @@ class MoELayer:
         """Whole layer; returns (y, aux loss tensor).  Asynchronous."""
         self.router(x)
         self.dispatch(x)
+        self.quantize(x)
         self.experts()
         self.shared(x)
         self.combine(residual)
