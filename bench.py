@@ -12,7 +12,10 @@ median duration, measured with HIP events on the stream the kernels run on.
 A third pass repeats the steps after a 512 MB scratch write each ("cold":
 no input left in the last-level cache); a last one times whole steps of the
 same layer with the routed FFN gathering its rows through the dispatch
-permutation ("gathered").  The CPU baseline times the float64
+permutation ("gathered"); then training steps (forward + backward) and, on
+the same shapes with e4m3 expert weights, steps of the layer with the expert
+products on e4m3 activations ("fp8", reported apart: another precision).
+The CPU baseline times the float64
 oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -32,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer fwd tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_traffic_mixtral.json")
 
@@ -118,6 +122,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the training-step (forward + backward) leg")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-activation leg")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration) and exit")
     args = ap.parse_args()
@@ -333,6 +338,58 @@ def main():
                             "moe_router_backward, moe_permute_backward); stage medians with HIP events between them"}
         del blayer
 
+    # timed region 6 (last): the same shapes with e4m3 expert weights and the
+    # expert products on e4m3 activations (per-row codes and scales for x and
+    # the hidden layer); another precision, so reported apart from `value`
+    fp8 = None
+    if not args.no_fp8 and cfg.act_dtype == "bf16" and cfg.ffn != "linear" and cfg.d % 128 == 0 \
+            and cfg.d_ff % 128 == 0:
+        import dataclasses
+        cfg8 = dataclasses.replace(cfg, w_dtype="fp8", name=cfg.name + "_e4m3")
+        arr8 = W.generate(cfg8)
+        flayer = MoELayer(**layer_kwargs(cfg8, arr8, C, device="cuda"), fp8_act=True)
+        del arr8
+        for _ in range(args.warmup):
+            flayer.forward(x)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            flayer.forward(x)
+        stop.record()
+        torch.cuda.synchronize()
+        ms_f8 = start.elapsed_time(stop) / args.steps
+        fst = ["router", "dispatch", "quantize", "experts", "shared", "combine"]
+        fev = {s_: [] for s_ in fst}
+        for _ in range(args.steps):
+            m = [torch.cuda.Event(enable_timing=True) for _ in range(len(fst) + 1)]
+            m[0].record()
+            flayer.router(x)
+            m[1].record()
+            flayer.dispatch(x)
+            m[2].record()
+            flayer.quantize(x)
+            m[3].record()
+            flayer.experts()
+            m[4].record()
+            flayer.shared(x)
+            m[5].record()
+            flayer.combine()
+            m[6].record()
+            for i, s_ in enumerate(fst):
+                fev[s_].append((m[i], m[i + 1]))
+        torch.cuda.synchronize()
+        fms = {s_: float(np.median([a_.elapsed_time(b_) for a_, b_ in fev[s_]])) for s_ in fst}
+        f_kept = int(flayer.offsets[-1].item())
+        f_flops = ffn_flops_per_row(cfg) * f_kept
+        f_tf = f_flops / (fms["experts"] * 1e-3) / 1e12
+        fp8 = {"ms_per_step": ms_f8, "value": cfg.T / (ms_f8 * 1e-3), "unit": "tokens/s", "stages_ms": fms,
+               "ffn_tflops": f_tf, "peak": PEAK_FP8_TFLOPS, "frac": f_tf / PEAK_FP8_TFLOPS,
+               "ffn_flops_per_launch": f_flops,
+               "note": "e4m3 expert weights (per-row scales) and e4m3 activations (per-row scales, hidden layer "
+                       "requantised); moe_quantize_rows_e4m3 + moe_expert_ffn_fp8 (rows gathered through "
+                       "perm_token); router fp32"}
+        del flayer
+
     a_kept = int(layer.offsets[-1].item())
     ffn_flops = ffn_flops_per_row(cfg) * a_kept
     sh_flops = ffn_flops_per_row(cfg) * cfg.T * cfg.n_shared
@@ -373,6 +430,7 @@ def main():
                                  for k_ in ("router", "dispatch", "combine", "router_noisy")},
         "shared_tflops": (sh_flops / (st_ms["shared"] * 1e-3) / 1e12) if cfg.n_shared else None,
         "backward": backward,
+        "fp8": fp8,
         "kept_rows": a_kept,
         "cold": {
             "note": "median step with a 512 MB scratch write before each step (no input in the last-level cache)",
