@@ -38,6 +38,7 @@ namespace {
 constexpr int kBT = 256;          // threads
 constexpr int kBM = 128, kBN = 128, kBK = 32;
 constexpr int kBxcds = 8;
+constexpr int kBGroup = 8;      // n-tiles per ordering group
 
 __device__ __forceinline__ int bswz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
@@ -93,7 +94,11 @@ __global__ __launch_bounds__(kBT, 2) void bwd_gemm_kernel(BwdGemmParams p) {
   const int fr = lane & 31, fc = lane >> 5;
 
   // ---- tile decode: blocks of one XCD (blockIdx % 8) take a contiguous
-  // range of tiles, m-tiles of one n-tile next to each other ----
+  // range of tiles.  The tiles come in groups of kBGroup n-tiles; inside a
+  // group (dgrad) segment by segment, each segment's m-tiles for every
+  // n-tile, or (wgrad) m-tile by m-tile, each for every n-tile of the group.
+  // The 64 tiles an XCD runs at once (two per CU) then share 8 A and 8 B
+  // tiles instead of one B tile and 64 A tiles. ----
   const int n_tiles = (p.N + kBN - 1) / kBN;
   int e, row0, rows_valid, nt, k_begin, k_end;
   long a_row0 = 0, b_row0 = 0;
@@ -109,8 +114,11 @@ __global__ __launch_bounds__(kBT, 2) void bwd_gemm_kernel(BwdGemmParams p) {
       if (L >= V) return;
       e = L / (m_tiles * n_tiles);
       const int r = L - e * m_tiles * n_tiles;
-      nt = r / m_tiles;
-      row0 = (r % m_tiles) * kBM;
+      const int grp = r / (m_tiles * kBGroup);
+      const int gs = min(kBGroup, n_tiles - grp * kBGroup);
+      const int rr = r - grp * m_tiles * kBGroup;
+      nt = grp * kBGroup + rr % gs;
+      row0 = (rr / gs) * kBM;
       rows_valid = min(kBM, p.M - row0);
       k_begin = p.offsets[e];
       k_end = p.offsets[e + 1];
@@ -125,11 +133,15 @@ __global__ __launch_bounds__(kBT, 2) void bwd_gemm_kernel(BwdGemmParams p) {
       if (slot >= per) return;
       L = (blockIdx.x % kBxcds) * per + slot;
       if (L >= V) return;
-      nt = L / m_total;
-      const int mt = L - nt * m_total;
-      e = seg_of(p.ts, p.E, mt);
+      const int grp = L / (m_total * kBGroup);
+      const int gs = min(kBGroup, n_tiles - grp * kBGroup);
+      const int Lr = L - grp * m_total * kBGroup;
+      e = seg_of(p.ts, p.E, Lr / gs);
+      const int me = p.ts[e + 1] - p.ts[e];
+      const int r = Lr - p.ts[e] * gs;
+      nt = grp * kBGroup + r / me;
       const int seg0 = p.offsets[e];
-      row0 = seg0 + (mt - p.ts[e]) * kBM;
+      row0 = seg0 + (r % me) * kBM;
       rows_valid = min(kBM, p.offsets[e + 1] - row0);
       k_begin = 0;
       k_end = p.K;
