@@ -674,17 +674,18 @@ __global__ __launch_bounds__(kLgThreads) void router_logits_kernel(const uint16_
 // NOISY: the partial rows hold 2 E logits per token, the clean ones then the
 // noise projection's; the noisy logit is clean + b_g + draw * (softplus(
 // projection + b_n) + eps).  PER: logits per thread, 16 E / 512 rounded up
-// to a power of two.  Every load of a group of four slices, and the bias and
-// draws, is in flight before the first wait: at one block per CU the kernel
-// is a chain of memory round trips otherwise.
+// to a power of two.  Every load of a group of G slices (4, or 1 when there
+// is a single slice), and the bias and draws, is in flight before the first
+// wait: at one block per CU the kernel is a chain of memory round trips
+// otherwise.
 constexpr int kFnTok = 16;                    // tokens per block
 constexpr int kFnWaves = 8;
 constexpr int kFnThreads = 64 * kFnWaves;
-constexpr int kFnGroup = 4;                   // slices per round of loads
 
-template <bool NOISY, int PER>
+template <bool NOISY, int PER, int G>
 __global__ __launch_bounds__(kFnThreads) void router_finish_kernel(RouterArgs a, const float* __restrict__ part,
                                                                     int nslice) {
+  constexpr int kFnGroup = G;                 // slices per round of loads
   // launch_finish picks PER with PER * kFnThreads >= kFnTok * E
   __shared__ float lg[kFnTok * kRtMaxE];
   __shared__ float wcol[kFnWaves * kRtMaxE];
@@ -773,18 +774,26 @@ __global__ __launch_bounds__(kFnThreads) void router_finish_kernel(RouterArgs a,
   }
 }
 
-// finishing kernel for E experts: logits per thread as a template argument
-template <bool NOISY>
-void launch_finish(const RouterArgs& a, const float* part, int nslice, int nb, hipStream_t stream) {
+// finishing kernel for E experts: logits per thread and slices per round of
+// loads as template arguments (a single slice: no clamped reloads of it)
+template <bool NOISY, int G>
+void launch_finish_g(const RouterArgs& a, const float* part, int nslice, int nb, hipStream_t stream) {
   const dim3 grid(nb), block(kFnThreads);
   if (a.E <= 32)
-    hipLaunchKernelGGL((router_finish_kernel<NOISY, 1>), grid, block, 0, stream, a, part, nslice);
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 1, G>), grid, block, 0, stream, a, part, nslice);
   else if (a.E <= 64)
-    hipLaunchKernelGGL((router_finish_kernel<NOISY, 2>), grid, block, 0, stream, a, part, nslice);
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 2, G>), grid, block, 0, stream, a, part, nslice);
   else if (a.E <= 128)
-    hipLaunchKernelGGL((router_finish_kernel<NOISY, 4>), grid, block, 0, stream, a, part, nslice);
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 4, G>), grid, block, 0, stream, a, part, nslice);
   else
-    hipLaunchKernelGGL((router_finish_kernel<NOISY, 8>), grid, block, 0, stream, a, part, nslice);
+    hipLaunchKernelGGL((router_finish_kernel<NOISY, 8, G>), grid, block, 0, stream, a, part, nslice);
+}
+template <bool NOISY>
+void launch_finish(const RouterArgs& a, const float* part, int nslice, int nb, hipStream_t stream) {
+  if (nslice == 1)
+    launch_finish_g<NOISY, 1>(a, part, nslice, nb, stream);
+  else
+    launch_finish_g<NOISY, 4>(a, part, nslice, nb, stream);
 }
 
 // prob_colsum[e] = sum over blocks of the partial sums.  One block per
