@@ -378,6 +378,26 @@ int moe_aux_loss(const int32_t* counts_routed, const float* prob_colsum, int T, 
                  float alpha, float* loss, hipStream_t stream);
 
 /*
+ * The same loss straight from a router call's workspace, for callers that
+ * pass prob_colsum = NULL to moe_router_topk or moe_router_topk_noisy: the
+ * router then leaves its per-block probability column sums in the workspace
+ * and launches nothing more, and this call forms the column sums (written to
+ * prob_colsum when it is not NULL) and the loss in one launch.  Both equal,
+ * bit for bit, what the router with prob_colsum followed by moe_aux_loss
+ * give (the same fp64 partial sums and reduction trees).
+ *   router_workspace  the workspace of that router call, not written to
+ *                     since; T, d, E, x_dt as passed to it; noisy = 1 for
+ *                     moe_router_topk_noisy, 0 for moe_router_topk
+ *   counts_routed [E] int32; prob_colsum [E] fp32 out or NULL; loss out
+ * Errors as moe_aux_loss, plus MOE_ERR_WORKSPACE when T > 0 and the
+ * workspace is smaller than that router call needs.
+ */
+int moe_aux_loss_from_router(const int32_t* counts_routed, const void* router_workspace,
+                             size_t workspace_bytes, int T, int d, int E, int x_dt, int noisy,
+                             int k, float alpha, float* prob_colsum, float* loss,
+                             hipStream_t stream);
+
+/*
  * ==== Backward pass (training) ==================================================
  * Gradients of L = <dy, y> + daux * aux for the forward layer above, given
  * the layer-output gradient dy [T, d_out] and the aux-loss gradient daux.

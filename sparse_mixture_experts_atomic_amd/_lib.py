@@ -60,6 +60,7 @@ _SIGS = {
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _vp]),
     "moe_aux_loss": (_i, [_vp, _vp, _i, _i, _i, _f, _vp, _vp]),
+    "moe_aux_loss_from_router": (_i, [_vp, _vp, _sz, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]),
     "moe_quantize_rows_e4m3": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
     "moe_ffn_fp8_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_expert_ffn_fp8": (_i, [_i, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -237,6 +238,15 @@ def aux_loss(counts_routed, prob_colsum, T, k, E, alpha, loss, stream=None):
     st = lib().moe_aux_loss(_p(counts_routed), _p(prob_colsum), T, k, E, float(alpha), _p(loss),
                             _stream(stream))
     _check("moe_aux_loss", st)
+
+
+def aux_loss_from_router(counts_routed, router_workspace, T, d, E, x_dt, noisy, k, alpha, loss, prob_colsum=None,
+                         stream=None):
+    ws_bytes = router_workspace.numel() * router_workspace.element_size()
+    st = lib().moe_aux_loss_from_router(_p(counts_routed), _p(router_workspace), ws_bytes, T, d, E, x_dt,
+                                        1 if noisy else 0, k, float(alpha), _p(prob_colsum), _p(loss),
+                                        _stream(stream))
+    _check("moe_aux_loss_from_router", st)
 
 
 # ---------------------------------------------------------------- backward

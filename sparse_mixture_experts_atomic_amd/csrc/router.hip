@@ -813,6 +813,60 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* part, i
   if (threadIdx.x == 0) out[e] = static_cast<float>(red[0]);
 }
 
+// Column sums and balance loss in one launch, from the per-block partial
+// column sums a router call left in its workspace.  Every column sum is
+// formed exactly as colsum_reduce_kernel forms it (256 strided fp64 partial
+// sums, then the same tree), 8 experts per round, and the loss exactly as
+// aux_loss_kernel forms it, so both equal what moe_router_topk with
+// prob_colsum followed by moe_aux_loss give, bit for bit.
+constexpr int kAxChunk = 8;
+__global__ __launch_bounds__(256) void aux_from_parts_kernel(const float* __restrict__ part, int nb, int E,
+                                                             const int32_t* __restrict__ counts, int T_, int k,
+                                                             float alpha, float* __restrict__ prob_colsum,
+                                                             float* __restrict__ loss) {
+  __shared__ double red[kAxChunk][256];
+  __shared__ float csum[kRtMaxE];
+  __shared__ float fred[256];
+  const int i = threadIdx.x;
+  for (int e0 = 0; e0 < E; e0 += kAxChunk) {
+#pragma unroll
+    for (int c = 0; c < kAxChunk; ++c) {
+      const int e = e0 + c;
+      double sum = 0.0;
+      if (e < E)
+        for (int b = i; b < nb; b += 256) sum += static_cast<double>(part[static_cast<size_t>(b) * E + e]);
+      red[c][i] = sum;
+    }
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (i < o) {
+#pragma unroll
+        for (int c = 0; c < kAxChunk; ++c) red[c][i] += red[c][i + o];
+      }
+      __syncthreads();
+    }
+    if (i < kAxChunk && e0 + i < E) {
+      const float v = static_cast<float>(red[i][0]);
+      csum[e0 + i] = v;
+      if (prob_colsum) prob_colsum[e0 + i] = v;
+    }
+    __syncthreads();
+  }
+  float sv = 0.f;
+  if (T_ > 0) {
+    const float inv_tk = 1.0f / (static_cast<float>(T_) * static_cast<float>(k));
+    const float inv_t = 1.0f / static_cast<float>(T_);
+    for (int e = i; e < E; e += 256) sv += (static_cast<float>(counts[e]) * inv_tk) * (csum[e] * inv_t);
+  }
+  fred[i] = sv;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (i < o) fred[i] += fred[i + o];
+    __syncthreads();
+  }
+  if (i == 0) *loss = alpha * static_cast<float>(E) * fred[0];
+}
+
 inline int router_blocks(int T) { return (T + kRtTok - 1) / kRtTok; }
 
 // upper bound of the block count of any router kernel (per-block
@@ -852,6 +906,16 @@ inline size_t logit_ws_offset(int T, int E) {
   return align_up(static_cast<size_t>(router_max_blocks(T)) * E * sizeof(float), kWsAlign);
 }
 
+// blocks of the router kernel that writes the per-block column sums (the
+// first nb x E floats of the workspace)
+inline int router_nb(int T, int d, int E, int x_dt, bool noisy) {
+  const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE;
+  const bool mf = x_dt == MOE_BF16 && !m8;
+  int kw8 = 1, tg8 = 1;
+  mf8_shape(T, d, noisy ? 1 : kM8Cpw, kw8, tg8);
+  return m8 ? (T + 16 * tg8 - 1) / (16 * tg8) : (mf ? (T + kFnTok - 1) / kFnTok : router_blocks(T));
+}
+
 // the launches of both entry points; arguments already validated.  noise ==
 // nullptr: the clean router.  bf16: MFMA kernels (up to 8 experts: whole
 // rows per block, one launch; otherwise the tiled logits GEMM, then the
@@ -865,7 +929,7 @@ int router_run(const void* x, int x_dt, const float* w_g, const float* b_g, cons
   float* part = static_cast<float*>(workspace);
   int kw8 = 1, tg8 = 1;
   mf8_shape(T, d, noisy ? 1 : kM8Cpw, kw8, tg8);
-  const int nb = m8 ? (T + 16 * tg8 - 1) / (16 * tg8) : (mf ? (T + kFnTok - 1) / kFnTok : router_blocks(T));
+  const int nb = router_nb(T, d, E, x_dt, noisy);
   RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg, w_n, b_n, noise, eps};
   if (T > 0 && m8) {
     if (noisy)
@@ -1032,6 +1096,21 @@ int moe_router_topk_noisy(const void* x, int x_dt, const float* w_g, const float
   // no tokens: only the (zero) column sums, as the clean router writes them
   return router_run(x, x_dt, w_g, b_g, w_n, b_n, T > 0 ? noise : nullptr, noise_eps, T, d, E, k, gate_mode,
                     topk_idx, topk_gate, prob_colsum, logits_dbg, workspace, stream);
+}
+
+int moe_aux_loss_from_router(const int32_t* counts_routed, const void* router_workspace, size_t workspace_bytes,
+                             int T, int d, int E, int x_dt, int noisy, int k, float alpha, float* prob_colsum,
+                             float* loss, hipStream_t stream) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kRtMaxE) return MOE_ERR_UNSUPPORTED;
+  if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!counts_routed || !loss || (prob_colsum && !aligned16(prob_colsum))) return MOE_ERR_INVALID_ARG;
+  const size_t need = noisy ? moe_router_noisy_workspace_size(T, d, E, x_dt) : moe_router_workspace_size(T, d, E, x_dt);
+  if (T > 0 && (!router_workspace || workspace_bytes < need || !aligned16(router_workspace))) return MOE_ERR_WORKSPACE;
+  const int nb = T > 0 ? router_nb(T, d, E, x_dt, noisy != 0) : 0;
+  hipLaunchKernelGGL(aux_from_parts_kernel, dim3(1), dim3(256), 0, stream, static_cast<const float*>(router_workspace),
+                     nb, E, counts_routed, T, k, alpha, prob_colsum, loss);
+  return check_launch();
 }
 
 }  // extern "C"

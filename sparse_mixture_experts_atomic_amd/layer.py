@@ -61,6 +61,7 @@ class MoELayer:
         self.logits = None
         act = L.F32 if act_dtype == torch.float32 else L.BF16
         self.ws_router = self._ws(L.router_workspace_size(T, d, E, act), dev)
+        self._router_ws = (self.ws_router, False)   # the workspace aux() reads (noisy or not)
         self.ws_disp = self._ws(L.dispatch_workspace_size(T, k, E), dev)
         self.ws_ffn = self._ws(L.ffn_workspace_size(self.kind, act, A, E, d, d_ff, d_out), dev)
         if n_shared:
@@ -77,18 +78,24 @@ class MoELayer:
         return torch.zeros((max(int(n), 256),), dtype=torch.uint8, device=dev)
 
     # individual stages (the tests drive them one at a time) ----------------
-    def router(self, x):
+    def router(self, x, with_colsum=False):
+        """Router; its per-block probability column sums stay in the workspace
+        for aux() (one launch fewer), unless with_colsum asks the router to
+        reduce them into prob_colsum itself."""
         L.router_topk(x, self.w["w_g"], self.w.get("b_g"), self.k, self.gate, self.topk_idx, self.topk_gate,
-                      self.prob_colsum, self.logits, self.ws_router)
+                      self.prob_colsum if with_colsum else None, self.logits, self.ws_router)
+        self._router_ws = (self.ws_router, False)
 
-    def router_noisy(self, x, w_n, b_n, noise, eps=1e-2):
+    def router_noisy(self, x, w_n, b_n, noise, eps=1e-2, with_colsum=False):
         """Training-mode router with noisy gating: the same outputs as router(),
         from logits with noise[t, e] * (softplus(x W_n^T + b_n) + eps) added."""
         if getattr(self, "ws_router_noisy", None) is None:
             act = L.F32 if self.act_dtype == torch.float32 else L.BF16
             self.ws_router_noisy = self._ws(L.router_noisy_workspace_size(self.T, self.d, self.E, act), x.device)
         L.router_topk_noisy(x, self.w["w_g"], self.w.get("b_g"), w_n, b_n, noise, eps, self.k, self.gate,
-                            self.topk_idx, self.topk_gate, self.prob_colsum, None, self.ws_router_noisy)
+                            self.topk_idx, self.topk_gate, self.prob_colsum if with_colsum else None, None,
+                            self.ws_router_noisy)
+        self._router_ws = (self.ws_router_noisy, True)
 
     def dispatch(self, x, topk_idx=None):
         if self.gather_rows:
@@ -142,7 +149,12 @@ class MoELayer:
                   self.shared_y if shared_y is None else shared_y, self.n_shared, residual, self.y)
 
     def aux(self):
-        L.aux_loss(self.counts_routed, self.prob_colsum, self.T, self.k, self.E, self.alpha, self.loss)
+        """Balance loss and prob_colsum from the last router call's workspace
+        (moe_aux_loss_from_router: one launch for both)."""
+        ws, noisy = self._router_ws
+        act = L.F32 if self.act_dtype == torch.float32 else L.BF16
+        L.aux_loss_from_router(self.counts_routed, ws, self.T, self.d, self.E, act, noisy, self.k, self.alpha,
+                               self.loss, self.prob_colsum)
 
     # ---------------------------------------------------------------- training
     def enable_backward(self):

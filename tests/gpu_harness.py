@@ -147,7 +147,7 @@ class Run:
     # -- stages ---------------------------------------------------------------
     def check_router(self):
         cfg = self.cfg
-        self.layer.router(self.x)
+        self.layer.router(self.x, with_colsum=True)
         torch.cuda.synchronize()
         idx_g = self.layer.topk_idx.cpu().numpy()
         gate_g = self.layer.topk_gate.cpu().numpy().astype(np.float64)
@@ -301,6 +301,10 @@ class Run:
         self.layer.aux()
         torch.cuda.synchronize()
         got = float(self.layer.loss.item())
+        # the column sums the fused aux call forms from the router's workspace
+        # are the router's own, bit for bit
+        assert np.array_equal(self.layer.prob_colsum.cpu().numpy().astype(np.float64), self.colsum_g), \
+            f"{cfg.name}: prob_colsum from moe_aux_loss_from_router differs from the router's"
         ref = O.aux_loss(self.disp["counts_routed"], self.colsum_g, cfg.T, cfg.k, cfg.E, cfg.alpha)
         assert abs(got - ref) <= 1e-5 * max(abs(ref), 1e-30), f"{cfg.name}: aux {got} vs {ref}"
         # and from scratch (counts from the oracle's own routing)

@@ -191,3 +191,26 @@ def test_combine_and_aux_validation_before_launch():
     assert lib.moe_combine(f, L.BF16, f, f, 0, 2, 8, None, 0, None, f, None) == L.OK   # T = 0: nothing to do
     assert lib.moe_aux_loss(f, f, 4, 3, 2, 0.01, f, None) == L.ERR_INVALID_ARG
     assert lib.moe_aux_loss(None, f, 4, 1, 2, 0.01, f, None) == L.ERR_INVALID_ARG
+
+
+def test_aux_from_router_validation_before_launch():
+    lib = L.lib()
+    f = 1 << 20
+    g = lib.moe_aux_loss_from_router
+    need = L.router_workspace_size(4096, 4096, 8, L.BF16)
+
+    def call(cnt=f, ws=f, wsb=need, T=4096, d=4096, E=8, dt=L.BF16, noisy=0, k=2, pc=None, loss=f):
+        return g(cnt, ws, wsb, T, d, E, dt, noisy, k, 0.01, pc, loss, None)
+
+    assert call(k=9) == L.ERR_INVALID_ARG
+    assert call(cnt=None) == L.ERR_INVALID_ARG
+    assert call(loss=None) == L.ERR_INVALID_ARG
+    assert call(dt=7) == L.ERR_INVALID_ARG
+    assert call(pc=f + 4) == L.ERR_INVALID_ARG
+    assert call(E=512, k=2) == L.ERR_UNSUPPORTED
+    assert call(wsb=need - 1) == L.ERR_WORKSPACE
+    assert call(ws=None) == L.ERR_WORKSPACE
+    # the noisy router's workspace is the one checked when noisy = 1
+    need_n = L.router_noisy_workspace_size(4096, 4096, 8, L.BF16)
+    assert need_n > need
+    assert call(noisy=1, wsb=need) == L.ERR_WORKSPACE
