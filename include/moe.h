@@ -381,14 +381,15 @@ int moe_aux_loss(const int32_t* counts_routed, const float* prob_colsum, int T, 
  * The same loss straight from a router call's workspace, for callers that
  * pass prob_colsum = NULL to moe_router_topk or moe_router_topk_noisy: the
  * router then leaves its per-block probability column sums in the workspace
- * and launches nothing more, and this call forms the column sums (written to
- * prob_colsum when it is not NULL) and the loss in one launch.  Both equal,
- * bit for bit, what the router with prob_colsum followed by moe_aux_loss
- * give (the same fp64 partial sums and reduction trees).
+ * and launches nothing more.  This call forms the column sums into
+ * prob_colsum and the loss, in one launch for up to 32 experts (two beyond:
+ * a single block would be slower than the extra launch).  Both equal, bit
+ * for bit, what the router with prob_colsum followed by moe_aux_loss give
+ * (the same fp64 partial sums and reduction trees).
  *   router_workspace  the workspace of that router call, not written to
  *                     since; T, d, E, x_dt as passed to it; noisy = 1 for
  *                     moe_router_topk_noisy, 0 for moe_router_topk
- *   counts_routed [E] int32; prob_colsum [E] fp32 out or NULL; loss out
+ *   counts_routed [E] int32; prob_colsum [E] fp32 out (required); loss out
  * Errors as moe_aux_loss, plus MOE_ERR_WORKSPACE when T > 0 and the
  * workspace is smaller than that router call needs.
  */

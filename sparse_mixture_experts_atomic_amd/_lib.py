@@ -240,7 +240,7 @@ def aux_loss(counts_routed, prob_colsum, T, k, E, alpha, loss, stream=None):
     _check("moe_aux_loss", st)
 
 
-def aux_loss_from_router(counts_routed, router_workspace, T, d, E, x_dt, noisy, k, alpha, loss, prob_colsum=None,
+def aux_loss_from_router(counts_routed, router_workspace, T, d, E, x_dt, noisy, k, alpha, loss, prob_colsum,
                          stream=None):
     ws_bytes = router_workspace.numel() * router_workspace.element_size()
     st = lib().moe_aux_loss_from_router(_p(counts_routed), _p(router_workspace), ws_bytes, T, d, E, x_dt,

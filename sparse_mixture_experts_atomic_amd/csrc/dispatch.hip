@@ -167,6 +167,10 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const V* __restrict__
 // wait.  The block's rows of x are loaded into registers first, so their HBM
 // latency overlaps the index work; each row is then stored to its kept
 // slots.  Same outputs as the count/rank/permute path, bit for bit.
+// PRE: for more than 8 experts, where counting every id in every block
+// takes an LDS atomic per id, the per-256-token-block counts come from
+// dispatch_count_kernel (one launch before) and a block sums those, counting
+// only the ids of its own 256-token block that precede its tokens.
 // at most 63 int4 loads + 1 tail id = 253 ids per thread, so the packed 8-bit
 // per-thread counts below cannot overflow
 // Sum of v over the 64 lanes of a wavefront, valid in lane 63: quad
@@ -188,11 +192,12 @@ constexpr int kIdPre = 8;                      // int4 id loads per thread issue
 constexpr int kFusedThreads = 256;
 constexpr int kFusedMaxVec = 16;               // row vectors per thread (the largest NQ instance)
 
-template <int NQ>
+template <int NQ, bool PRE>
 __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int C, int tpb, const uint4* __restrict__ x, int nvec,
     uint4* __restrict__ xp, int32_t* __restrict__ counts_routed, int32_t* __restrict__ counts_kept,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ dest_pos, int32_t* __restrict__ perm_token) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dest_pos, int32_t* __restrict__ perm_token,
+    const int32_t* __restrict__ block_counts, int nbc) {
   __shared__ int before[kDsMaxE];
   __shared__ int total[kDsMaxE];
   __shared__ int off[kDsMaxE];
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
     const int j = tid + kFusedThreads * u;
     int i4 = j + rot;
     if (i4 >= n4) i4 -= n4;
-    iv[u] = j < n4 ? reinterpret_cast<const int4*>(idx)[i4] : make_int4(-1, -1, -1, -1);
+    iv[u] = (!PRE && j < n4) ? reinterpret_cast<const int4*>(idx)[i4] : make_int4(-1, -1, -1, -1);
   }
   const int nb_ent = (t1 - t0) * k;
   const int my_ent = tid < nb_ent ? idx[static_cast<size_t>(t0) * k + tid] : -1;
@@ -237,7 +242,26 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
     }
   }
 
-  // 3. expert totals and counts before t0, from all T*k ids
+  // 3. expert totals and counts before t0, from all T*k ids (PRE: from the
+  //    per-256-token-block counts and the ids of t0's block before t0)
+  if constexpr (PRE) {
+    const int cb = t0 / kDsTok;
+    for (int e = tid; e < E; e += kFusedThreads) {
+      int tot = 0, bef = 0;
+      for (int b = 0; b < nbc; ++b) {
+        const int c = block_counts[static_cast<size_t>(b) * E + e];
+        tot += c;
+        bef += b < cb ? c : 0;
+      }
+      total[e] = tot;
+      before[e] = bef;
+    }
+    __syncthreads();
+    for (int i = cb * kDsTok * k + tid; i < n_before; i += kFusedThreads) {
+      const int e = idx[i];
+      if (e >= 0 && e < E) atomicAdd(&before[e], 1);
+    }
+  } else {
   for (int e = tid; e < E; e += kFusedThreads) {
     before[e] = 0;
     total[e] = 0;
@@ -331,24 +355,32 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
     }
     for (int i = 4 * n4 + tid; i < n_all; i += kFusedThreads) count(i, idx[i]);
   }
+  }
   if (tid < nb_ent) ent[tid] = my_ent;
   __syncthreads();
 
   // 3. kept counts and their exclusive scan over experts (offsets)
   if (E <= 64) {
-    if (tid == 0) {
-      int prefix = 0;
-      for (int e = 0; e < E; ++e) {
-        const int kept = C < 0 ? total[e] : min(total[e], C);
-        off[e] = prefix;
-        if (blockIdx.x == 0) {
-          counts_routed[e] = total[e];
-          counts_kept[e] = kept;
-          offsets[e] = prefix;
-        }
-        prefix += kept;
+    // one wavefront, lane e = expert e: kept counts, then an inclusive scan
+    // by shuffles (exclusive = inclusive - own)
+    if (wave == 0) {
+      const int tot = lane < E ? total[lane] : 0;
+      const int kept = C < 0 ? tot : min(tot, C);
+      int incl = kept;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
       }
-      if (blockIdx.x == 0) offsets[E] = prefix;
+      if (lane < E) {
+        off[lane] = incl - kept;
+        if (blockIdx.x == 0) {
+          counts_routed[lane] = tot;
+          counts_kept[lane] = kept;
+          offsets[lane] = incl - kept;
+        }
+      }
+      if (blockIdx.x == 0 && lane == E - 1) offsets[E] = incl;
     }
   } else {
   const int per = (E + kFusedThreads - 1) / kFusedThreads;
@@ -481,12 +513,27 @@ int moe_dispatch_permute(const int32_t* topk_idx, int T, int k, int E, int capac
     const int nblk = (T + tpb - 1) / tpb;
     const uint4* xv = copy_rows ? static_cast<const uint4*>(x) : nullptr;
     uint4* xpv = copy_rows ? static_cast<uint4*>(x_perm) : nullptr;
-#define MOE_FUSED(NQ)                                                                                            \
-  hipLaunchKernelGGL(dispatch_fused_kernel<NQ>, dim3(nblk), dim3(kFusedThreads), 0, stream, topk_idx, T, k, E,  \
-                     capacity, tpb, xv, nvec, xpv, counts_routed, counts_kept, offsets, dest_pos, perm_token)
-    if (nq <= 4) MOE_FUSED(4);
-    else if (nq <= 8) MOE_FUSED(8);
-    else MOE_FUSED(16);
+    // more than 8 experts and more than 4096 ids: count once per 256-token
+    // block first (dispatch_count_kernel) instead of every id in every block
+    const bool pre = E > kPackedE && static_cast<long>(T) * k > 4096;
+    if (pre) {
+      hipLaunchKernelGGL(dispatch_count_kernel, dim3(nb), dim3(kDsTok), 0, stream, topk_idx, T, k, E, bc);
+      const int st = check_launch();
+      if (st != MOE_OK) return st;
+    }
+#define MOE_FUSED(NQ, PRE)                                                                                       \
+  hipLaunchKernelGGL((dispatch_fused_kernel<NQ, PRE>), dim3(nblk), dim3(kFusedThreads), 0, stream, topk_idx, T, \
+                     k, E, capacity, tpb, xv, nvec, xpv, counts_routed, counts_kept, offsets, dest_pos,          \
+                     perm_token, static_cast<const int32_t*>(bc), nb)
+    if (pre) {
+      if (nq <= 4) MOE_FUSED(4, true);
+      else if (nq <= 8) MOE_FUSED(8, true);
+      else MOE_FUSED(16, true);
+    } else {
+      if (nq <= 4) MOE_FUSED(4, false);
+      else if (nq <= 8) MOE_FUSED(8, false);
+      else MOE_FUSED(16, false);
+    }
 #undef MOE_FUSED
     return check_launch();
   }

@@ -814,58 +814,73 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* part, i
 }
 
 // Column sums and balance loss in one launch, from the per-block partial
-// column sums a router call left in its workspace.  Every column sum is
-// formed exactly as colsum_reduce_kernel forms it (256 strided fp64 partial
-// sums, then the same tree), 8 experts per round, and the loss exactly as
-// aux_loss_kernel forms it, so both equal what moe_router_topk with
-// prob_colsum followed by moe_aux_loss give, bit for bit.
-constexpr int kAxChunk = 8;
+// column sums a router call left in its workspace, for up to ME experts.
+// Every column sum is formed exactly as colsum_reduce_kernel forms it (256
+// strided fp64 partial sums over the blocks, then the same tree: the two
+// cross-wavefront steps in LDS, the other six by shuffles in wavefront 0,
+// which pair the same lanes), and the loss exactly as aux_loss_kernel forms
+// it (its tree steps of 32 and more only add zeros here), so both equal what
+// moe_router_topk with prob_colsum followed by moe_aux_loss give, bit for
+// bit.  Loads and LDS accesses are unconditional (clamped addresses):
+// predicated ones compiled into a branch and a wait per element.
+template <int ME>
 __global__ __launch_bounds__(256) void aux_from_parts_kernel(const float* __restrict__ part, int nb, int E,
                                                              const int32_t* __restrict__ counts, int T_, int k,
                                                              float alpha, float* __restrict__ prob_colsum,
                                                              float* __restrict__ loss) {
-  __shared__ double red[kAxChunk][256];
-  __shared__ float csum[kRtMaxE];
-  __shared__ float fred[256];
+  __shared__ double red[ME][256];
+  __shared__ float csum[ME];
   const int i = threadIdx.x;
-  for (int e0 = 0; e0 < E; e0 += kAxChunk) {
+  const int lane = i & 63;
+  double acc[ME];
 #pragma unroll
-    for (int c = 0; c < kAxChunk; ++c) {
-      const int e = e0 + c;
-      double sum = 0.0;
-      if (e < E)
-        for (int b = i; b < nb; b += 256) sum += static_cast<double>(part[static_cast<size_t>(b) * E + e]);
-      red[c][i] = sum;
-    }
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (i < o) {
+  for (int c = 0; c < ME; ++c) acc[c] = 0.0;
+  for (int b = i; b < nb; b += 256) {
+    float v[ME];
 #pragma unroll
-        for (int c = 0; c < kAxChunk; ++c) red[c][i] += red[c][i + o];
-      }
-      __syncthreads();
-    }
-    if (i < kAxChunk && e0 + i < E) {
-      const float v = static_cast<float>(red[i][0]);
-      csum[e0 + i] = v;
-      if (prob_colsum) prob_colsum[e0 + i] = v;
-    }
-    __syncthreads();
+    for (int c = 0; c < ME; ++c) v[c] = part[static_cast<size_t>(b) * E + min(c, E - 1)];
+#pragma unroll
+    for (int c = 0; c < ME; ++c) acc[c] += static_cast<double>(v[c]);
   }
+#pragma unroll
+  for (int c = 0; c < ME; ++c) red[c][i] = acc[c];
+  __syncthreads();
+  if (i < 128) {
+    double x1[ME];
+#pragma unroll
+    for (int c = 0; c < ME; ++c) x1[c] = red[c][i + 128];
+#pragma unroll
+    for (int c = 0; c < ME; ++c) red[c][i] = acc[c] + x1[c];
+  }
+  __syncthreads();
+  if (i >= 64) return;
+  double v[ME];
+#pragma unroll
+  for (int c = 0; c < ME; ++c) v[c] = red[c][lane] + red[c][lane + 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int c = 0; c < ME; ++c) v[c] += __shfl_down(v[c], o);
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c < ME; ++c) csum[c] = static_cast<float>(v[c]);
+  }
+  // the lanes of this wavefront read what lane 0 wrote: LDS operations of a
+  // wavefront complete in order; the fence keeps the reads after the writes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  const float cs = csum[min(lane, ME - 1)];
+  if (lane < E) prob_colsum[lane] = cs;
   float sv = 0.f;
-  if (T_ > 0) {
+  if (T_ > 0 && lane < E) {
     const float inv_tk = 1.0f / (static_cast<float>(T_) * static_cast<float>(k));
     const float inv_t = 1.0f / static_cast<float>(T_);
-    for (int e = i; e < E; e += 256) sv += (static_cast<float>(counts[e]) * inv_tk) * (csum[e] * inv_t);
+    sv = (static_cast<float>(counts[lane]) * inv_tk) * (cs * inv_t);
   }
-  fred[i] = sv;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (i < o) fred[i] += fred[i + o];
-    __syncthreads();
-  }
-  if (i == 0) *loss = alpha * static_cast<float>(E) * fred[0];
+#pragma unroll
+  for (int o = ME / 2; o > 0; o >>= 1) sv += __shfl_down(sv, o);
+  if (lane == 0) *loss = alpha * static_cast<float>(E) * sv;
 }
+constexpr int kAxMaxE = 32;
 
 inline int router_blocks(int T) { return (T + kRtTok - 1) / kRtTok; }
 
@@ -1104,13 +1119,27 @@ int moe_aux_loss_from_router(const int32_t* counts_routed, const void* router_wo
   if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (E > kRtMaxE) return MOE_ERR_UNSUPPORTED;
   if (x_dt != MOE_F32 && x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (!counts_routed || !loss || (prob_colsum && !aligned16(prob_colsum))) return MOE_ERR_INVALID_ARG;
+  if (!counts_routed || !loss || !prob_colsum || !aligned16(prob_colsum)) return MOE_ERR_INVALID_ARG;
   const size_t need = noisy ? moe_router_noisy_workspace_size(T, d, E, x_dt) : moe_router_workspace_size(T, d, E, x_dt);
   if (T > 0 && (!router_workspace || workspace_bytes < need || !aligned16(router_workspace))) return MOE_ERR_WORKSPACE;
   const int nb = T > 0 ? router_nb(T, d, E, x_dt, noisy != 0) : 0;
-  hipLaunchKernelGGL(aux_from_parts_kernel, dim3(1), dim3(256), 0, stream, static_cast<const float*>(router_workspace),
-                     nb, E, counts_routed, T, k, alpha, prob_colsum, loss);
-  return check_launch();
+  if (E <= kAxMaxE) {
+    const float* part = static_cast<const float*>(router_workspace);
+    if (E <= 8)
+      hipLaunchKernelGGL(aux_from_parts_kernel<8>, dim3(1), dim3(256), 0, stream, part, nb, E, counts_routed, T, k,
+                         alpha, prob_colsum, loss);
+    else
+      hipLaunchKernelGGL(aux_from_parts_kernel<32>, dim3(1), dim3(256), 0, stream, part, nb, E, counts_routed, T, k,
+                         alpha, prob_colsum, loss);
+    return check_launch();
+  }
+  // more experts: one block per expert for the column sums (a single block
+  // is slower there than the extra launch), then the loss
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3(E), dim3(256), 0, stream, static_cast<const float*>(router_workspace),
+                     nb, E, prob_colsum);
+  const int st = check_launch();
+  if (st != MOE_OK) return st;
+  return moe_aux_loss(counts_routed, prob_colsum, T, k, E, alpha, loss, stream);
 }
 
 }  // extern "C"

@@ -199,7 +199,7 @@ def test_aux_from_router_validation_before_launch():
     g = lib.moe_aux_loss_from_router
     need = L.router_workspace_size(4096, 4096, 8, L.BF16)
 
-    def call(cnt=f, ws=f, wsb=need, T=4096, d=4096, E=8, dt=L.BF16, noisy=0, k=2, pc=None, loss=f):
+    def call(cnt=f, ws=f, wsb=need, T=4096, d=4096, E=8, dt=L.BF16, noisy=0, k=2, pc=f, loss=f):
         return g(cnt, ws, wsb, T, d, E, dt, noisy, k, 0.01, pc, loss, None)
 
     assert call(k=9) == L.ERR_INVALID_ARG
@@ -207,6 +207,7 @@ def test_aux_from_router_validation_before_launch():
     assert call(loss=None) == L.ERR_INVALID_ARG
     assert call(dt=7) == L.ERR_INVALID_ARG
     assert call(pc=f + 4) == L.ERR_INVALID_ARG
+    assert call(pc=None) == L.ERR_INVALID_ARG
     assert call(E=512, k=2) == L.ERR_UNSUPPORTED
     assert call(wsb=need - 1) == L.ERR_WORKSPACE
     assert call(ws=None) == L.ERR_WORKSPACE

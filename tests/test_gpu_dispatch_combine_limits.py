@@ -97,3 +97,23 @@ def test_combine_beyond_the_grid_y_limit(dtype):
     tol = 1e-5 if dtype == torch.float32 else 2e-2
     assert err <= tol, f"combine T={T}: err {err:.3e}"
     say(f"combine T={T} {dtype}: err {err:.2e}, dropped slots {int((disp['dest_pos'] < 0).sum())}")
+
+
+@pytest.mark.parametrize("T,k,E,C,skew", [(1000, 6, 16, -1, False), (777, 6, 100, 40, True),
+                                          (4096, 6, 64, -1, True), (3000, 2, 9, 500, True)])
+def test_dispatch_with_precounted_blocks(T, k, E, C, skew):
+    """More than 8 experts and more than 4096 ids: the one-launch kernel takes
+    its counts from the per-256-token-block counts of a launch before it;
+    token ranges that straddle those blocks, capacity drops, skewed loads."""
+    name = f"dispatch precount T={T} k={k} E={E} C={C}"
+    say(f"[case] {name}")
+    rng = np.random.default_rng(T + E)
+    if skew:
+        # a few experts take most of the assignments
+        p = rng.random(E) ** 6
+        p /= p.sum()
+        idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    else:
+        idx = _distinct_ids(rng, T, k, E)
+    x = torch.from_numpy(rng.standard_normal((T, 256)).astype(np.float32)).to(torch.bfloat16).to("cuda")
+    _check_dispatch(name, idx, E, C, x)
