@@ -1110,28 +1110,38 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
 // wavefronts of 128 x 128 (4 x 4 fragments, 256 accumulator registers).  A
 // k-step is 64 values: a lane supplies 32 bytes of its row (row lane % 32,
 // k-half lane / 32), read as two 16-byte chunks; A and B use the same lane
-// to k mapping, which is all the product needs.  Two LDS stages of 64 KB:
-//   k-step 0 of stage s: 16 MFMAs, reading k-step 1's fragments meanwhile;
-//   wait for stage s + 1's DMAs, barrier (every wavefront is done with
-//   stage s's buffer);
-//   k-step 1: 16 MFMAs, issuing stage s + 2's DMAs into the freed buffer
-//   (one per MFMA) and reading stage s + 1's k-step 0 fragments.
+// to k mapping, which is all the product needs.
+// The stages move through the bf16 kernel's ring of five 32 KB half-slots
+// (stage s: A in half-slot (2 s) % 5, B in (2 s + 1) % 5) with its issue
+// schedule: two k-steps of 16 MFMAs per stage; the window from barrier s to
+// barrier s + 1 (the 14 MFMAs after barrier s, k-step 0 of stage s + 1 and
+// the first 2 MFMAs of its k-step 1) issues B(s + 2) over its first half into
+// A(s)'s half-slot and A(s + 3) over its second half into B(s)'s, one DMA per
+// two MFMAs; the fragment reads of the next k-step go one per MFMA.  (A
+// double buffer of two 64 KB stages waited for the next stage's DMAs in the
+// middle of every stage: 40-53% MFMA busy.)
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 constexpr int kF8BK = 128;         // K values (bytes) per stage
-constexpr int kF8Stage = 256 * kF8BK / 16;   // uint4 per operand and stage
-// LDS: two stages of A and B (128 KB), reused after the loop by the
-// epilogue's staging (four wavefronts of 128 rows x 136 bf16 = 136 KB)
-constexpr int kF8Lds = 4 * 128 * (128 + 8) * 2 / 16 > 4 * kF8Stage ? 4 * 128 * (128 + 8) * 2 / 16 : 4 * kF8Stage;
+constexpr int kF8Half = 256 * kF8BK / 16;    // uint4 per half-slot (one operand of one stage)
+// the epilogue's staging (four wavefronts of 128 rows x 136 bf16 = 136 KB)
+// and the row scales (2 KB) after it reuse the ring
+constexpr int kF8Stg = 4 * 128 * (128 + 8) * 2;
+static_assert(kF8Stg + 4 * 128 * 4 <= 5 * kF8Half * 16, "epilogue staging and row scales fit in the ring");
 
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams p) {
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   constexpr int CH = 8;                      // 16-byte chunks per LDS row
   constexpr int ND = 256 * CH / kThreads;    // DMA instructions per operand and stage (8)
-  __shared__ uint4 ldsm[kF8Lds];             // [buffer][A, B][256 rows x 8 chunks], then the epilogue staging
-  __shared__ float rsl[4][128];              // row scales of each wavefront's rows
-  static_assert(kF8Lds * 16 + 4 * 128 * 4 <= 160 * 1024, "LDS");
-  auto lds = [&](int buf, int op) __attribute__((always_inline)) { return ldsm + (buf * 2 + op) * kF8Stage; };
+  constexpr int HALF = kF8Half;
+  constexpr int NQ = 16;                     // MFMAs per k-step
+  constexpr int NKS = 2;                     // k-steps per stage
+  constexpr int kPre = 2;                    // MFMAs of the last k-step before the barrier
+  constexpr int NM = NQ - kPre;              // and after it
+  constexpr int WIN = NQ * NKS;              // window positions
+  constexpr int SP = WIN / 2 / ND;           // window positions between DMAs of one operand
+  static_assert(SP * ND == WIN / 2 && WIN / 2 + (ND - 1) * SP <= WIN - kPre, "window layout");
+  __shared__ uint4 ring[5 * HALF];           // 160 KB
 
   const int n_tiles = (p.N + HC - 1) / HC;
   const int m_total = p.ts[p.E];
@@ -1175,23 +1185,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
   const char* b_sb3 = EPI == EPI_SWIGLU ? uniform_ptr(static_cast<const char*>(p.B3) + static_cast<size_t>(e) * N * K)
                                         : b_sb1;
   const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
-  auto issue = [&](int st, int buf, int q) __attribute__((always_inline)) {
-    // q < ND: A instruction q; else B instruction q - ND (SwiGLU: rows 64..127
-    // of each 128-row half are up rows)
-    if (q < ND) {
-      dma16(a_sb + st * kF8BK, a_vo[q], lds_addr(lds(buf, 0) + q * 256) + wave_lds);
-    } else {
-      const int i = q - ND;
-      const char* bb = (EPI == EPI_SWIGLU && ((i * 32) & 64)) ? b_sb3 : b_sb1;
-      dma16(bb + st * kF8BK, b_vo[i], lds_addr(lds(buf, 1) + i * 256) + wave_lds);
-    }
+  auto hs = [](int c) __attribute__((always_inline)) { return c >= 5 ? c - 5 : c; };
+  auto issue_a = [&](int st, int h, int q) __attribute__((always_inline)) {
+    dma16(a_sb + st * kF8BK, a_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
   };
-  // fragment of k-step ks: rows rb + fr, chunks 4 ks + 2 fc (+ 1)
-  auto read_frag = [&](const uint4* S, int row, int ks) __attribute__((always_inline)) {
-    const uint4 lo = S[dma_swz<CH>(row, 4 * ks + 2 * fc)];
-    const uint4 hi = S[dma_swz<CH>(row, 4 * ks + 2 * fc + 1)];
-    return i32x8_t{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                   static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  // SwiGLU: rows 64..127 of each 128-row half are up rows
+  auto issue_b = [&](int st, int h, int q) __attribute__((always_inline)) {
+    const char* bb = (EPI == EPI_SWIGLU && ((q * 32) & 64)) ? b_sb3 : b_sb1;
+    dma16(bb + st * kF8BK, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+  };
+  // chunk c (0..15) of k-step ks's fragments: fragment c / 2 (A 0..3, B
+  // 4..7), its 16-byte half c % 2 (chunk 4 ks + 2 fc + c % 2 of the row)
+  auto read_chunk = [&](const uint4* SA, const uint4* SB, int ks, int c, i32x8_t (&f)[8])
+      __attribute__((always_inline)) {
+    const int r = c >> 1, h = c & 1;
+    const uint4 v = r < 4 ? SA[dma_swz<CH>(wm * 128 + r * 32 + fr, 4 * ks + 2 * fc + h)]
+                          : SB[dma_swz<CH>(wn * 128 + (r - 4) * 32 + fr, 4 * ks + 2 * fc + h)];
+    f[r][4 * h] = static_cast<int>(v.x);
+    f[r][4 * h + 1] = static_cast<int>(v.y);
+    f[r][4 * h + 2] = static_cast<int>(v.z);
+    f[r][4 * h + 3] = static_cast<int>(v.w);
   };
   f32x16_t acc[4][4];
 #pragma unroll
@@ -1202,66 +1215,119 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   // a wavefront whose rows all lie past the segment's end skips its MFMAs
   const bool wave_rows = wm * 128 < rows_valid;
-  i32x8_t f0[8], f1[8];                      // fragments: A 0..3, B 4..7
-  auto read_all = [&](i32x8_t (&f)[8], int buf, int ks, int r) __attribute__((always_inline)) {
-    if (r < 4) f[r] = read_frag(lds(buf, 0), wm * 128 + r * 32 + fr, ks);
-    else f[r] = read_frag(lds(buf, 1), wn * 128 + (r - 4) * 32 + fr, ks);
-  };
   auto mma = [&](const i32x8_t (&f)[8], int q) __attribute__((always_inline)) {
     const int i = q >> 2, j = q & 3;
     if (wave_rows)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[i], f[4 + j], acc[i][j], 0, 0, 0, 127, 0, 127);
   };
+  i32x8_t f0[8], f1[8];                      // k-step 0 and k-step 1 fragments
 
-  // prologue: stages 0 and 1 in flight, wait for stage 0
+  // One stage; flags as in the bf16 kernel: NEXT = stage s + 1 exists; PREB /
+  // PREA = this stage issues the rest of B(s + 1) / A(s + 2) (window s - 1);
+  // POSTB = B(s + 2)'s first part after barrier s; WAITN = DMAs allowed in
+  // flight at the wait (A(s + 2), issued last).
+  auto stage = [&](auto next, auto preb, auto prea, auto postb, auto waitn, int s, int cA)
+      __attribute__((always_inline)) {
+    const uint4* Ac = ring + cA * HALF;
+    const uint4* Bc = ring + hs(cA + 1) * HALF;
+    const uint4* An = ring + hs(cA + 2) * HALF;
+    const uint4* Bn = ring + hs(cA + 3) * HALF;
+    const int h_preb = hs(cA + 3);
+    const int h_prea = hs(cA + 4);
+    auto pre_dma = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < WIN / 2 && i % SP == 0 && decltype(preb)::value) issue_b(s + 1, h_preb, i / SP);
+      if constexpr (i >= WIN / 2 && (i - WIN / 2) % SP == 0 && decltype(prea)::value)
+        issue_a(s + 2, h_prea, (i - WIN / 2) / SP);
+    };
+    // k-step 0 (f0), reading k-step 1's fragments into f1
+    template_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      mma(f0, q);
+      read_chunk(Ac, Bc, 1, q, f1);
+      pre_dma(std::integral_constant<int, NM + q>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // k-step 1 (f1): kPre MFMAs, the wait and barrier s, then the rest with
+    // stage s + 1's k-step 0 fragments into f0
+    template_for<kPre>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      mma(f1, q);
+      pre_dma(std::integral_constant<int, WIN - kPre + q>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    wait_vmcnt<decltype(waitn)::value>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    template_for<NM>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      mma(f1, kPre + q);
+      if constexpr (decltype(next)::value) {
 #pragma unroll
-  for (int q = 0; q < 2 * ND; ++q) issue(0, 0, q);
+        for (int c = q * 16 / NM; c < (q + 1) * 16 / NM; ++c) read_chunk(An, Bn, 0, c, f0);
+      }
+      if constexpr (q % SP == 0 && decltype(postb)::value) issue_b(s + 2, cA, q / SP);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using W0 = std::integral_constant<int, 0>;
+  using WA = std::integral_constant<int, ND>;
+  // prologue: A(0), B(0), A(1), B(1), A(2) into half-slots 0 .. 4; wait for stage 0
+#pragma unroll
+  for (int q = 0; q < ND; ++q) issue_a(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < ND; ++q) issue_b(0, 1, q);
   if (KT > 1) {
 #pragma unroll
-    for (int q = 0; q < 2 * ND; ++q) issue(1, 1, q);
+    for (int q = 0; q < ND; ++q) issue_a(1, 2, q);
+#pragma unroll
+    for (int q = 0; q < ND; ++q) issue_b(1, 3, q);
+  }
+  if (KT > 2) {
+#pragma unroll
+    for (int q = 0; q < ND; ++q) issue_a(2, 4, q);
+    wait_vmcnt<3 * ND>();
+  } else if (KT > 1) {
     wait_vmcnt<2 * ND>();
   } else {
     wait_vmcnt<0>();
   }
   lds_barrier();
 #pragma unroll
-  for (int r = 0; r < 8; ++r) read_all(f0, 0, 0, r);
-  for (int s = 0; s < KT; ++s) {
-    const int buf = s & 1;
-    // k-step 0 on f0; k-step 1's fragments into f1
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mma(f0, q);
-      if (q < 8) read_all(f1, buf, 1, q);
-      __builtin_amdgcn_sched_barrier(0);
+  for (int c = 0; c < 16; ++c) read_chunk(ring, ring + HALF, 0, c, f0);
+  if (KT == 1) {
+    stage(F_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
+  } else if (KT == 2) {
+    stage(T_{}, F_{}, F_{}, F_{}, W0{}, 0, 0);
+    stage(F_{}, F_{}, F_{}, F_{}, W0{}, 1, 2);
+  } else {
+    stage(T_{}, F_{}, F_{}, T_{}, WA{}, 0, 0);
+    int cA = 2;
+    for (int s = 1; s <= KT - 3; ++s) {
+      stage(T_{}, T_{}, T_{}, T_{}, WA{}, s, cA);
+      cA = hs(cA + 2);
     }
-    // stage s + 1 landed (this wavefront's DMAs) and every wavefront is done
-    // with stage s's buffer
-    wait_vmcnt<0>();
-    lds_barrier();
-    const bool next = s + 1 < KT, next2 = s + 2 < KT;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mma(f1, q);
-      if (next2) issue(s + 2, buf, q);
-      if (next && q < 8) read_all(f0, buf ^ 1, 0, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // s = KT - 2: only the rest of B(KT - 1) left to issue
+    stage(T_{}, T_{}, F_{}, F_{}, W0{}, KT - 2, cA);
+    stage(F_{}, F_{}, F_{}, F_{}, W0{}, KT - 1, hs(cA + 2));
   }
-  // epilogue: the buffers are free (no DMA in flight, the last reads came
-  // before the last barrier); row scales of the wavefront's rows into LDS
-  lds_barrier();
+  // the ring is free (the last LDS reads of every wavefront came before the
+  // last barrier, no DMA is in flight): row scales of the wavefront's rows
+  // after the staging area, then the epilogue
+  float* rsl = reinterpret_cast<float*>(reinterpret_cast<char*>(ring) + kF8Stg) + wave * 128;
   for (int r = lane; r < 128; r += 64) {
     const int lr = min(wm * 128 + r, rows_valid - 1);
     const int grow = row0 + lr;
     const int src = gat ? min(max(p.gather[grow], 0), p.a_rows - 1) : (p.a_shared ? grow - seg0 : grow);
-    rsl[wave][r] = p.row_scale[src];
+    rsl[r] = p.row_scale[src];
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
   const int col0 = EPI == EPI_SWIGLU ? nt * HC + wn * 64 : nt * 256 + wn * 128;
-  wave_epilogue<EPI, 4, true>(acc, reinterpret_cast<uint16_t*>(ldsm) + wave * 128 * (OC + 8), p, e,
-                              row0 + wm * 128, rows_valid - wm * 128, col0, rsl[wave]);
+  wave_epilogue<EPI, 4, true>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * (OC + 8), p, e,
+                              row0 + wm * 128, rows_valid - wm * 128, col0, rsl);
 }
 
 template <int EPI, int BK, bool FP8>
