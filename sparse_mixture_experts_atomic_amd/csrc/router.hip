@@ -195,6 +195,96 @@ __device__ __forceinline__ float token8_softmax_topk(float z, int e, int t, cons
   return p;
 }
 
+// All-reductions over a row of 16 lanes (gfx9 DPP: quad butterflies, then
+// rotations by 4 and 8 within the row; every lane ends with the result).
+template <int CTRL>
+__device__ __forceinline__ float dpp_r(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_ri(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_r<0xb1>(v));
+  v = fmaxf(v, dpp_r<0x4e>(v));
+  v = fmaxf(v, dpp_r<0x124>(v));              // row_ror:4
+  return fmaxf(v, dpp_r<0x128>(v));           // row_ror:8
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_r<0xb1>(v);
+  v += dpp_r<0x4e>(v);
+  v += dpp_r<0x124>(v);
+  return v + dpp_r<0x128>(v);
+}
+template <int CTRL>
+__device__ __forceinline__ void row16_argmax_step(float& bv, int& bi) {
+  const float ov = dpp_r<CTRL>(bv);
+  const int oi = dpp_ri<CTRL>(bi);
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+__device__ __forceinline__ void row16_argmax(float& bv, int& bi) {
+  row16_argmax_step<0xb1>(bv, bi);
+  row16_argmax_step<0x4e>(bv, bi);
+  row16_argmax_step<0x124>(bv, bi);
+  row16_argmax_step<0x128>(bv, bi);
+}
+
+// fp32 softmax and top-k of one token's logits z[0..E) by a row of 16 lanes
+// (E <= 16 NS, k <= 16): lane l of the row holds experts l + 16 i.  k rounds
+// of a row arg-max (largest logit, lower id on ties); lane j of the row keeps
+// the winner of round j.  Writes the token's outputs and its probabilities
+// to pr[0..E).  Four tokens per wavefront at once, where one token per
+// wavefront left 48 of 64 lanes idle in every reduction.
+template <int NS>
+__device__ __forceinline__ void token16_softmax_topk(const float* z, int t, const RouterArgs& a, float* pr, int l) {
+  float zr[NS], ex[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) zr[i] = l + 16 * i < a.E ? z[l + 16 * i] : -INFINITY;
+  float m = zr[0];
+#pragma unroll
+  for (int i = 1; i < NS; ++i) m = fmaxf(m, zr[i]);
+  m = row16_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    ex[i] = l + 16 * i < a.E ? expf(zr[i] - m) : 0.f;
+    s += ex[i];
+  }
+  s = row16_sum(s);
+  const float inv = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = l + 16 * i;
+    if (e < a.E) {
+      if (a.logits_dbg) a.logits_dbg[static_cast<size_t>(t) * a.E + e] = zr[i];
+      pr[e] = ex[i] * inv;
+    }
+  }
+  uint32_t taken = 0;
+  float myp = 0.f, psum = 0.f;
+  int myi = 0;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int e = l + 16 * i;
+      if (e < a.E && !((taken >> i) & 1u) && better(zr[i], e, bv, bi)) { bv = zr[i]; bi = e; }
+    }
+    row16_argmax(bv, bi);
+    const float p = expf(bv - m) * inv;
+    if ((bi & 15) == l) taken |= 1u << (bi >> 4);
+    if (l == j) { myp = p; myi = bi; }
+    psum += p;
+  }
+  if (l < a.k) {
+    const size_t o = static_cast<size_t>(t) * a.k + l;
+    a.topk_idx[o] = myi;
+    a.topk_gate[o] = a.mode == MOE_GATE_RENORM ? myp / psum : myp;
+  }
+}
+
 // One block = 32 tokens x all E experts.  Logits are accumulated in
 // registers (2 tokens x 4 experts per thread per 64-expert group) from LDS
 // tiles of x and W_g, then kept in LDS for the softmax/top-k phase, which
@@ -760,6 +850,26 @@ __global__ __launch_bounds__(kFnThreads) void router_finish_kernel(RouterArgs a,
     if (j < n_ent) lg[j] = z[u];
   }
   __syncthreads();
+  if (a.k <= 16) {
+    // a row of 16 lanes per token (waves 0-3 take the block's 16 tokens), the
+    // probabilities to LDS (pr aliases lg: each row reads its own token's
+    // logits into registers before writing), column sums in token order
+    float* pr = lg;
+    if (tid < 16 * kFnTok) {
+      const int tl = tid >> 4;
+      const int t = t0 + tl;
+      if (t < a.T) token16_softmax_topk<kRtMaxE / 16>(lg + tl * a.E, t, a, pr + tl * a.E, tid & 15);
+      else
+        for (int e = tid & 15; e < a.E; e += 16) pr[tl * a.E + e] = 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < a.E; e += kFnThreads) {
+      float v = 0.f;
+      for (int tl = 0; tl < kFnTok; ++tl) v += pr[tl * a.E + e];
+      a.colsum_part[static_cast<size_t>(blockIdx.x) * a.E + e] = v;
+    }
+    return;
+  }
   for (int tl = wave; tl < kFnTok; tl += kFnWaves) {
     const int t = t0 + tl;
     if (t >= a.T) break;
