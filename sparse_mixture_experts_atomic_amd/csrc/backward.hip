@@ -470,13 +470,60 @@ int moe_permute_backward(const void* dx_rows, int dt, const int32_t* dest_pos, i
 namespace moe {
 namespace {
 
-// workspace: the 128-row tile map, the fp32 pre-activations h1 (h3), and
-// the bf16 dh1 (dh3) and activation a, each [max_rows, d_ff]
+// Transposed weights for dX = dh W (the first layer's weights, gate and up
+// side by side for SwiGLU): out[e][n][k] = W1[e][k][n] for k < K1, else
+// W3[e][k - K1][n]; n < N, k < Kt.  64 x 64 tiles through LDS, 16-byte
+// loads and stores of whole 128-byte rows.  With them dX runs on the
+// forward's LDS-DMA grouped GEMM (both operands K-contiguous), which reads
+// what the register-transposing backward kernel asked of the L2 at a quarter
+// of the bytes per MFMA.
+__global__ __launch_bounds__(256) void transpose_w_kernel(const uint16_t* __restrict__ W1,
+                                                          const uint16_t* __restrict__ W3, int K1, int Kt, int N,
+                                                          uint16_t* __restrict__ out) {
+  __shared__ uint4 tile[64 * 9];               // 64 rows (k) of 64 bf16, pitch 72 bf16
+  const int e = blockIdx.z;
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(tile);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i;
+    const int r = q >> 3, c = q & 7;
+    const int k = k0 + r, n = n0 + 8 * c;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (k < Kt && n < N) {
+      const uint16_t* src = k < K1 ? W1 + (static_cast<size_t>(e) * K1 + k) * N
+                                   : W3 + (static_cast<size_t>(e) * (Kt - K1) + (k - K1)) * N;
+      v = *reinterpret_cast<const uint4*>(src + n);
+    }
+    tile[r * 9 + c] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i;
+    const int r = q >> 3, c = q & 7;             // output row n0 + r, columns k0 + 8 c ..
+    const int n = n0 + r, k = k0 + 8 * c;
+    if (n < N && k < Kt) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = static_cast<uint32_t>(t16[(8 * c + 2 * j) * 72 + r]) |
+               (static_cast<uint32_t>(t16[(8 * c + 2 * j + 1) * 72 + r]) << 16);
+      *reinterpret_cast<uint4*>(out + (static_cast<size_t>(e) * N + n) * Kt + k) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// workspace: the 128- and 256-row tile maps, the fp32 pre-activations h1
+// (h3), the bf16 dh [max_rows, n1] ([max_rows, 2 n1] for SwiGLU: dh1 then dh3
+// in each row) and activation a [max_rows, d_ff], the transposed first-layer
+// weights [E, d, Kt] and the forward GEMM's split-tail partial sums
 struct FfnBwdLayout {
-  size_t ts128, h1, h3, dh1, dh3, a, total;
+  size_t ts128, ts256, h1, h3, dh, a, wt, partial, total;
 };
 
-FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d_ff) {
+FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int d_out) {
   FfnBwdLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -484,14 +531,17 @@ FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d_ff) {
     o += align_up(bytes, kWsAlign);
     return at;
   };
-  const size_t ff = static_cast<size_t>(max_rows) * static_cast<size_t>(d_ff > 0 ? d_ff : 0);
-  L.ts128 = take(static_cast<size_t>(E + 1) * 4);
   const bool two = kind != MOE_FFN_LINEAR;
+  const size_t ff = static_cast<size_t>(max_rows) * static_cast<size_t>(d_ff > 0 ? d_ff : 0);
+  const size_t kt = two ? static_cast<size_t>(d_ff) * (kind == MOE_FFN_SWIGLU ? 2 : 1) : static_cast<size_t>(d_out);
+  L.ts128 = take(static_cast<size_t>(E + 1) * 4);
+  L.ts256 = take(static_cast<size_t>(E + 1) * 4);
   L.h1 = two ? take(ff * 4) : 0;
   L.h3 = kind == MOE_FFN_SWIGLU ? take(ff * 4) : 0;
-  L.dh1 = two ? take(ff * 2) : 0;
-  L.dh3 = kind == MOE_FFN_SWIGLU ? take(ff * 2) : 0;
+  L.dh = two ? take(static_cast<size_t>(max_rows) * kt * 2) : 0;
   L.a = two ? take(ff * 2) : 0;
+  L.wt = take(static_cast<size_t>(E) * static_cast<size_t>(d) * kt * 2);
+  L.partial = take(static_cast<size_t>(current_cu_count()) * 256 * 256 * 4);
   L.total = o;
   return L;
 }
@@ -502,10 +552,8 @@ FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d_ff) {
 extern "C" {
 
 size_t moe_ffn_backward_workspace_size(int kind, int max_rows, int E, int d, int d_ff, int d_out) {
-  (void)d;
-  (void)d_out;
-  if (max_rows < 0 || E < 1) return 0;
-  return ffn_bwd_layout(kind, max_rows, E, d_ff).total;
+  if (max_rows < 0 || E < 1 || d < 1 || d_out < 1) return 0;
+  return ffn_bwd_layout(kind, max_rows, E, d, d_ff, d_out).total;
 }
 
 int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
@@ -532,7 +580,7 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   const void* ptrs[] = {x_rows, offsets, w1, w3, w2, b1, b2, dy_rows, dx_rows, dw1, dw3, dw2, db1, db2};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
-  const FfnBwdLayout lay = ffn_bwd_layout(kind, max_rows, E, d_ff);
+  const FfnBwdLayout lay = ffn_bwd_layout(kind, max_rows, E, d, d_ff, d_out);
   if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
   if (max_rows == 0) {
     // no rows: every weight gradient is zero (a fill kernel, no memset node)
@@ -548,13 +596,16 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   int32_t* ts128 = reinterpret_cast<int32_t*>(ws + lay.ts128);
   float* h1 = two ? reinterpret_cast<float*>(ws + lay.h1) : nullptr;
   float* h3 = kind == MOE_FFN_SWIGLU ? reinterpret_cast<float*>(ws + lay.h3) : nullptr;
-  uint16_t* dh1 = two ? reinterpret_cast<uint16_t*>(ws + lay.dh1) : nullptr;
-  uint16_t* dh3 = kind == MOE_FFN_SWIGLU ? reinterpret_cast<uint16_t*>(ws + lay.dh3) : nullptr;
+  const int n1 = two ? d_ff : d_out;
+  // dh: [max_rows, kt]; for SwiGLU dh1 in columns [0, d_ff), dh3 in [d_ff, 2 d_ff)
+  const int kt = kind == MOE_FFN_SWIGLU ? 2 * n1 : n1;
+  uint16_t* dh1 = two ? reinterpret_cast<uint16_t*>(ws + lay.dh) : nullptr;
+  uint16_t* dh3 = kind == MOE_FFN_SWIGLU ? dh1 + n1 : nullptr;
   uint16_t* act = two ? reinterpret_cast<uint16_t*>(ws + lay.a) : nullptr;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + lay.wt);
   const int shared = row_mode == MOE_ROWS_SHARED ? 1 : 0;
   const uint16_t* X = static_cast<const uint16_t*>(x_rows);
   const uint16_t* DY = static_cast<const uint16_t*>(dy_rows);
-  const int n1 = two ? d_ff : d_out;
 
   int st = launch_tile_map(offsets, E, kBwdBM, ts128, stream);
   if (st != MOE_OK) return st;
@@ -604,6 +655,7 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     b.ts = ts128;
     b.E = E;
     b.ldc = d_ff;
+    b.ldo = kt;
     b.H1 = h1;
     b.H3 = h3;
     b.O1 = dh1;
@@ -613,26 +665,32 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     st = launch_bwd_gemm(BWD_DGRAD, epi, b, mt128, stream);
     if (st != MOE_OK) return st;
   }
-  // 3. dX = dh1 W1 (+ dh3 W3) over K = n1 (2 d_ff for SwiGLU); linear: dY W1
+  // 3. dX = dh W13 over K = kt (dh1 W1 + dh3 W3 for SwiGLU; linear: dY W1):
+  //    the first layer's weights transposed to [E, d, kt], then the forward's
+  //    grouped GEMM (both operands K-contiguous)
   {
-    BwdGemmParams b{};
-    b.A = two ? dh1 : DY;
-    b.A2 = dh3;
-    b.lda = n1;
-    b.a_shared = two ? 0 : shared;
-    b.B = static_cast<const uint16_t*>(w1);
-    b.B2 = static_cast<const uint16_t*>(w3);
-    b.ldb = d;
-    b.b_estride = static_cast<long>(n1) * d;
-    b.N = d;
-    b.K1 = n1;
-    b.K = dh3 ? 2 * n1 : n1;
-    b.offsets = offsets;
-    b.ts = ts128;
-    b.E = E;
-    b.ldc = d;
-    b.O1 = static_cast<uint16_t*>(dx_rows);
-    st = launch_bwd_gemm(BWD_DGRAD, BWD_EPI_STORE, b, mt128, stream);
+    const dim3 tg((d + 63) / 64, (kt + 63) / 64, E);
+    hipLaunchKernelGGL(transpose_w_kernel, tg, dim3(256), 0, stream, static_cast<const uint16_t*>(w1),
+                       static_cast<const uint16_t*>(w3), n1, kt, d, wt);
+    st = check_launch();
+    if (st != MOE_OK) return st;
+    int32_t* ts256 = reinterpret_cast<int32_t*>(ws + lay.ts256);
+    st = launch_tile_map(offsets, E, kGemmBM, ts256, stream);
+    if (st != MOE_OK) return st;
+    GemmParams g{};
+    g.A = two ? dh1 : DY;
+    g.a_shared = two ? 0 : shared;
+    g.offsets = offsets;
+    g.ts = ts256;
+    g.E = E;
+    g.B1 = wt;
+    g.C = static_cast<uint16_t*>(dx_rows);
+    g.N = d;
+    g.K = kt;
+    g.partial = reinterpret_cast<float*>(ws + lay.partial);
+    g.n_cu = current_cu_count();
+    g.split_max = kGemmSplitMax;
+    st = launch_grouped_gemm(EPI_PLAIN, false, g, max_rows, (max_rows + kGemmBM - 1) / kGemmBM + E, stream);
     if (st != MOE_OK) return st;
   }
   // 4. weight gradients, K = the segment's rows: dW2 = dY^T a; dW1 = dh1^T X
@@ -660,10 +718,10 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     st = wgrad(DY, d_out, shared, act, d_ff, 0, d_out, d_ff, dw2);
     if (st != MOE_OK) return st;
   }
-  st = wgrad(two ? dh1 : DY, n1, two ? 0 : shared, X, d, shared, n1, d, dw1);
+  st = wgrad(two ? dh1 : DY, two ? kt : n1, two ? 0 : shared, X, d, shared, n1, d, dw1);
   if (st != MOE_OK) return st;
   if (dh3) {
-    st = wgrad(dh3, d_ff, 0, X, d, shared, d_ff, d, dw3);
+    st = wgrad(dh3, kt, 0, X, d, shared, d_ff, d, dw3);
     if (st != MOE_OK) return st;
   }
   // 5. bias gradients: sums over each segment's rows

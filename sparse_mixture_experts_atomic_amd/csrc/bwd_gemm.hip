@@ -317,22 +317,24 @@ __global__ __launch_bounds__(kBT, 2) void bwd_gemm_kernel(BwdGemmParams p) {
           p.Cf[static_cast<size_t>(row0 + lr) * p.ldc + col] = p.bias ? v + p.bias[static_cast<size_t>(e) * p.N + col] : v;
         } else {
           const size_t o = static_cast<size_t>(row0 + lr) * p.ldc + col;
+          // O1, O2 (the dh outputs) may have their own row stride
+          const size_t od = p.ldo ? static_cast<size_t>(row0 + lr) * p.ldo + col : o;
           if constexpr (EPI == BWD_EPI_STORE) {
-            p.O1[o] = f32_to_bf16(v);
+            p.O1[od] = f32_to_bf16(v);
           } else if constexpr (EPI == BWD_EPI_SWIGLU) {
             const float h1 = p.H1[o], h3 = p.H3[o];
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * h1));
             const float si = h1 * sg;
-            p.O1[o] = f32_to_bf16(v * h3 * sg * (1.0f + h1 * (1.0f - sg)));
-            p.O2[o] = f32_to_bf16(v * si);
+            p.O1[od] = f32_to_bf16(v * h3 * sg * (1.0f + h1 * (1.0f - sg)));
+            p.O2[od] = f32_to_bf16(v * si);
             p.O3[o] = f32_to_bf16(si * h3);
           } else if constexpr (EPI == BWD_EPI_RELU) {
             const float h = p.H1[o];
-            p.O1[o] = f32_to_bf16(h > 0.f ? v : 0.f);
+            p.O1[od] = f32_to_bf16(h > 0.f ? v : 0.f);
             p.O3[o] = f32_to_bf16(fmaxf(h, 0.f));
           } else {   // BWD_EPI_GELU
             const float h = p.H1[o];
-            p.O1[o] = f32_to_bf16(v * gelu_grad_f32(h));
+            p.O1[od] = f32_to_bf16(v * gelu_grad_f32(h));
             p.O3[o] = f32_to_bf16(gelu_f32(h));
           }
         }

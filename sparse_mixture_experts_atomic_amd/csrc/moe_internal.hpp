@@ -199,6 +199,7 @@ struct BwdGemmParams {
   uint16_t* O1;
   uint16_t* O2;
   uint16_t* O3;
+  long ldo;                  // row stride of O1 and O2 (0: ldc)
 };
 constexpr int kBwdBM = 128;   // rows per m-tile of the dgrad tile map
 
