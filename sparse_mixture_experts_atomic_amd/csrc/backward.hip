@@ -612,8 +612,35 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   const int mt128 = (max_rows + kBwdBM - 1) / kBwdBM + E;
 
   // 1. recompute the first layer's pre-activations h1 (+ bias) and h3 in
-  //    fp32 (forward layout, no activation)
+  //    fp32 (forward layout, no activation): on the forward's LDS-DMA kernel
+  //    with its fp32 pre-activation epilogue (one launch for gate and up),
+  //    else on the backward kernel
+  int32_t* ts256 = reinterpret_cast<int32_t*>(ws + lay.ts256);
+  st = launch_tile_map(offsets, E, kGemmBM, ts256, stream);
+  if (st != MOE_OK) return st;
+  const int mt256 = (max_rows + kGemmBM - 1) / kGemmBM + E;
+  bool pre_done = false;
   if (two) {
+    GemmParams f{};
+    f.A = X;
+    f.a_shared = shared;
+    f.offsets = offsets;
+    f.ts = ts256;
+    f.E = E;
+    f.B1 = w1;
+    f.B3 = w3;
+    f.bias = b1;
+    f.N = d_ff;
+    f.K = d;
+    f.n_cu = current_cu_count();
+    f.split_max = 1;
+    f.pre1 = h1;
+    f.pre3 = h3;
+    st = launch_grouped_gemm_pre(kind == MOE_FFN_SWIGLU ? EPI_SWIGLU : EPI_PLAIN, f, mt256, stream);
+    if (st == MOE_OK) pre_done = true;
+    else if (st != MOE_ERR_UNSUPPORTED) return st;
+  }
+  if (two && !pre_done) {
     BwdGemmParams g{};
     g.A = X;
     g.lda = d;
@@ -639,6 +666,8 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
       st = launch_bwd_gemm(BWD_FWD, BWD_EPI_STORE, g, mt128, stream);
       if (st != MOE_OK) return st;
     }
+  }
+  if (two) {
     // 2. da = dY W2 (K = d_out), with the activation's backward in the
     //    epilogue: dh1 (dh3) and the activation a
     BwdGemmParams b{};
@@ -674,9 +703,6 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
                        static_cast<const uint16_t*>(w3), n1, kt, d, wt);
     st = check_launch();
     if (st != MOE_OK) return st;
-    int32_t* ts256 = reinterpret_cast<int32_t*>(ws + lay.ts256);
-    st = launch_tile_map(offsets, E, kGemmBM, ts256, stream);
-    if (st != MOE_OK) return st;
     GemmParams g{};
     g.A = two ? dh1 : DY;
     g.a_shared = two ? 0 : shared;
@@ -690,7 +716,7 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     g.partial = reinterpret_cast<float*>(ws + lay.partial);
     g.n_cu = current_cu_count();
     g.split_max = kGemmSplitMax;
-    st = launch_grouped_gemm(EPI_PLAIN, false, g, max_rows, (max_rows + kGemmBM - 1) / kGemmBM + E, stream);
+    st = launch_grouped_gemm(EPI_PLAIN, false, g, max_rows, mt256, stream);
     if (st != MOE_OK) return st;
   }
   // 4. weight gradients, K = the segment's rows: dW2 = dY^T a; dW1 = dh1^T X

@@ -484,10 +484,35 @@ __device__ __forceinline__ SplitPlan split_plan(int V, int KT, int R, int n_cu, 
 // other wavefront uses.
 // RS: fp8 activations; rsl[r] (LDS) is the scale of the wavefront's row r,
 // applied with the column scale before the activation.
-template <int EPI, int FM, bool RS = false>
+template <int EPI, int FM, bool RS = false, bool PRE = false>
 __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint16_t* st, const GemmParams& p, int e,
                                               int row0, int rows_valid, int col0, const float* rsl = nullptr) {
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
+  if constexpr (PRE) {
+    // fp32 pre-activations straight from the accumulators (32 lanes store
+    // 128 contiguous bytes of a row): gate (+ bias) to pre1, SwiGLU's up to pre3
+    const int N = p.N;
+    const int lane = threadIdx.x & 63;
+    const int fr = lane & 31, fc = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < OC / 32; ++j) {
+      const int col = col0 + j * 32 + fr;
+      if (col >= N) continue;
+      const float bias = (EPI != EPI_SWIGLU && p.bias) ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+          if (r < rows_valid) {
+            const size_t o = static_cast<size_t>(row0 + r) * N + col;
+            p.pre1[o] = acc[i][j][q] + bias;
+            if (EPI == EPI_SWIGLU) p.pre3[o] = acc[i][j + 2][q];
+          }
+        }
+    }
+    return;
+  }
   constexpr int PITCH = OC + 8;           // the two lane halves of a write land 16 banks apart
   constexpr int PR = OC / 8;              // 16-byte pieces per row
   const int N = p.N;
@@ -661,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 // tile and store raw accumulators.  (The tile body is a generic lambda
 // rather than a function template: written as a function, the register
 // allocator spilled some 200 accumulator registers around the stage loop.)
-template <int EPI, int BK, bool FP8>
+template <int EPI, int BK, bool FP8, bool PRE = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr int BM = 256;
   constexpr int R = 2;                  // split parts are whole stage pairs
@@ -1084,8 +1109,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     // last barrier and no load is in flight
     constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
     const int col0 = EPI == EPI_SWIGLU ? nt * HC + wn * 64 : nt * BN + wn * 128;
-    wave_epilogue<EPI, FM>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * (OC + 8), p, e, row0 + wm * WM,
-                           rows_valid - wm * WM, col0);
+    wave_epilogue<EPI, FM, false, PRE>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * (OC + 8), p, e,
+                                       row0 + wm * WM, rows_valid - wm * WM, col0);
   };
   if constexpr (!FP8) {
     if (unit < 0 && tc.rows_valid <= 64) {
@@ -1330,26 +1355,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
                               row0 + wm * 128, rows_valid - wm * 128, col0, rsl);
 }
 
-template <int EPI, int BK, bool FP8>
-int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+template <int EPI, int BK, bool FP8, bool PRE>
+int launch_dma_pre(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   const long n_tiles = (p.N + HC - 1) / HC;
   long blocks = n_tiles * m_tiles_max;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   // the tail can matter only for a grid of a few rounds; otherwise no split
   // (and no reduction launch)
-  const bool split = p.split_max > 1 && p.partial && p.n_cu > 0 && n_tiles * m_tiles_max <= 4L * p.n_cu;
+  const bool split = !PRE && p.split_max > 1 && p.partial && p.n_cu > 0 && n_tiles * m_tiles_max <= 4L * p.n_cu;
   if (split) blocks += p.n_cu;   // full + rem * S = V + rem * (S - 1) < V + n_cu
   if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
   GemmParams q = p;
   if (!split) q.split_max = 1;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK, FP8>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, q);
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK, FP8, PRE>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, stream, q);
   int st = check_launch();
   if (st != MOE_OK || !split) return st;
   hipLaunchKernelGGL((split_reduce_kernel<EPI, BK>), dim3(static_cast<unsigned>(4 * p.n_cu)), dim3(kThreads), 0, stream,
                      p);
   return check_launch();
+}
+
+template <int EPI, int BK, bool FP8>
+int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  return launch_dma_pre<EPI, BK, FP8, false>(p, m_tiles_max, stream);
 }
 
 template <int BM, int BN, int NH, int EPI, bool FP8>
@@ -1404,6 +1434,18 @@ int launch_grouped_gemm_f8(int epi, const GemmParams& p, int m_tiles_max, hipStr
 // 256-row tiles throughout (one tile map serves both GEMMs of an FFN); the
 // weight-row width is 256 unless that leaves too few tiles to fill 256 CUs
 // a few times over, in which case 128.
+int launch_grouped_gemm_pre(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  const bool dma_ok = p.K % kDmaKMult == 0 && p.N % 8 == 0 && static_cast<size_t>(p.N) * p.K * 2 < (size_t(1) << 31) &&
+                      static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31) && !p.gather && !p.s1 &&
+                      p.pre1 && (epi != EPI_SWIGLU || p.pre3);
+  if (!dma_ok) return MOE_ERR_UNSUPPORTED;
+  GemmParams q = p;
+  q.split_max = 1;
+  if (epi == EPI_SWIGLU) return launch_dma_pre<EPI_SWIGLU, kDmaBK, false, true>(q, m_tiles_max, stream);
+  if (epi == EPI_PLAIN) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, true>(q, m_tiles_max, stream);
+  return MOE_ERR_UNSUPPORTED;
+}
+
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream) {
   (void)max_rows;
   // LDS-DMA kernel: bf16 weights, K a multiple of the ring's K per round,

@@ -129,6 +129,8 @@ struct GemmParams {
   int n_cu;                  // compute units (one block of the DMA kernel each)
   int split_max;             // most K parts of a split tile (1: no split)
   const float* row_scale;    // fp8 activations: scale of each source row of A (or null)
+  float* pre1;               // pre-activation outputs (fp32 [*, N]; launch_grouped_gemm_pre only):
+  float* pre3;               //   gate (+ bias) and, for SwiGLU, up
 };
 
 // Bytes of the split-tail partial buffer for n_cu compute units.
@@ -143,6 +145,10 @@ int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, in
 // C = epi(diag(row scales) A B^T diag(column scales)) per segment, bf16 out.
 // K % 128 == 0, N % 8 == 0.
 int launch_grouped_gemm_f8(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
+// The first layer's pre-activations in fp32 (acc + bias to pre1; SwiGLU: gate
+// to pre1, up to pre3) on the LDS-DMA kernel; bf16 weights, K % 128 == 0, no
+// split tail.  MOE_ERR_UNSUPPORTED for shapes it does not take.
+int launch_grouped_gemm_pre(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
 
 // Per-row e4m3 quantisation (quant.hip): scale[r] = max |x[r, :]| / 448 (1
 // for a zero row), q = e4m3(x / scale); rows_dev (device, or null) bounds the
