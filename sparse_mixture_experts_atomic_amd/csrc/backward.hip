@@ -515,12 +515,64 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const uint16_t* __rest
   }
 }
 
+// Per-segment transposes for the weight gradients: out[f][128 ts[e] + r] =
+// in[base_e + r][f] for the r < rows_e of segment e (base_e = offsets[e], or
+// 0 when every segment reads the same rows), zero for the padding rows up to
+// the next multiple of 128 (ts: the 128-row tile map).  64 x 64 tiles through
+// LDS as in transpose_w_kernel; a tile never straddles two segments.
+__global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __restrict__ in, long ldin, int F,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ ts, int E, int shared,
+                                                            uint16_t* __restrict__ out, long ldout) {
+  __shared__ uint4 tile[64 * 9];
+  const int k0 = blockIdx.y * 64, f0 = blockIdx.x * 64;
+  if (k0 >= ts[E] * 128) return;
+  int lo = 0, hi = E;                          // the segment: largest e with 128 ts[e] <= k0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ts[mid] * 128 <= k0) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int r0 = k0 - ts[e] * 128;
+  const int rows = offsets[e + 1] - offsets[e];
+  const long base = shared ? 0 : offsets[e];
+  const int tid = threadIdx.x;
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(tile);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i;
+    const int r = q >> 3, c = q & 7;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r0 + r < rows && f0 + 8 * c < F) v = *reinterpret_cast<const uint4*>(in + (base + r0 + r) * ldin + f0 + 8 * c);
+    tile[r * 9 + c] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i;
+    const int r = q >> 3, c = q & 7;             // output row f0 + r, columns k0 + 8 c ..
+    if (f0 + r < F) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = static_cast<uint32_t>(t16[(8 * c + 2 * j) * 72 + r]) |
+               (static_cast<uint32_t>(t16[(8 * c + 2 * j + 1) * 72 + r]) << 16);
+      *reinterpret_cast<uint4*>(out + static_cast<size_t>(f0 + r) * ldout + k0 + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// out[e] = e M for e <= E (the row offsets of E segments of M rows)
+__global__ void iota_kernel(int32_t* out, int E, int M) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) out[e] = e * M;
+}
+
 // workspace: the 128- and 256-row tile maps, the fp32 pre-activations h1
 // (h3), the bf16 dh [max_rows, n1] ([max_rows, 2 n1] for SwiGLU: dh1 then dh3
 // in each row) and activation a [max_rows, d_ff], the transposed first-layer
 // weights [E, d, Kt] and the forward GEMM's split-tail partial sums
 struct FfnBwdLayout {
-  size_t ts128, ts256, h1, h3, dh, a, wt, partial, total;
+  size_t ts128, ts256, h1, h3, dh, a, wt, partial, kp, xt, dyt, at, dht, wofs_o, wofs_1, tsw_o, tsw_1, total;
 };
 
 FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int d_out) {
@@ -542,6 +594,17 @@ FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int 
   L.a = two ? take(ff * 2) : 0;
   L.wt = take(static_cast<size_t>(E) * static_cast<size_t>(d) * kt * 2);
   L.partial = take(static_cast<size_t>(current_cu_count()) * 256 * 256 * 4);
+  // weight gradients: activations transposed per segment to [features, kp],
+  // kp >= max_rows + 128 E bounds the sum of the segments padded to 128 rows
+  L.kp = align_up(static_cast<size_t>(max_rows) + 128 * static_cast<size_t>(E), 64);   // 16-byte rows
+  L.xt = take(static_cast<size_t>(d) * L.kp * 2);
+  L.dyt = take(static_cast<size_t>(d_out) * L.kp * 2);
+  L.at = two ? take(static_cast<size_t>(d_ff) * L.kp * 2) : 0;
+  L.dht = two ? take(kt * L.kp * 2) : 0;
+  L.wofs_o = take(static_cast<size_t>(E + 1) * 4);
+  L.wofs_1 = take(static_cast<size_t>(E + 1) * 4);
+  L.tsw_o = take(static_cast<size_t>(E + 1) * 4);
+  L.tsw_1 = take(static_cast<size_t>(E + 1) * 4);
   L.total = o;
   return L;
 }
@@ -720,7 +783,67 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     if (st != MOE_OK) return st;
   }
   // 4. weight gradients, K = the segment's rows: dW2 = dY^T a; dW1 = dh1^T X
-  //    (linear: dY^T X); dW3 = dh3^T X
+  //    (linear: dY^T X); dW3 = dh3^T X.  On the forward's LDS-DMA GEMM over
+  //    the activations transposed per segment (each segment padded to 128
+  //    rows with zeros; segments of the transposed buffers start at 128 ts128[e]),
+  //    else on the backward kernel (transposing in registers)
+  const long kp = static_cast<long>(lay.kp);
+  auto dma_fits = [&](int N) {
+    return static_cast<size_t>(kGemmBM) * kp * 2 < (size_t(1) << 31) &&
+           static_cast<size_t>(N) * kp * 2 < (size_t(1) << 31) && N % 8 == 0;
+  };
+  const bool wg_dma = dma_fits(d) && (!two || dma_fits(d_ff));
+  if (wg_dma) {
+    uint16_t* XT = reinterpret_cast<uint16_t*>(ws + lay.xt);
+    uint16_t* DYT = reinterpret_cast<uint16_t*>(ws + lay.dyt);
+    auto transpose = [&](const uint16_t* in, long ldin, int F, int sh, uint16_t* out) {
+      const dim3 g((F + 63) / 64, static_cast<unsigned>((kp + 63) / 64));
+      hipLaunchKernelGGL(transpose_seg_kernel, g, dim3(256), 0, stream, in, ldin, F, offsets, ts128, E, sh, out, kp);
+      return check_launch();
+    };
+    auto wgrad_dma = [&](const uint16_t* A_, const uint16_t* B_, int M, int N, int32_t* wofs, int32_t* tsw,
+                         float* out) {
+      hipLaunchKernelGGL(iota_kernel, dim3(1), dim3(256), 0, stream, wofs, E, M);
+      int r = check_launch();
+      if (r != MOE_OK) return r;
+      r = launch_tile_map(wofs, E, kGemmBM, tsw, stream);
+      if (r != MOE_OK) return r;
+      GemmParams g{};
+      g.A = A_;
+      g.a_shared = 1;
+      g.offsets = wofs;
+      g.ts = tsw;
+      g.E = E;
+      g.B1 = B_;
+      g.N = N;
+      g.pre1 = out;
+      g.kseg = ts128;
+      g.lda = kp;
+      g.ldb = kp;
+      g.n_cu = current_cu_count();
+      return launch_grouped_gemm_wgrad(g, static_cast<int>((static_cast<long>(E) * M + kGemmBM - 1) / kGemmBM) + E,
+                                       stream);
+    };
+    int32_t* wofs_o = reinterpret_cast<int32_t*>(ws + lay.wofs_o);
+    int32_t* wofs_1 = reinterpret_cast<int32_t*>(ws + lay.wofs_1);
+    int32_t* tsw_o = reinterpret_cast<int32_t*>(ws + lay.tsw_o);
+    int32_t* tsw_1 = reinterpret_cast<int32_t*>(ws + lay.tsw_1);
+    st = transpose(X, d, d, shared, XT);
+    if (st == MOE_OK) st = transpose(DY, d_out, d_out, shared, DYT);
+    if (st != MOE_OK) return st;
+    if (two) {
+      uint16_t* AT = reinterpret_cast<uint16_t*>(ws + lay.at);
+      uint16_t* DHT = reinterpret_cast<uint16_t*>(ws + lay.dht);
+      st = transpose(act, d_ff, d_ff, 0, AT);
+      if (st == MOE_OK) st = transpose(dh1, kt, kt, 0, DHT);
+      if (st == MOE_OK) st = wgrad_dma(DYT, AT, d_out, d_ff, wofs_o, tsw_o, dw2);
+      if (st == MOE_OK) st = wgrad_dma(DHT, XT, n1, d, wofs_1, tsw_1, dw1);
+      if (st == MOE_OK && dh3) st = wgrad_dma(DHT + static_cast<size_t>(n1) * kp, XT, n1, d, wofs_1, tsw_1, dw3);
+    } else {
+      st = wgrad_dma(DYT, XT, n1, d, wofs_1, tsw_1, dw1);
+    }
+    if (st != MOE_OK) return st;
+  } else {
   auto wgrad = [&](const uint16_t* A, long lda, int a_sh, const uint16_t* B, long ldb, int b_sh, int M, int N,
                    float* out) {
     BwdGemmParams b{};
@@ -749,6 +872,7 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   if (dh3) {
     st = wgrad(dh3, kt, 0, X, d, shared, d_ff, d, dw3);
     if (st != MOE_OK) return st;
+  }
   }
   // 5. bias gradients: sums over each segment's rows
   if (db1) {

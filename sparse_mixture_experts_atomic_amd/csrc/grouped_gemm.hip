@@ -489,27 +489,52 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
                                               int row0, int rows_valid, int col0, const float* rsl = nullptr) {
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
   if constexpr (PRE) {
-    // fp32 pre-activations straight from the accumulators (32 lanes store
-    // 128 contiguous bytes of a row): gate (+ bias) to pre1, SwiGLU's up to pre3
+    // fp32 outputs (gate (+ bias) to pre1, SwiGLU's up to pre3) staged
+    // through the wavefront's LDS block in two passes (SwiGLU: gate, then
+    // up, 128 rows x 64 columns; else rows 0-63, then 64-127, of 128
+    // columns), then stored as whole 16-byte pieces of rows.  (Stored
+    // straight from the accumulators, 4 bytes a lane, the epilogue of a
+    // weight-gradient tile took longer than its 16 stages.)
     const int N = p.N;
     const int lane = threadIdx.x & 63;
     const int fr = lane & 31, fc = lane >> 5;
+    constexpr int RP = EPI == EPI_SWIGLU ? 32 * FM : 16 * FM;   // rows per pass
+    constexpr int PF = OC + 4;                                   // staging pitch (floats)
+    static_assert(RP * PF * 4 <= 128 * (128 + 8) * 2, "staging block (the caller spaces the blocks so)");
+    float* stf = reinterpret_cast<float*>(st);
 #pragma unroll
-    for (int j = 0; j < OC / 32; ++j) {
-      const int col = col0 + j * 32 + fr;
-      if (col >= N) continue;
-      const float bias = (EPI != EPI_SWIGLU && p.bias) ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+      float* dst = (EPI == EPI_SWIGLU && pass == 1) ? p.pre3 : p.pre1;
+      const int rb = EPI == EPI_SWIGLU ? 0 : pass * RP;          // first row of the pass
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < OC / 32; ++j) {
+        const int col = col0 + j * 32 + fr;
+        const float bias =
+            (EPI != EPI_SWIGLU && p.bias && col < N) ? p.bias[static_cast<size_t>(e) * N + col] : 0.f;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
-          if (r < rows_valid) {
-            const size_t o = static_cast<size_t>(row0 + r) * N + col;
-            p.pre1[o] = acc[i][j][q] + bias;
-            if (EPI == EPI_SWIGLU) p.pre3[o] = acc[i][j + 2][q];
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = i * 32 + (q >> 2) * 8 + fc * 4 + (q & 3);
+            if (r >= rb && r < rb + RP) {
+              const float v = (EPI == EPI_SWIGLU && pass == 1) ? acc[i][j + 2][q] : acc[i][j][q] + bias;
+              stf[(r - rb) * PF + j * 32 + fr] = v;
+            }
           }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+#pragma unroll 4
+      for (int u = 0; u < RP * (OC / 4) / 64; ++u) {
+        const int c = lane + 64 * u;
+        const int r = c / (OC / 4);
+        const int pc = (c % (OC / 4)) * 4;
+        if (rb + r < rows_valid && col0 + pc < N) {
+          const float4 v = *reinterpret_cast<const float4*>(stf + r * PF + pc);
+          *reinterpret_cast<float4*>(dst + static_cast<size_t>(row0 + rb + r) * N + col0 + pc) = v;
         }
+      }
+      // the next pass overwrites the block: every lane's reads come first
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
     }
     return;
   }
@@ -686,8 +711,13 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 // tile and store raw accumulators.  (The tile body is a generic lambda
 // rather than a function template: written as a function, the register
 // allocator spilled some 200 accumulator registers around the stage loop.)
-template <int EPI, int BK, bool FP8, bool PRE = false>
+// XM: 0 the forward (bf16 or e4m3 C); 1 fp32 pre-activations (PRE epilogue);
+// 2 weight gradients: per-segment K ranges (kseg), row pitches lda / ldb, B
+// shared by the segments, fp32 output through the PRE epilogue
+template <int EPI, int BK, bool FP8, int XM = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
+  constexpr bool PRE = XM >= 1;
+  constexpr bool WG = XM == 2;
   constexpr int BM = 256;
   constexpr int R = 2;                  // split parts are whole stage pairs
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
@@ -712,8 +742,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     L = sp.full + unit / sp.S;
   }
   const int ks0 = unit < 0 ? 0 : (unit % sp.S) * sp.chunk;   // first stage of this block
-  const int nks = unit < 0 ? KT : min(sp.chunk, KT - ks0);    // stages (even, >= 2)
   const TileCoord tc = tile_coord(p, L, m_total, n_tiles, BM);
+  // weight gradients: the segment's own K range (a multiple of 128, may be 0)
+  // (kseg counts units of 128 columns)
+  const int kb = WG ? p.kseg[tc.e] * kDmaKMult : 0;
+  const int nks = WG ? (p.kseg[tc.e + 1] * kDmaKMult - kb) / BK
+                     : (unit < 0 ? KT : min(sp.chunk, KT - ks0));   // stages (even, >= 2)
   auto tile = [&](auto fmc) __attribute__((always_inline)) {
     constexpr int FM = decltype(fmc)::value;
     constexpr int BN = 256;
@@ -751,14 +785,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     // first row and each lane's offset that of its source row (the host
     // keeps a_rows * K * 2 below 2^31)
     const bool gat = p.gather != nullptr;
+    const long lda = WG ? p.lda : K;
     const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(
-        gat ? p.A : p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * K));
+        gat ? p.A : p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * lda + kb));
     uint32_t a_vo[LDA];
 #pragma unroll
     for (int i = 0; i < LDA; ++i) {
       const int r = min(i * RPI + tid / CH, rows_valid - 1);
       const int src = gat ? min(max(p.gather[row0 + r], 0), p.a_rows - 1) : r;   // clamped: never outside A
-      a_vo[i] = static_cast<uint32_t>((src * K + cq * 8) * 2);
+      a_vo[i] = static_cast<uint32_t>((src * lda + cq * 8) * 2);
     }
     const int cqb = (tid & (CHB - 1)) ^ ((tid >> 4) & (CHB - 1));
     const char* b_sb[LDB];
@@ -778,8 +813,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
         n = nt * BN + r;
       }
       n = min(n, N - 1);
-      b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(e) * N * K * EB);
-      b_vo[i] = static_cast<uint32_t>(n * K * EB + cqb * 16);
+      if constexpr (WG) {
+        b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(kb) * EB);
+        b_vo[i] = static_cast<uint32_t>(n * p.ldb * EB + cqb * 16);
+      } else {
+        b_sb[i] = uniform_ptr(static_cast<const char*>(base) + static_cast<size_t>(e) * N * K * EB);
+        b_vo[i] = static_cast<uint32_t>(n * K * EB + cqb * 16);
+      }
     }
     const uint32_t wave_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) * 1024u;
     // half-slot index (2 s + c) % 5 from (2 s) % 5 (both < 5)
@@ -942,6 +982,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     using F_ = std::false_type;
     using W0 = std::integral_constant<int, 0>;
     using WA = std::integral_constant<int, LDA>;
+    // (weight gradients of an expert without rows: no stages, zero output)
+    if (!WG || nks > 0) {
     if constexpr (FM <= 2 && !FP8) {
       // 128- and 64-row tiles, bf16: the mirrored ring.  A stage moves 48 KB (A is
       // half as tall) for half the MFMAs, so issued as above the B DMAs come
@@ -1089,6 +1131,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       }
     }
 
+    }
     if constexpr (FM == 4) {
       if (unit >= 0) {
         // split unit: raw accumulators to the partial buffer, in the MFMA layout
@@ -1109,8 +1152,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     // last barrier and no load is in flight
     constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
     const int col0 = EPI == EPI_SWIGLU ? nt * HC + wn * 64 : nt * BN + wn * 128;
-    wave_epilogue<EPI, FM, false, PRE>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * (OC + 8), p, e,
-                                       row0 + wm * WM, rows_valid - wm * WM, col0);
+    // (the fp32 staging of PRE takes the 128 + 8 bf16 pitch whatever OC is)
+    wave_epilogue<EPI, FM, false, PRE>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * ((PRE ? 128 : OC) + 8), p,
+                                       e, row0 + wm * WM, rows_valid - wm * WM, col0);
   };
   if constexpr (!FP8) {
     if (unit < 0 && tc.rows_valid <= 64) {
@@ -1355,8 +1399,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
                               row0 + wm * 128, rows_valid - wm * 128, col0, rsl);
 }
 
-template <int EPI, int BK, bool FP8, bool PRE>
+template <int EPI, int BK, bool FP8, int XM>
 int launch_dma_pre(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  constexpr bool PRE = XM >= 1;
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   const long n_tiles = (p.N + HC - 1) / HC;
   long blocks = n_tiles * m_tiles_max;
@@ -1368,7 +1413,7 @@ int launch_dma_pre(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
   if (blocks > 0x7fffffffL) return MOE_ERR_UNSUPPORTED;
   GemmParams q = p;
   if (!split) q.split_max = 1;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK, FP8, PRE>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<EPI, BK, FP8, XM>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
                      0, stream, q);
   int st = check_launch();
   if (st != MOE_OK || !split) return st;
@@ -1379,7 +1424,7 @@ int launch_dma_pre(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
 
 template <int EPI, int BK, bool FP8>
 int launch_dma(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
-  return launch_dma_pre<EPI, BK, FP8, false>(p, m_tiles_max, stream);
+  return launch_dma_pre<EPI, BK, FP8, 0>(p, m_tiles_max, stream);
 }
 
 template <int BM, int BN, int NH, int EPI, bool FP8>
@@ -1441,9 +1486,21 @@ int launch_grouped_gemm_pre(int epi, const GemmParams& p, int m_tiles_max, hipSt
   if (!dma_ok) return MOE_ERR_UNSUPPORTED;
   GemmParams q = p;
   q.split_max = 1;
-  if (epi == EPI_SWIGLU) return launch_dma_pre<EPI_SWIGLU, kDmaBK, false, true>(q, m_tiles_max, stream);
-  if (epi == EPI_PLAIN) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, true>(q, m_tiles_max, stream);
+  if (epi == EPI_SWIGLU) return launch_dma_pre<EPI_SWIGLU, kDmaBK, false, 1>(q, m_tiles_max, stream);
+  if (epi == EPI_PLAIN) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 1>(q, m_tiles_max, stream);
   return MOE_ERR_UNSUPPORTED;
+}
+
+int launch_grouped_gemm_wgrad(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  // 31-bit per-lane byte offsets: 256 rows of A, N rows of B, at their pitches
+  const bool ok = p.kseg && p.a_shared && p.pre1 && p.N % 8 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
+                  static_cast<size_t>(kGemmBM) * p.lda * 2 < (size_t(1) << 31) &&
+                  static_cast<size_t>(p.N) * p.ldb * 2 < (size_t(1) << 31) && !p.gather && !p.s1 && !p.bias;
+  if (!ok) return MOE_ERR_UNSUPPORTED;
+  GemmParams q = p;
+  q.split_max = 1;
+  q.K = kDmaKMult;              // (the per-segment K ranges come from kseg)
+  return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 2>(q, m_tiles_max, stream);
 }
 
 int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, int m_tiles_max, hipStream_t stream) {

@@ -131,6 +131,11 @@ struct GemmParams {
   const float* row_scale;    // fp8 activations: scale of each source row of A (or null)
   float* pre1;               // pre-activation outputs (fp32 [*, N]; launch_grouped_gemm_pre only):
   float* pre3;               //   gate (+ bias) and, for SwiGLU, up
+  // launch_grouped_gemm_wgrad only: segment e takes K columns [128 kseg[e],
+  // 128 kseg[e+1]) of A (rows from 0, pitch lda) and of B (shared by all
+  // segments, pitch ldb); fp32 output to pre1
+  const int32_t* kseg;
+  long lda, ldb;
 };
 
 // Bytes of the split-tail partial buffer for n_cu compute units.
@@ -149,6 +154,13 @@ int launch_grouped_gemm_f8(int epi, const GemmParams& p, int m_tiles_max, hipStr
 // to pre1, up to pre3) on the LDS-DMA kernel; bf16 weights, K % 128 == 0, no
 // split tail.  MOE_ERR_UNSUPPORTED for shapes it does not take.
 int launch_grouped_gemm_pre(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
+// Weight gradients as grouped GEMMs on the LDS-DMA kernel: per segment e,
+// pre1[e][M][N] (fp32; segments of M rows from p.offsets = e M) = A[:, K_e]
+// B[:, K_e]^T over K_e = columns [128 kseg[e], 128 kseg[e+1]), both operands
+// K-contiguous (activations transposed per segment, each zero-padded to a
+// multiple of 128 columns).
+// MOE_ERR_UNSUPPORTED for shapes it does not take.
+int launch_grouped_gemm_wgrad(const GemmParams& p, int m_tiles_max, hipStream_t stream);
 
 // Per-row e4m3 quantisation (quant.hip): scale[r] = max |x[r, :]| / 448 (1
 // for a zero row), q = e4m3(x / scale); rows_dev (device, or null) bounds the
