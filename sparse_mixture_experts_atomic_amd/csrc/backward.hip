@@ -19,6 +19,8 @@
 // reproducible bit for bit.
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -592,7 +594,10 @@ FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int 
   L.h3 = kind == MOE_FFN_SWIGLU ? take(ff * 4) : 0;
   L.dh = two ? take(static_cast<size_t>(max_rows) * kt * 2) : 0;
   L.a = two ? take(ff * 2) : 0;
-  L.wt = take(static_cast<size_t>(E) * static_cast<size_t>(d) * kt * 2);
+  // transposed weights: the first layer's [E, d, kt] for dX, before it the
+  // second layer's [E, d_ff, d_out] for da
+  L.wt = take(static_cast<size_t>(E) * std::max(static_cast<size_t>(d) * kt,
+                                                two ? static_cast<size_t>(d_ff) * static_cast<size_t>(d_out) : 0) * 2);
   L.partial = take(static_cast<size_t>(current_cu_count()) * 256 * 256 * 4);
   // weight gradients: activations transposed per segment to [features, kp],
   // kp >= max_rows + 128 E bounds the sum of the segments padded to 128 rows
@@ -732,7 +737,37 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   }
   if (two) {
     // 2. da = dY W2 (K = d_out), with the activation's backward in the
-    //    epilogue: dh1 (dh3) and the activation a
+    //    epilogue: dh1 (dh3) and the activation a.  On the forward's LDS-DMA
+    //    kernel over W2 transposed to [E, d_ff, d_out], else on the backward
+    //    kernel
+    const int epi = kind == MOE_FFN_SWIGLU ? BWD_EPI_SWIGLU : kind == MOE_FFN_RELU ? BWD_EPI_RELU : BWD_EPI_GELU;
+    const dim3 tg((d_ff + 63) / 64, (d_out + 63) / 64, E);
+    hipLaunchKernelGGL(transpose_w_kernel, tg, dim3(256), 0, stream, static_cast<const uint16_t*>(w2),
+                       static_cast<const uint16_t*>(nullptr),
+                       d_out, d_out, d_ff, wt);
+    st = check_launch();
+    if (st != MOE_OK) return st;
+    GemmParams a{};
+    a.A = DY;
+    a.a_shared = shared;
+    a.offsets = offsets;
+    a.ts = ts256;
+    a.E = E;
+    a.B1 = wt;
+    a.N = d_ff;
+    a.K = d_out;
+    a.n_cu = current_cu_count();
+    a.split_max = 1;
+    a.hin1 = h1;
+    a.hin3 = h3;
+    a.o1 = dh1;
+    a.o2 = dh3;
+    a.o3 = act;
+    a.ldo = kt;
+    st = launch_grouped_gemm_actbwd(epi, a, mt256, stream);
+    if (st != MOE_ERR_UNSUPPORTED && st != MOE_OK) return st;
+  }
+  if (two && st == MOE_ERR_UNSUPPORTED) {
     BwdGemmParams b{};
     b.A = DY;
     b.lda = d_out;

@@ -62,20 +62,6 @@ __device__ __forceinline__ int seg_of(const int32_t* ts, int E, int m) {
   return lo;
 }
 
-// d/du of u * Phi(u) = Phi(u) + u phi(u); Phi from erfc by Abramowitz and
-// Stegun 7.1.26 as in gelu_f32 (absolute error below 1.5e-7)
-__device__ __forceinline__ float gelu_grad_f32(float u) {
-  const float x = fabsf(u) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float q = fmaf(t, 1.061405429f, -1.453152027f);
-  q = fmaf(t, q, 1.421413741f);
-  q = fmaf(t, q, -0.284496736f);
-  q = fmaf(t, q, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);   // e^(-u^2/2)
-  const float erfc = q * t * e;
-  const float Phi = 0.5f * (u >= 0.f ? 2.0f - erfc : erfc);
-  return Phi + u * (0.3989422804014327f * e);
-}
 
 }  // namespace
 

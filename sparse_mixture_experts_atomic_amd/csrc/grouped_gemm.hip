@@ -484,10 +484,81 @@ __device__ __forceinline__ SplitPlan split_plan(int V, int KT, int R, int n_cu, 
 // other wavefront uses.
 // RS: fp8 activations; rsl[r] (LDS) is the scale of the wavefront's row r,
 // applied with the column scale before the activation.
-template <int EPI, int FM, bool RS = false, bool PRE = false>
+template <int EPI, int FM, bool RS = false, bool PRE = false, int BWE = 0>
 __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint16_t* st, const GemmParams& p, int e,
                                               int row0, int rows_valid, int col0, const float* rsl = nullptr) {
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
+  if constexpr (BWE != 0) {
+    // the activation's backward (B rows plain, 128 columns): per 32-row
+    // fragment, every output of an element formed at once from the fp32
+    // pre-activations, staged as bf16 (three 32 x 136 blocks) and stored as
+    // whole 16-byte pieces of rows.  BWE = 1 SwiGLU (dh1, dh3, a), 2 ReLU,
+    // 3 GELU (dh, a).
+    constexpr int NO = BWE == 1 ? 3 : 2;
+    constexpr int PITCH = 128 + 8;
+    constexpr int PR = 128 / 8;
+    const int N = p.N;
+    const int lane = threadIdx.x & 63;
+    const int fr = lane & 31, fc = lane >> 5;
+    template_for<FM>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = col0 + j * 32 + fr;
+        const bool cv = col < N;
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) {
+          float out[NO][2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int r = i * 32 + ((q + h) >> 2) * 8 + fc * 4 + ((q + h) & 3);
+            const bool ok = cv && r < rows_valid;
+            const size_t o = static_cast<size_t>(row0 + (ok ? r : 0)) * N + (ok ? col : 0);
+            const float v = acc[i][j][q + h];
+            const float h1 = ok ? p.hin1[o] : 0.f;
+            if constexpr (BWE == 1) {
+              const float h3 = ok ? p.hin3[o] : 0.f;
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * h1));
+              const float si = h1 * sg;
+              out[0][h] = v * h3 * sg * (1.0f + h1 * (1.0f - sg));
+              out[1][h] = v * si;
+              out[2][h] = si * h3;
+            } else if constexpr (BWE == 2) {
+              out[0][h] = h1 > 0.f ? v : 0.f;
+              out[1][h] = fmaxf(h1, 0.f);
+            } else {
+              out[0][h] = v * gelu_grad_f32(h1);
+              out[1][h] = gelu_f32(h1);
+            }
+          }
+          const int r = (q >> 2) * 8 + fc * 4 + (q & 3);   // rows r, r + 1 of the fragment
+#pragma unroll
+          for (int t = 0; t < NO; ++t) {
+            const uint32_t pk = pack_bf16x2(out[t][0], out[t][1]);
+            st[(t * 32 + r) * PITCH + j * 32 + fr] = static_cast<uint16_t>(pk);
+            st[(t * 32 + r + 1) * PITCH + j * 32 + fr] = static_cast<uint16_t>(pk >> 16);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+#pragma unroll
+      for (int u = 0; u < NO * 32 * PR / 64; ++u) {
+        const int c = lane + 64 * u;
+        const int t = c / (32 * PR);
+        const int r = (c / PR) % 32;
+        const int pc = (c % PR) * 8;
+        const int gr = i * 32 + r;
+        if (gr < rows_valid && col0 + pc < N) {
+          uint16_t* dst = t == NO - 1 ? p.o3 : (t == 0 ? p.o1 : p.o2);
+          const long ld = t == NO - 1 ? N : p.ldo;
+          const uint4 val = *reinterpret_cast<const uint4*>(st + (t * 32 + r) * PITCH + pc);
+          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(row0 + gr) * ld + col0 + pc) = val;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+    });
+    return;
+  }
   if constexpr (PRE) {
     // fp32 outputs (gate (+ bias) to pre1, SwiGLU's up to pre3) staged
     // through the wavefront's LDS block in two passes (SwiGLU: gate, then
@@ -716,8 +787,9 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 // shared by the segments, fp32 output through the PRE epilogue
 template <int EPI, int BK, bool FP8, int XM = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
-  constexpr bool PRE = XM >= 1;
+  constexpr bool PRE = XM == 1 || XM == 2;
   constexpr bool WG = XM == 2;
+  constexpr int BWE = XM >= 3 ? XM - 2 : 0;   // 3, 4, 5: the SwiGLU, ReLU, GELU backward epilogue
   constexpr int BM = 256;
   constexpr int R = 2;                  // split parts are whole stage pairs
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
@@ -1153,8 +1225,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
     const int col0 = EPI == EPI_SWIGLU ? nt * HC + wn * 64 : nt * BN + wn * 128;
     // (the fp32 staging of PRE takes the 128 + 8 bf16 pitch whatever OC is)
-    wave_epilogue<EPI, FM, false, PRE>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * ((PRE ? 128 : OC) + 8), p,
-                                       e, row0 + wm * WM, rows_valid - wm * WM, col0);
+    wave_epilogue<EPI, FM, false, PRE, BWE>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * ((PRE ? 128 : OC) + 8),
+                                            p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
   };
   if constexpr (!FP8) {
     if (unit < 0 && tc.rows_valid <= 64) {
@@ -1401,7 +1473,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
 
 template <int EPI, int BK, bool FP8, int XM>
 int launch_dma_pre(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
-  constexpr bool PRE = XM >= 1;
+  constexpr bool PRE = XM >= 1;          // (no split tail for any of the extra modes)
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   const long n_tiles = (p.N + HC - 1) / HC;
   long blocks = n_tiles * m_tiles_max;
@@ -1488,6 +1560,20 @@ int launch_grouped_gemm_pre(int epi, const GemmParams& p, int m_tiles_max, hipSt
   q.split_max = 1;
   if (epi == EPI_SWIGLU) return launch_dma_pre<EPI_SWIGLU, kDmaBK, false, 1>(q, m_tiles_max, stream);
   if (epi == EPI_PLAIN) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 1>(q, m_tiles_max, stream);
+  return MOE_ERR_UNSUPPORTED;
+}
+
+int launch_grouped_gemm_actbwd(int bwd_epi, const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  const bool ok = p.K % kDmaKMult == 0 && p.N % 8 == 0 && p.ldo % 8 == 0 &&
+                  static_cast<size_t>(p.N) * p.K * 2 < (size_t(1) << 31) &&
+                  static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31) && !p.gather && !p.s1 && !p.bias &&
+                  p.hin1 && p.o1 && p.o3 && (bwd_epi != BWD_EPI_SWIGLU || (p.hin3 && p.o2));
+  if (!ok) return MOE_ERR_UNSUPPORTED;
+  GemmParams q = p;
+  q.split_max = 1;
+  if (bwd_epi == BWD_EPI_SWIGLU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 3>(q, m_tiles_max, stream);
+  if (bwd_epi == BWD_EPI_RELU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 4>(q, m_tiles_max, stream);
+  if (bwd_epi == BWD_EPI_GELU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 5>(q, m_tiles_max, stream);
   return MOE_ERR_UNSUPPORTED;
 }
 

@@ -99,6 +99,21 @@ __device__ __forceinline__ float gelu_f32(float u) {
   return 0.5f * u * (u >= 0.f ? 2.0f - y : y);
 }
 
+// d/du of u * Phi(u) = Phi(u) + u phi(u); Phi from erfc by Abramowitz and
+// Stegun 7.1.26 as in gelu_f32 (absolute error below 1.5e-7)
+__device__ __forceinline__ float gelu_grad_f32(float u) {
+  const float x = fabsf(u) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);   // e^(-u^2/2)
+  const float erfc = q * t * e;
+  const float Phi = 0.5f * (u >= 0.f ? 2.0f - erfc : erfc);
+  return Phi + u * (0.3989422804014327f * e);
+}
+
 // activation of a non-gated first layer (identity for EPI_PLAIN)
 template <int EPI>
 __device__ __forceinline__ float act1(float v) {
@@ -136,6 +151,15 @@ struct GemmParams {
   // segments, pitch ldb); fp32 output to pre1
   const int32_t* kseg;
   long lda, ldb;
+  // launch_grouped_gemm_actbwd only: the activation's backward in the
+  // epilogue, from the fp32 pre-activations hin1 (hin3) [*, N]: o1 = dh1,
+  // o2 = dh3 (row pitch ldo), o3 = the activation a (pitch N), bf16
+  const float* hin1;
+  const float* hin3;
+  uint16_t* o1;
+  uint16_t* o2;
+  uint16_t* o3;
+  long ldo;
 };
 
 // Bytes of the split-tail partial buffer for n_cu compute units.
@@ -161,6 +185,10 @@ int launch_grouped_gemm_pre(int epi, const GemmParams& p, int m_tiles_max, hipSt
 // multiple of 128 columns).
 // MOE_ERR_UNSUPPORTED for shapes it does not take.
 int launch_grouped_gemm_wgrad(const GemmParams& p, int m_tiles_max, hipStream_t stream);
+// da = dY W2 with the activation's backward in the epilogue (bwd_epi: one of
+// BWD_EPI_SWIGLU, _RELU, _GELU) on the LDS-DMA kernel, B = W2 transposed to
+// [E, d_ff, d_out]; MOE_ERR_UNSUPPORTED for shapes it does not take.
+int launch_grouped_gemm_actbwd(int bwd_epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
 
 // Per-row e4m3 quantisation (quant.hip): scale[r] = max |x[r, :]| / 448 (1
 // for a zero row), q = e4m3(x / scale); rows_dev (device, or null) bounds the
