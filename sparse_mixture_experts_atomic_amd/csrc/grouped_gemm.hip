@@ -489,70 +489,71 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
                                               int row0, int rows_valid, int col0, const float* rsl = nullptr) {
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
   if constexpr (BWE != 0) {
-    // the activation's backward (B rows plain, 128 columns): per 32-row
-    // fragment, every output of an element formed at once from the fp32
-    // pre-activations, staged as bf16 (three 32 x 136 blocks) and stored as
-    // whole 16-byte pieces of rows.  BWE = 1 SwiGLU (dh1, dh3, a), 2 ReLU,
-    // 3 GELU (dh, a).
-    constexpr int NO = BWE == 1 ? 3 : 2;
-    constexpr int PITCH = 128 + 8;
-    constexpr int PR = 128 / 8;
+    // the activation's backward (B rows plain, 128 columns), per 32-row
+    // fragment: the fp32 accumulators staged through the wavefront's LDS
+    // block (32 x 132 floats), then each lane takes pieces of 8 columns of a
+    // row: 16-byte loads of the fp32 pre-activations, every output of the 8
+    // elements formed at once, 16-byte stores.  BWE = 1 SwiGLU (dh1, dh3,
+    // a), 2 ReLU, 3 GELU (dh, a).
+    constexpr int FP = 128 + 4;
+    float* sf = reinterpret_cast<float*>(st);
     const int N = p.N;
     const int lane = threadIdx.x & 63;
     const int fr = lane & 31, fc = lane >> 5;
     template_for<FM>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = col0 + j * 32 + fr;
-        const bool cv = col < N;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; q += 2) {
-          float out[NO][2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int r = i * 32 + ((q + h) >> 2) * 8 + fc * 4 + ((q + h) & 3);
-            const bool ok = cv && r < rows_valid;
-            const size_t o = static_cast<size_t>(row0 + (ok ? r : 0)) * N + (ok ? col : 0);
-            const float v = acc[i][j][q + h];
-            const float h1 = ok ? p.hin1[o] : 0.f;
-            if constexpr (BWE == 1) {
-              const float h3 = ok ? p.hin3[o] : 0.f;
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * h1));
-              const float si = h1 * sg;
-              out[0][h] = v * h3 * sg * (1.0f + h1 * (1.0f - sg));
-              out[1][h] = v * si;
-              out[2][h] = si * h3;
-            } else if constexpr (BWE == 2) {
-              out[0][h] = h1 > 0.f ? v : 0.f;
-              out[1][h] = fmaxf(h1, 0.f);
-            } else {
-              out[0][h] = v * gelu_grad_f32(h1);
-              out[1][h] = gelu_f32(h1);
-            }
-          }
-          const int r = (q >> 2) * 8 + fc * 4 + (q & 3);   // rows r, r + 1 of the fragment
-#pragma unroll
-          for (int t = 0; t < NO; ++t) {
-            const uint32_t pk = pack_bf16x2(out[t][0], out[t][1]);
-            st[(t * 32 + r) * PITCH + j * 32 + fr] = static_cast<uint16_t>(pk);
-            st[(t * 32 + r + 1) * PITCH + j * 32 + fr] = static_cast<uint16_t>(pk >> 16);
-          }
-        }
-      }
+        for (int q = 0; q < 16; ++q) sf[((q >> 2) * 8 + fc * 4 + (q & 3)) * FP + j * 32 + fr] = acc[i][j][q];
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
 #pragma unroll
-      for (int u = 0; u < NO * 32 * PR / 64; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int c = lane + 64 * u;
-        const int t = c / (32 * PR);
-        const int r = (c / PR) % 32;
-        const int pc = (c % PR) * 8;
+        const int r = c >> 4, cc = (c & 15) * 8;
         const int gr = i * 32 + r;
-        if (gr < rows_valid && col0 + pc < N) {
-          uint16_t* dst = t == NO - 1 ? p.o3 : (t == 0 ? p.o1 : p.o2);
-          const long ld = t == NO - 1 ? N : p.ldo;
-          const uint4 val = *reinterpret_cast<const uint4*>(st + (t * 32 + r) * PITCH + pc);
-          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(row0 + gr) * ld + col0 + pc) = val;
+        const bool ok = gr < rows_valid && col0 + cc < N;
+        const size_t o = ok ? static_cast<size_t>(row0 + gr) * N + col0 + cc : 0;
+        float v[8], h1[8], h3[8];
+        *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(sf + r * FP + cc);
+        *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(sf + r * FP + cc + 4);
+        *reinterpret_cast<float4*>(h1) = *reinterpret_cast<const float4*>(p.hin1 + o);
+        *reinterpret_cast<float4*>(h1 + 4) = *reinterpret_cast<const float4*>(p.hin1 + o + 4);
+        if constexpr (BWE == 1) {
+          *reinterpret_cast<float4*>(h3) = *reinterpret_cast<const float4*>(p.hin3 + o);
+          *reinterpret_cast<float4*>(h3 + 4) = *reinterpret_cast<const float4*>(p.hin3 + o + 4);
+        }
+        uint32_t w0[4], w1[4], w2[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float x0[2], x1[2], x2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int m = 2 * t + h;
+            if constexpr (BWE == 1) {
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * h1[m]));
+              const float si = h1[m] * sg;
+              x0[h] = v[m] * h3[m] * sg * (1.0f + h1[m] * (1.0f - sg));
+              x1[h] = v[m] * si;
+              x2[h] = si * h3[m];
+            } else if constexpr (BWE == 2) {
+              x0[h] = h1[m] > 0.f ? v[m] : 0.f;
+              x2[h] = fmaxf(h1[m], 0.f);
+            } else {
+              x0[h] = v[m] * gelu_grad_f32(h1[m]);
+              x2[h] = gelu_f32(h1[m]);
+            }
+          }
+          w0[t] = pack_bf16x2(x0[0], x0[1]);
+          if constexpr (BWE == 1) w1[t] = pack_bf16x2(x1[0], x1[1]);
+          w2[t] = pack_bf16x2(x2[0], x2[1]);
+        }
+        if (ok) {
+          const size_t ro = static_cast<size_t>(row0 + gr);
+          *reinterpret_cast<uint4*>(p.o1 + ro * p.ldo + col0 + cc) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+          if constexpr (BWE == 1)
+            *reinterpret_cast<uint4*>(p.o2 + ro * p.ldo + col0 + cc) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+          *reinterpret_cast<uint4*>(p.o3 + ro * N + col0 + cc) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
