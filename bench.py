@@ -55,9 +55,12 @@ def stage_bytes(cfg, a_kept: int) -> dict:
     router = T * d * sx + E * d * 4 + T * k * 8 + E * 4
     # noisy gating adds the noise projection, its bias and the draws
     router_noisy = router + E * d * 4 + E * 4 + T * E * 4
+    # draws from the counter-based generator inside the kernels: no [T, E] read
+    router_noisy_philox = router + E * d * 4 + E * 4
     dispatch = T * k * 4 + T * d * sx + a_kept * d * sx + T * k * 4 * 2
     combine = a_kept * do * sx + T * k * 8 + T * do * sx + (cfg.n_shared * T * do * sx)
-    return {"router": router, "dispatch": dispatch, "combine": combine, "router_noisy": router_noisy}
+    return {"router": router, "dispatch": dispatch, "combine": combine, "router_noisy": router_noisy,
+            "router_noisy_philox": router_noisy_philox}
 
 
 FFN_SOURCES = ("ffn.hip", "grouped_gemm.hip", "moe_internal.hpp")
@@ -223,6 +226,8 @@ def main():
     w_n, b_n, noise = W.gen_noisy_gate(cfg)
     w_n, b_n, noise = to_tensor(w_n, "cuda"), to_tensor(b_n, "cuda"), to_tensor(noise, "cuda")
     loop_st_ms["router_noisy"] = loop_ms(lambda: layer.router_noisy(x, w_n, b_n, noise, 1e-2))
+    loop_st_ms["router_noisy_philox"] = loop_ms(lambda: layer.router_noisy(x, w_n, b_n, None, 1e-2, seed=1234,
+                                                                           offset=5))
     layer.router(x)
     torch.cuda.synchronize()
 
@@ -427,7 +432,7 @@ def main():
         },
         "stages_ms_loop": loop_st_ms,
         "stages_hbm_frac_loop": {k_: byts[k_] / (loop_st_ms[k_] * 1e-3) / 1e9 / PEAK_HBM_GBPS
-                                 for k_ in ("router", "dispatch", "combine", "router_noisy")},
+                                 for k_ in ("router", "dispatch", "combine", "router_noisy", "router_noisy_philox")},
         "shared_tflops": (sh_flops / (st_ms["shared"] * 1e-3) / 1e12) if cfg.n_shared else None,
         "backward": backward,
         "fp8": fp8,

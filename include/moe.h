@@ -12,8 +12,9 @@
  * The layer is five calls, run in this order on one stream:
  *   moe_router_topk -> moe_dispatch_permute -> moe_expert_ffn_grouped
  *   (routed experts, then shared experts) -> moe_combine -> moe_aux_loss.
- * Variants: moe_router_topk_noisy in place of moe_router_topk (noisy gating
- * in training mode), and moe_dispatch_permute without the row copy followed
+ * Variants: moe_router_topk_noisy or moe_router_topk_noisy_philox in place
+ * of moe_router_topk (noisy gating in training mode, with the caller's
+ * normal draws or with draws from a counter-based generator), and moe_dispatch_permute without the row copy followed
  * by moe_expert_ffn_gathered in place of moe_expert_ffn_grouped for the
  * routed experts (the FFN reads x through the permutation).
  *
@@ -186,6 +187,42 @@ int moe_router_topk_noisy(const void* x, int x_dt, const float* w_g, const float
                           int32_t* topk_idx, float* topk_gate, float* prob_colsum,
                           float* logits_dbg, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * ---- (a'') The noisy gate's draws from a counter-based generator ------------
+ * The pages draw the normal sample inside the gate (P2 §2.1; P5 代码实战,
+ * NoisyTop1Gate in training mode) and name no generator.  Here draw number
+ * i of the stream (seed, offset) is fixed by those three integers alone:
+ *   Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+ *   Easy as 1, 2, 3", SC 2011) with key (seed low 32 bits, seed high 32
+ *   bits) on counter (j low, j high, offset low, offset high), j = i / 4,
+ *   gives words w0..w3; with p = (i mod 4) / 2, u1 = (w[2p] + 1/2) 2^-32 and
+ *   u2 = (w[2p+1] + 1/2) 2^-32, the draw is sqrt(-2 ln u1) cos(2 pi u2) for
+ *   even i and sqrt(-2 ln u1) sin(2 pi u2) for odd i (Box-Muller), computed
+ *   in fp64 and rounded once to fp32.
+ * The noisy gate uses draw t * E + e for token t and expert e, so a
+ * training step passes a fresh offset (or seed) and the same (seed, offset)
+ * reproduces its draws.
+ *
+ * moe_router_topk_noisy_philox: moe_router_topk_noisy with noise[t, e] =
+ * draw t * E + e, drawn inside the router's kernels (no [T, E] buffer).
+ * Every other argument, constraint, workspace and error as for
+ * moe_router_topk_noisy; moe_aux_loss_from_router reads its workspace with
+ * noisy = 1.
+ *
+ * moe_gate_noise_philox: out[i] = draw i for i < n (fp32 [n] out, device
+ * memory, 4-byte aligned), e.g. the [T, E] draws of one call of
+ * moe_router_topk_noisy_philox for moe_router_topk_noisy or for a replay.
+ * n = 0 launches nothing; n > 2^62 or out == NULL (n > 0) is
+ * MOE_ERR_INVALID_ARG.
+ */
+int moe_router_topk_noisy_philox(const void* x, int x_dt, const float* w_g, const float* b_g,
+                                 const float* w_n, const float* b_n, uint64_t seed, uint64_t offset,
+                                 float noise_eps, int T, int d, int E, int k, int gate_mode,
+                                 int32_t* topk_idx, float* topk_gate, float* prob_colsum,
+                                 float* logits_dbg, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+int moe_gate_noise_philox(uint64_t seed, uint64_t offset, size_t n, float* out, hipStream_t stream);
 
 /*
  * ---- (b) Dispatch: histogram, scan, stable token-order rank, capacity, permute

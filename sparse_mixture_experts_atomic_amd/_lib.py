@@ -39,6 +39,7 @@ _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
 _f = ctypes.c_float
+_u64 = ctypes.c_uint64
 
 _SIGS = {
     "moe_abi_version": (_i, []),
@@ -51,6 +52,9 @@ _SIGS = {
     "moe_router_noisy_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_router_topk_noisy": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
+    "moe_router_topk_noisy_philox": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _u64, _u64, _f, _i, _i, _i, _i, _i, _vp,
+                                          _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_gate_noise_philox": (_i, [_u64, _u64, _sz, _vp, _vp]),
     "moe_dispatch_workspace_size": (_sz, [_i, _i, _i]),
     "moe_dispatch_permute": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_ffn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
@@ -193,6 +197,23 @@ def router_topk_noisy(x, w_g, b_g, w_n, b_n, noise, noise_eps, k, gate_mode, top
                                      float(noise_eps), T, d, E, k, gate_mode, _p(topk_idx), _p(topk_gate),
                                      _p(prob_colsum), _p(logits_dbg), _p(workspace), ws_bytes, _stream(stream))
     _check("moe_router_topk_noisy", st)
+
+
+def router_topk_noisy_philox(x, w_g, b_g, w_n, b_n, seed, offset, noise_eps, k, gate_mode, topk_idx, topk_gate,
+                             prob_colsum=None, logits_dbg=None, workspace=None, stream=None):
+    T, d = x.shape
+    E = w_g.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().moe_router_topk_noisy_philox(_p(x), dtype_code(x), _p(w_g), _p(b_g), _p(w_n), _p(b_n), int(seed),
+                                            int(offset), float(noise_eps), T, d, E, k, gate_mode, _p(topk_idx),
+                                            _p(topk_gate), _p(prob_colsum), _p(logits_dbg), _p(workspace), ws_bytes,
+                                            _stream(stream))
+    _check("moe_router_topk_noisy_philox", st)
+
+
+def gate_noise_philox(seed, offset, out, stream=None):
+    st = lib().moe_gate_noise_philox(int(seed), int(offset), out.numel(), _p(out), _stream(stream))
+    _check("moe_gate_noise_philox", st)
 
 
 def dispatch_permute(topk_idx, E, capacity_, x, x_perm, counts_routed, counts_kept, offsets, dest_pos,

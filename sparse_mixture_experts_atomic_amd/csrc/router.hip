@@ -6,6 +6,7 @@
 // P3 §3.1 (keep the k largest, optionally renormalised).
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "moe_internal.hpp"
@@ -39,9 +40,61 @@ struct RouterArgs {
   // noisy gating: z += noise[t, e] * (softplus((x W_n^T)[t, e] + b_n[e]) + eps)
   const float* w_n;
   const float* b_n;
-  const float* noise;   // [T, E] standard normal draws
+  const float* noise;   // [T, E] standard normal draws, or nullptr: drawn here
   float eps;
+  unsigned long long seed, offset;   // the counter-based stream of the draws
 };
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+// As Easy as 1, 2, 3", SC 2011, section 5): ten rounds over a 128-bit
+// counter under a 64-bit key; each round multiplies words 0 and 2 by fixed
+// 32-bit multipliers, keeps the low halves, xors the high halves into the
+// other two words with the key, and permutes; the key takes a Weyl step
+// between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
+                                              uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint32_t hi0 = __umulhi(kM0, c0), lo0 = kM0 * c0;
+    const uint32_t hi1 = __umulhi(kM1, c2), lo1 = kM1 * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+}
+
+// Standard normal draw i of the stream (seed, offset): counter block i / 4
+// (counter words: block low, block high, offset low, offset high; key: seed
+// low, seed high), the pair of output words (i mod 4) / 2 as u1, u2 =
+// (word + 1/2) 2^-32, and the Box-Muller value sqrt(-2 ln u1) times cos
+// (even i) or sin (odd i) of 2 pi u2.  In fp64, rounded once to fp32.
+__device__ __forceinline__ float philox_normal(unsigned long long seed, unsigned long long offset,
+                                               unsigned long long i) {
+  const unsigned long long j = i >> 2;
+  uint32_t c0 = static_cast<uint32_t>(j), c1 = static_cast<uint32_t>(j >> 32);
+  uint32_t c2 = static_cast<uint32_t>(offset), c3 = static_cast<uint32_t>(offset >> 32);
+  philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  const bool second = (i >> 1) & 1;
+  const double u1 = (static_cast<double>(second ? c2 : c0) + 0.5) * 0x1p-32;
+  const double u2 = (static_cast<double>(second ? c3 : c1) + 0.5) * 0x1p-32;
+  const double r = sqrt(-2.0 * log(u1));
+  double sn, cs;
+  sincospi(2.0 * u2, &sn, &cs);
+  return static_cast<float>((i & 1) ? r * sn : r * cs);
+}
+
+// the noisy gate's draw for flat index t E + e
+__device__ __forceinline__ float gate_draw(const RouterArgs& a, size_t i) {
+  return a.noise ? a.noise[i] : philox_normal(a.seed, a.offset, i);
+}
 
 // ln(1 + e^u) without overflow for large u or loss of the small term
 __device__ __forceinline__ float softplus_f(float u) { return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))); }
@@ -386,7 +439,7 @@ __global__ __launch_bounds__(kRtThreads) void router_generic_kernel(RouterArgs a
           if (e < a.E && t < a.T) {
             float u = static_cast<float>(tot[i][j]);
             if (a.b_n) u += a.b_n[e];
-            lg[(ty * 2 + i) * a.E + e] += a.noise[static_cast<size_t>(t) * a.E + e] * (softplus_f(u) + a.eps);
+            lg[(ty * 2 + i) * a.E + e] += gate_draw(a, static_cast<size_t>(t) * a.E + e) * (softplus_f(u) + a.eps);
           }
         }
     }
@@ -587,7 +640,7 @@ __global__ __launch_bounds__(64 * kM8Waves) void router_mf8_kernel(RouterArgs a,
         }
         if (a.b_n) zn += a.b_n[ee];
         const int t = t0 + tl;
-        if (t < a.T) z += a.noise[static_cast<size_t>(t) * a.E + ee] * (softplus_f(zn) + a.eps);
+        if (t < a.T) z += gate_draw(a, static_cast<size_t>(t) * a.E + ee) * (softplus_f(zn) + a.eps);
       }
     }
     lg[tl][ee] = z;
@@ -807,8 +860,13 @@ __global__ __launch_bounds__(kFnThreads) void router_finish_kernel(RouterArgs a,
     for (int u = 0; u < PER; ++u) bg[u] = a.b_g[jj[u] % a.E];
   }
   if constexpr (NOISY) {
+    if (a.noise) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) dr[u] = a.noise[static_cast<size_t>(t0) * a.E + jj[u]];
+      for (int u = 0; u < PER; ++u) dr[u] = a.noise[static_cast<size_t>(t0) * a.E + jj[u]];
+    } else {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) dr[u] = philox_normal(a.seed, a.offset, static_cast<size_t>(t0) * a.E + jj[u]);
+    }
     if (a.b_n) {
 #pragma unroll
       for (int u = 0; u < PER; ++u) bn[u] = a.b_n[jj[u] % a.E];
@@ -1041,21 +1099,24 @@ inline int router_nb(int T, int d, int E, int x_dt, bool noisy) {
   return m8 ? (T + 16 * tg8 - 1) / (16 * tg8) : (mf ? (T + kFnTok - 1) / kFnTok : router_blocks(T));
 }
 
-// the launches of both entry points; arguments already validated.  noise ==
-// nullptr: the clean router.  bf16: MFMA kernels (up to 8 experts: whole
+// the launches of every router entry point; arguments already validated.
+// noise == nullptr and !drawn: the clean router; drawn: the noisy router
+// with its draws from the stream (seed, offset).  bf16: MFMA kernels (up to 8 experts: whole
 // rows per block, one launch; otherwise the tiled logits GEMM, then the
 // finishing kernel); fp32 activations: the generic kernel.
 int router_run(const void* x, int x_dt, const float* w_g, const float* b_g, const float* w_n, const float* b_n,
                const float* noise, float eps, int T, int d, int E, int k, int gate_mode, int32_t* topk_idx,
-               float* topk_gate, float* prob_colsum, float* logits_dbg, void* workspace, hipStream_t stream) {
-  const bool noisy = noise != nullptr;
+               float* topk_gate, float* prob_colsum, float* logits_dbg, void* workspace, hipStream_t stream,
+               bool drawn = false, unsigned long long seed = 0, unsigned long long offset = 0) {
+  const bool noisy = noise != nullptr || drawn;
   const bool m8 = x_dt == MOE_BF16 && E <= kM8MaxE;
   const bool mf = x_dt == MOE_BF16 && !m8;
   float* part = static_cast<float*>(workspace);
   int kw8 = 1, tg8 = 1;
   mf8_shape(T, d, noisy ? 1 : kM8Cpw, kw8, tg8);
   const int nb = router_nb(T, d, E, x_dt, noisy);
-  RouterArgs a{x, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, part, logits_dbg, w_n, b_n, noise, eps};
+  RouterArgs a{x,     w_g,     b_g,  T,   d,   E,   k,    gate_mode, topk_idx, topk_gate, part,
+               logits_dbg, w_n, b_n, drawn ? nullptr : noise, eps, seed, offset};
   if (T > 0 && m8) {
     if (noisy)
       hipLaunchKernelGGL(router_mf8_kernel<true>, dim3(nb), dim3(64 * kw8 * tg8), 0, stream, a, kw8, tg8);
@@ -1158,9 +1219,34 @@ int scratch_on_current_device(void** out) {
 }  // namespace
 }  // namespace moe
 
+namespace moe {
+namespace {
+
+// out[i] = standard normal draw start + i of the stream (seed, offset), a
+// grid-stride loop
+__global__ __launch_bounds__(256) void gate_noise_kernel(unsigned long long seed, unsigned long long offset, size_t n,
+                                                         float* __restrict__ out) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    out[i] = philox_normal(seed, offset, i);
+}
+
+}  // namespace
+}  // namespace moe
+
 using namespace moe;
 
 extern "C" {
+
+int moe_gate_noise_philox(uint64_t seed, uint64_t offset, size_t n, float* out, hipStream_t stream) {
+  if (n > (size_t(1) << 62)) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 8 * 256);
+  hipLaunchKernelGGL(gate_noise_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<unsigned long long>(seed), static_cast<unsigned long long>(offset), n, out);
+  return check_launch();
+}
 
 size_t moe_router_workspace_size(int T, int d, int E, int x_dt) {
   if (T < 0 || E < 1) return 0;
@@ -1221,6 +1307,21 @@ int moe_router_topk_noisy(const void* x, int x_dt, const float* w_g, const float
   // no tokens: only the (zero) column sums, as the clean router writes them
   return router_run(x, x_dt, w_g, b_g, w_n, b_n, T > 0 ? noise : nullptr, noise_eps, T, d, E, k, gate_mode,
                     topk_idx, topk_gate, prob_colsum, logits_dbg, workspace, stream);
+}
+
+int moe_router_topk_noisy_philox(const void* x, int x_dt, const float* w_g, const float* b_g, const float* w_n,
+                                 const float* b_n, uint64_t seed, uint64_t offset, float noise_eps, int T, int d,
+                                 int E, int k, int gate_mode, int32_t* topk_idx, float* topk_gate,
+                                 float* prob_colsum, float* logits_dbg, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  int st = router_check(x, x_dt, w_g, b_g, T, d, E, k, gate_mode, topk_idx, topk_gate, prob_colsum, logits_dbg);
+  if (st != MOE_OK) return st;
+  if (!w_n || !aligned16(w_n) || (b_n && !aligned16(b_n))) return MOE_ERR_INVALID_ARG;
+  if (!(noise_eps >= 0.f) || noise_eps > 3.0e38f) return MOE_ERR_INVALID_ARG;   // NaN, negative or infinite
+  if (!workspace_ok(T, prob_colsum, workspace, workspace_bytes, moe_router_noisy_workspace_size(T, d, E, x_dt)))
+    return MOE_ERR_WORKSPACE;
+  return router_run(x, x_dt, w_g, b_g, w_n, b_n, nullptr, noise_eps, T, d, E, k, gate_mode, topk_idx, topk_gate,
+                    prob_colsum, logits_dbg, workspace, stream, T > 0, seed, offset);
 }
 
 int moe_aux_loss_from_router(const int32_t* counts_routed, const void* router_workspace, size_t workspace_bytes,

@@ -86,15 +86,24 @@ class MoELayer:
                       self.prob_colsum if with_colsum else None, self.logits, self.ws_router)
         self._router_ws = (self.ws_router, False)
 
-    def router_noisy(self, x, w_n, b_n, noise, eps=1e-2, with_colsum=False):
+    def router_noisy(self, x, w_n, b_n, noise, eps=1e-2, with_colsum=False, seed=None, offset=0):
         """Training-mode router with noisy gating: the same outputs as router(),
-        from logits with noise[t, e] * (softplus(x W_n^T + b_n) + eps) added."""
+        from logits with noise[t, e] * (softplus(x W_n^T + b_n) + eps) added.
+        noise: the [T, E] normal draws, or None with ``seed`` given: draw
+        t E + e of the counter-based stream (seed, offset), drawn in the
+        router's kernels."""
         if getattr(self, "ws_router_noisy", None) is None:
             act = L.F32 if self.act_dtype == torch.float32 else L.BF16
             self.ws_router_noisy = self._ws(L.router_noisy_workspace_size(self.T, self.d, self.E, act), x.device)
-        L.router_topk_noisy(x, self.w["w_g"], self.w.get("b_g"), w_n, b_n, noise, eps, self.k, self.gate,
-                            self.topk_idx, self.topk_gate, self.prob_colsum if with_colsum else None, None,
-                            self.ws_router_noisy)
+        colsum = self.prob_colsum if with_colsum else None
+        if noise is None:
+            if seed is None:
+                raise ValueError("router_noisy needs the draws (noise) or a seed for the counter-based stream")
+            L.router_topk_noisy_philox(x, self.w["w_g"], self.w.get("b_g"), w_n, b_n, seed, offset, eps, self.k,
+                                       self.gate, self.topk_idx, self.topk_gate, colsum, None, self.ws_router_noisy)
+        else:
+            L.router_topk_noisy(x, self.w["w_g"], self.w.get("b_g"), w_n, b_n, noise, eps, self.k, self.gate,
+                                self.topk_idx, self.topk_gate, colsum, None, self.ws_router_noisy)
         self._router_ws = (self.ws_router_noisy, True)
 
     def dispatch(self, x, topk_idx=None):

@@ -120,3 +120,81 @@ def test_noisy_router_zero_tokens_writes_zero_column_sums():
     L.router_topk_noisy(x, w_g, None, w_g, None, noise, 1e-2, cfg.k, L.GATE_RENORM, idx, g, colsum, None, ws)
     torch.cuda.synchronize()
     assert torch.all(colsum.cpu() == 0)
+
+
+# ---- draws from the counter-based generator (moe_gate_noise_philox and
+# moe_router_topk_noisy_philox) --------------------------------------------
+
+from oracle import philox as OP    # noqa: E402
+
+
+@pytest.mark.parametrize("seed,offset,n", [(0, 0, 1000003), (0x0123456789ABCDEF, 0xFEDCBA9876543210, 65537),
+                                           (2 ** 64 - 1, 2 ** 64 - 1, 4099)])
+def test_philox_draws_match_oracle(seed, offset, n):
+    say(f"philox draws: seed {seed:#x} offset {offset:#x} n {n}")
+    out = torch.full((n,), -7.0, dtype=torch.float32, device="cuda")
+    L.gate_noise_philox(seed, offset, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = OP.philox_normals(seed, offset, n)
+    # fp64 on both sides, rounded once to fp32 on the GPU: within one fp32
+    # ulp of the oracle, and the same fp32 value unless the fp64 results sit
+    # on either side of a rounding boundary
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.all(err <= ulp), f"max err {np.max(err / ulp):.2f} ulp"
+    differ = int(np.sum(got != ref.astype(np.float32).astype(np.float64)))
+    assert differ <= max(2, n // 100000), differ
+    say(f"  {differ} of {n} draws differ from the oracle's fp32 rounding (by one ulp)")
+
+
+PHILOX_CASES = ["mixtral_p2", "switch_p5_top1", "deepseek", "stress", "tiny_f32", "f32_ragged", "bf16_e7_wide",
+                "bf16_kslices", "bf16_t1_e1"]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", PHILOX_CASES)
+def test_noisy_router_philox_matches_oracle(name):
+    cfg, eps, bias = CASES[name]
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    seed, offset = 0x5EED0000 + cfg.seed, 3 * cfg.seed + 1
+    say(f"noisy router, drawn on the device {name}: T={T} d={d} E={E} k={k} seed {seed:#x} offset {offset}")
+    dev = "cuda"
+    x = W.gen_x(cfg)
+    w_g, b_g = W.gen_router(cfg)
+    w_n, b_n, _ = W.gen_noisy_gate(cfg, bias)
+    dt = L.F32 if cfg.act_dtype == "f32" else L.BF16
+    t = lambda a: to_tensor(a, dev)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    gte = torch.full((T, k), -7.0, dtype=torch.float32, device=dev)
+    colsum = torch.full((E,), -7.0, dtype=torch.float32, device=dev)
+    lg = torch.full((T, E), -7.0, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(L.router_noisy_workspace_size(T, d, E, dt), 256), dtype=torch.uint8, device=dev)
+    L.router_topk_noisy_philox(t(x), t(w_g), t(b_g), t(w_n), t(b_n), seed, offset, eps, k, L.GATE_MODES[cfg.gate],
+                               idx, gte, colsum, lg, ws)
+    torch.cuda.synchronize()
+    got = (idx.cpu().numpy(), gte.cpu().numpy().astype(np.float64), colsum.cpu().numpy().astype(np.float64),
+           lg.cpu().numpy().astype(np.float64))
+
+    # against the oracle, with the oracle's draws of the same stream (fp32, as
+    # the layer holds them)
+    noise = OP.gate_noise(seed, offset, T, E).astype(np.float32)
+    f64 = lambda a: None if a is None else a.astype(np.float64)
+    z = O.noisy_router_logits(O.to_f64(x, cfg.act_dtype), f64(w_g), f64(b_g), f64(w_n), f64(b_n), f64(noise), eps)
+    tie, eg, ec = compare_router(name, z, k, cfg.gate, got[0], got[1], got[2])
+    zerr = float(np.max(np.abs(got[3] - z) / np.maximum(1.0, np.max(np.abs(z), axis=1, keepdims=True))))
+    assert zerr <= 1e-5, f"{name}: noisy logit err {zerr:.3e}"
+
+    # the same bits as moe_router_topk_noisy fed the generator's [T, E] draws
+    drawn = torch.empty((T, E), dtype=torch.float32, device=dev)
+    L.gate_noise_philox(seed, offset, drawn)
+    ref = _run(x, w_g, b_g, w_n, b_n, drawn.cpu().numpy(), eps, k, cfg.gate, T, d, E, dt)
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+    # another offset draws another sample
+    if T * E >= 64:
+        L.router_topk_noisy_philox(t(x), t(w_g), t(b_g), t(w_n), t(b_n), seed, offset + 1, eps, k,
+                                   L.GATE_MODES[cfg.gate], idx, gte, colsum, lg, ws)
+        torch.cuda.synchronize()
+        assert not np.array_equal(lg.cpu().numpy().astype(np.float64), got[3])
+    say(f"  near-tied {int(tie.sum())}, gate err {eg:.2e}, colsum err {ec:.2e}, logit err {zerr:.2e}")
