@@ -339,8 +339,11 @@ def main():
         backward = {"ms_per_train_step": ms_train, "train_tokens_per_s": cfg.T / (ms_train * 1e-3),
                     "stages_ms": bms, "ffn_bwd_flops": bwd_flops,
                     "ffn_bwd_tflops": bwd_flops / (bms["experts"] * 1e-3) / 1e12,
-                    "note": "forward + backward (moe_combine_backward, moe_expert_ffn_grouped_backward, "
-                            "moe_router_backward, moe_permute_backward); stage medians with HIP events between them"}
+                    "kept_pre_activations": bool(blayer._kept and blayer._kept["routed"]),
+                    "note": "training forward (moe_expert_ffn_grouped_train: the first product's fp32 "
+                            "pre-activations kept) + backward (moe_combine_backward, "
+                            "moe_expert_ffn_grouped_backward_kept, moe_router_backward, moe_permute_backward); "
+                            "stage medians with HIP events between them"}
         del blayer
 
     # timed region 6 (last): the same shapes with e4m3 expert weights and the

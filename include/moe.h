@@ -505,6 +505,43 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Training forward and backward with the first product kept (no
+ * recomputation in the backward).
+ *
+ * moe_expert_ffn_grouped_train: moe_expert_ffn_grouped for kind RELU, GELU
+ * or SWIGLU with bf16 activations and weights (PACKED or SHARED rows), which
+ * also writes the fp32 pre-activations of the first product, the values its
+ * activation was applied to:
+ *   h1  [max_rows, d_ff] fp32 out: W1 x + b1 (RELU, GELU), W1 x (SWIGLU)
+ *   h3  [max_rows, d_ff] fp32 out: W3 x (SWIGLU only; NULL otherwise)
+ * y_rows is the same, bit for bit, as moe_expert_ffn_grouped's.  Shapes the
+ * LDS-DMA GEMM does not take (d not a multiple of 128, or a weight matrix of
+ * 2 GiB and more) return MOE_ERR_UNSUPPORTED before writing y_rows, h1 or
+ * h3: run moe_expert_ffn_grouped and moe_expert_ffn_grouped_backward then.
+ * kind LINEAR, fp8 or fp32 data, or h1 == NULL with max_rows > 0, are
+ * MOE_ERR_INVALID_ARG.  Workspace: moe_ffn_workspace_size.
+ *
+ * moe_expert_ffn_grouped_backward_kept: moe_expert_ffn_grouped_backward
+ * with h1 (h3) the pre-activations kept by moe_expert_ffn_grouped_train for
+ * the same rows and weights, read instead of recomputed; the gradients are
+ * the same, bit for bit.  Its workspace (moe_ffn_backward_kept_workspace_size)
+ * leaves out the two [max_rows, d_ff] fp32 buffers of the recomputation.
+ */
+int moe_expert_ffn_grouped_train(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
+                                 const int32_t* offsets, int E, int d, int d_ff, int d_out,
+                                 const void* w1, const void* w3, const void* w2, int w_dt,
+                                 const float* b1, const float* b2, void* y_rows, float* h1, float* h3,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t moe_ffn_backward_kept_workspace_size(int kind, int max_rows, int E, int d, int d_ff, int d_out);
+int moe_expert_ffn_grouped_backward_kept(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
+                                         const int32_t* offsets, int E, int d, int d_ff, int d_out,
+                                         const void* w1, const void* w3, const void* w2, int w_dt,
+                                         const float* b1, const float* b2, const float* h1, const float* h3,
+                                         const void* dy_rows, void* dx_rows, float* dw1, float* dw3, float* dw2,
+                                         float* db1, float* db2, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
  * Router backward.  From the forward's fp32 logits z [T, E] (logits_dbg of
  * moe_router_topk), its top-k ids and gates and the gate gradients dgate of
  * moe_combine_backward, per token in fp32: p = softmax(z); the gate

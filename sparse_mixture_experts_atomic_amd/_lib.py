@@ -73,6 +73,12 @@ _SIGS = {
     "moe_ffn_backward_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn_grouped_backward": (_i, [_i, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_grouped_train": (_i, [_i, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp,
+                                          _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_ffn_backward_kept_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "moe_expert_ffn_grouped_backward_kept": (_i, [_i, _vp, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _i,
+                                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                                  _vp]),
     "moe_router_backward_workspace_size": (_sz, [_i, _i, _i]),
     "moe_router_backward": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _vp, _vp, _vp,
                                  _vp, _sz, _vp]),
@@ -292,6 +298,36 @@ def expert_ffn_grouped_backward(kind, x_rows, max_rows, row_mode, offsets, E, d,
                                                _p(b2), _p(dy_rows), _p(dx_rows), _p(dw1), _p(dw3), _p(dw2), _p(db1),
                                                _p(db2), _p(workspace), ws_bytes, _stream(stream))
     _check("moe_expert_ffn_grouped_backward", st)
+
+
+def expert_ffn_grouped_train(kind, x_rows, max_rows, row_mode, offsets, E, d, d_ff, d_out, w1, w3, w2, b1, b2,
+                             y_rows, h1, h3, workspace, stream=None) -> bool:
+    """Training forward keeping the first product's fp32 pre-activations in
+    h1 (h3); False (nothing written) where the library does not take the
+    shape, and moe_expert_ffn_grouped must run instead."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().moe_expert_ffn_grouped_train(kind, _p(x_rows), dtype_code(x_rows), max_rows, row_mode, _p(offsets), E,
+                                            d, d_ff, d_out, _p(w1), _p(w3), _p(w2), dtype_code(w1), _p(b1), _p(b2),
+                                            _p(y_rows), _p(h1), _p(h3), _p(workspace), ws_bytes, _stream(stream))
+    if st == ERR_UNSUPPORTED:
+        return False
+    _check("moe_expert_ffn_grouped_train", st)
+    return True
+
+
+def ffn_backward_kept_workspace_size(kind, max_rows, E, d, d_ff, d_out) -> int:
+    return lib().moe_ffn_backward_kept_workspace_size(kind, max_rows, E, d, d_ff, d_out)
+
+
+def expert_ffn_grouped_backward_kept(kind, x_rows, max_rows, row_mode, offsets, E, d, d_ff, d_out, w1, w3, w2, b1,
+                                     b2, h1, h3, dy_rows, dx_rows, dw1, dw3, dw2, db1, db2, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().moe_expert_ffn_grouped_backward_kept(kind, _p(x_rows), dtype_code(x_rows), max_rows, row_mode,
+                                                    _p(offsets), E, d, d_ff, d_out, _p(w1), _p(w3), _p(w2),
+                                                    dtype_code(w1), _p(b1), _p(b2), _p(h1), _p(h3), _p(dy_rows),
+                                                    _p(dx_rows), _p(dw1), _p(dw3), _p(dw2), _p(db1), _p(db2),
+                                                    _p(workspace), ws_bytes, _stream(stream))
+    _check("moe_expert_ffn_grouped_backward_kept", st)
 
 
 def router_backward_workspace_size(T, d, E) -> int:

@@ -577,7 +577,7 @@ struct FfnBwdLayout {
   size_t ts128, ts256, h1, h3, dh, a, wt, partial, kp, xt, dyt, at, dht, wofs_o, wofs_1, tsw_o, tsw_1, total;
 };
 
-FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int d_out) {
+FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int d_out, bool stashed = false) {
   FfnBwdLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -590,8 +590,9 @@ FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int 
   const size_t kt = two ? static_cast<size_t>(d_ff) * (kind == MOE_FFN_SWIGLU ? 2 : 1) : static_cast<size_t>(d_out);
   L.ts128 = take(static_cast<size_t>(E + 1) * 4);
   L.ts256 = take(static_cast<size_t>(E + 1) * 4);
-  L.h1 = two ? take(ff * 4) : 0;
-  L.h3 = kind == MOE_FFN_SWIGLU ? take(ff * 4) : 0;
+  // the recomputed pre-activations (none when the caller kept them)
+  L.h1 = two && !stashed ? take(ff * 4) : 0;
+  L.h3 = kind == MOE_FFN_SWIGLU && !stashed ? take(ff * 4) : 0;
   L.dh = two ? take(static_cast<size_t>(max_rows) * kt * 2) : 0;
   L.a = two ? take(ff * 2) : 0;
   // transposed weights: the first layer's [E, d, kt] for dX, before it the
@@ -614,21 +615,13 @@ FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int 
   return L;
 }
 
-}  // namespace
-}  // namespace moe
-
-extern "C" {
-
-size_t moe_ffn_backward_workspace_size(int kind, int max_rows, int E, int d, int d_ff, int d_out) {
-  if (max_rows < 0 || E < 1 || d < 1 || d_out < 1) return 0;
-  return ffn_bwd_layout(kind, max_rows, E, d, d_ff, d_out).total;
-}
-
-int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
-                                    const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1,
-                                    const void* w3, const void* w2, int w_dt, const float* b1, const float* b2,
-                                    const void* dy_rows, void* dx_rows, float* dw1, float* dw3, float* dw2, float* db1,
-                                    float* db2, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// The backward of the grouped FFN; h1_in (h3_in): the first product's fp32
+// pre-activations kept by the training forward, or nullptr to recompute them.
+int ffn_backward_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode, const int32_t* offsets,
+                     int E, int d, int d_ff, int d_out, const void* w1, const void* w3, const void* w2, int w_dt,
+                     const float* b1, const float* b2, const void* dy_rows, void* dx_rows, float* dw1, float* dw3,
+                     float* dw2, float* db1, float* db2, const float* h1_in, const float* h3_in, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
   if (kind != MOE_FFN_LINEAR && kind != MOE_FFN_RELU && kind != MOE_FFN_SWIGLU && kind != MOE_FFN_GELU)
     return MOE_ERR_INVALID_ARG;
   if (row_mode != MOE_ROWS_PACKED && row_mode != MOE_ROWS_SHARED) return MOE_ERR_INVALID_ARG;
@@ -645,10 +638,13 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   if (kind == MOE_FFN_SWIGLU && (b1 || b2)) return MOE_ERR_UNSUPPORTED;
   if (!two && b2) return MOE_ERR_INVALID_ARG;
   if ((b1 != nullptr) != (db1 != nullptr) || (b2 != nullptr) != (db2 != nullptr)) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {x_rows, offsets, w1, w3, w2, b1, b2, dy_rows, dx_rows, dw1, dw3, dw2, db1, db2};
+  const bool stashed = h1_in != nullptr;
+  if (stashed && (!two || (kind == MOE_FFN_SWIGLU) != (h3_in != nullptr))) return MOE_ERR_INVALID_ARG;
+  if (!stashed && h3_in) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_rows, offsets, w1, w3, w2, b1, b2, dy_rows, dx_rows, dw1, dw3, dw2, db1, db2, h1_in, h3_in};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
-  const FfnBwdLayout lay = ffn_bwd_layout(kind, max_rows, E, d, d_ff, d_out);
+  const FfnBwdLayout lay = ffn_bwd_layout(kind, max_rows, E, d, d_ff, d_out, stashed);
   if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
   if (max_rows == 0) {
     // no rows: every weight gradient is zero (a fill kernel, no memset node)
@@ -662,8 +658,10 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   }
   char* ws = static_cast<char*>(workspace);
   int32_t* ts128 = reinterpret_cast<int32_t*>(ws + lay.ts128);
-  float* h1 = two ? reinterpret_cast<float*>(ws + lay.h1) : nullptr;
-  float* h3 = kind == MOE_FFN_SWIGLU ? reinterpret_cast<float*>(ws + lay.h3) : nullptr;
+  float* h1w = two && !stashed ? reinterpret_cast<float*>(ws + lay.h1) : nullptr;
+  float* h3w = kind == MOE_FFN_SWIGLU && !stashed ? reinterpret_cast<float*>(ws + lay.h3) : nullptr;
+  const float* h1 = stashed ? h1_in : h1w;
+  const float* h3 = stashed ? h3_in : h3w;
   const int n1 = two ? d_ff : d_out;
   // dh: [max_rows, kt]; for SwiGLU dh1 in columns [0, d_ff), dh3 in [d_ff, 2 d_ff)
   const int kt = kind == MOE_FFN_SWIGLU ? 2 * n1 : n1;
@@ -687,8 +685,8 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
   st = launch_tile_map(offsets, E, kGemmBM, ts256, stream);
   if (st != MOE_OK) return st;
   const int mt256 = (max_rows + kGemmBM - 1) / kGemmBM + E;
-  bool pre_done = false;
-  if (two) {
+  bool pre_done = stashed;
+  if (two && !stashed) {
     GemmParams f{};
     f.A = X;
     f.a_shared = shared;
@@ -702,8 +700,8 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     f.K = d;
     f.n_cu = current_cu_count();
     f.split_max = 1;
-    f.pre1 = h1;
-    f.pre3 = h3;
+    f.pre1 = h1w;
+    f.pre3 = h3w;
     st = launch_grouped_gemm_pre(kind == MOE_FFN_SWIGLU ? EPI_SWIGLU : EPI_PLAIN, f, mt256, stream);
     if (st == MOE_OK) pre_done = true;
     else if (st != MOE_ERR_UNSUPPORTED) return st;
@@ -722,7 +720,7 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     g.offsets = offsets;
     g.ts = ts128;
     g.E = E;
-    g.Cf = h1;
+    g.Cf = h1w;
     g.ldc = d_ff;
     g.bias = b1;
     st = launch_bwd_gemm(BWD_FWD, BWD_EPI_STORE, g, mt128, stream);
@@ -730,7 +728,7 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     if (h3) {
       g.B = static_cast<const uint16_t*>(w3);
       g.bias = nullptr;
-      g.Cf = h3;
+      g.Cf = h3w;
       st = launch_bwd_gemm(BWD_FWD, BWD_EPI_STORE, g, mt128, stream);
       if (st != MOE_OK) return st;
     }
@@ -922,6 +920,49 @@ int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, in
     st = check_launch();
   }
   return st;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+size_t moe_ffn_backward_workspace_size(int kind, int max_rows, int E, int d, int d_ff, int d_out) {
+  if (max_rows < 0 || E < 1 || d < 1 || d_out < 1) return 0;
+  return ffn_bwd_layout(kind, max_rows, E, d, d_ff, d_out).total;
+}
+
+size_t moe_ffn_backward_kept_workspace_size(int kind, int max_rows, int E, int d, int d_ff, int d_out) {
+  if (max_rows < 0 || E < 1 || d < 1 || d_out < 1) return 0;
+  return ffn_bwd_layout(kind, max_rows, E, d, d_ff, d_out, true).total;
+}
+
+int moe_expert_ffn_grouped_backward(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
+                                    const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1,
+                                    const void* w3, const void* w2, int w_dt, const float* b1, const float* b2,
+                                    const void* dy_rows, void* dx_rows, float* dw1, float* dw3, float* dw2, float* db1,
+                                    float* db2, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return ffn_backward_run(kind, x_rows, act_dt, max_rows, row_mode, offsets, E, d, d_ff, d_out, w1, w3, w2, w_dt, b1,
+                          b2, dy_rows, dx_rows, dw1, dw3, dw2, db1, db2, nullptr, nullptr, workspace, workspace_bytes,
+                          stream);
+}
+
+int moe_expert_ffn_grouped_backward_kept(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
+                                         const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1,
+                                         const void* w3, const void* w2, int w_dt, const float* b1, const float* b2,
+                                         const float* h1, const float* h3, const void* dy_rows, void* dx_rows,
+                                         float* dw1, float* dw3, float* dw2, float* db1, float* db2, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  if (max_rows > 0 && !h1) return MOE_ERR_INVALID_ARG;
+  if (kind == MOE_FFN_LINEAR) return MOE_ERR_INVALID_ARG;
+  if (max_rows == 0) {
+    // nothing was kept; the gradients are zero as for the recomputing call
+    return ffn_backward_run(kind, x_rows, act_dt, 0, row_mode, offsets, E, d, d_ff, d_out, w1, w3, w2, w_dt, b1, b2,
+                            dy_rows, dx_rows, dw1, dw3, dw2, db1, db2, nullptr, nullptr, workspace, workspace_bytes,
+                            stream);
+  }
+  return ffn_backward_run(kind, x_rows, act_dt, max_rows, row_mode, offsets, E, d, d_ff, d_out, w1, w3, w2, w_dt, b1,
+                          b2, dy_rows, dx_rows, dw1, dw3, dw2, db1, db2, h1, h3, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

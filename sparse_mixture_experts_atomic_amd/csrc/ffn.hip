@@ -101,7 +101,8 @@ inline int m_tiles_max(int max_rows, int E) { return (max_rows + kGemmBM - 1) / 
 int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode, const int32_t* gather,
             int n_src, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1, const void* w3,
             const void* w2, int w_dt, const float* s1, const float* s3, const float* s2, const float* b1,
-            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream);
+            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream,
+            float* h1 = nullptr, float* h3 = nullptr);
 
 }  // namespace
 
@@ -144,6 +145,23 @@ int moe_expert_ffn_grouped(int kind, const void* x_rows, int act_dt, int max_row
   if (row_mode != MOE_ROWS_PACKED && row_mode != MOE_ROWS_SHARED) return MOE_ERR_INVALID_ARG;
   return ffn_run(kind, x_rows, act_dt, max_rows, row_mode, nullptr, 0, offsets, E, d, d_ff, d_out, w1, w3, w2, w_dt,
                  s1, s3, s2, b1, b2, y_rows, workspace, workspace_bytes, stream);
+}
+
+int moe_expert_ffn_grouped_train(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode,
+                                 const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1,
+                                 const void* w3, const void* w2, int w_dt, const float* b1, const float* b2,
+                                 void* y_rows, float* h1, float* h3, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (row_mode != MOE_ROWS_PACKED && row_mode != MOE_ROWS_SHARED) return MOE_ERR_INVALID_ARG;
+  if (max_rows > 0 && !h1) return MOE_ERR_INVALID_ARG;
+  if (kind == MOE_FFN_LINEAR) return MOE_ERR_INVALID_ARG;   // no activation: nothing to keep
+  if (max_rows == 0) {
+    // validate as the forward does, keep nothing
+    return ffn_run(kind, x_rows, act_dt, 0, row_mode, nullptr, 0, offsets, E, d, d_ff, d_out, w1, w3, w2, w_dt,
+                   nullptr, nullptr, nullptr, b1, b2, y_rows, workspace, workspace_bytes, stream);
+  }
+  return ffn_run(kind, x_rows, act_dt, max_rows, row_mode, nullptr, 0, offsets, E, d, d_ff, d_out, w1, w3, w2, w_dt,
+                 nullptr, nullptr, nullptr, b1, b2, y_rows, workspace, workspace_bytes, stream, h1, h3);
 }
 
 int moe_expert_ffn_gathered(int kind, const void* x, int act_dt, int n_src, const int32_t* perm_token,
@@ -253,7 +271,8 @@ namespace {
 int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode, const int32_t* gather,
             int n_src, const int32_t* offsets, int E, int d, int d_ff, int d_out, const void* w1, const void* w3,
             const void* w2, int w_dt, const float* s1, const float* s3, const float* s2, const float* b1,
-            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+            const float* b2, void* y_rows, void* workspace, size_t workspace_bytes, hipStream_t stream,
+            float* h1, float* h3) {
   if (kind != MOE_FFN_LINEAR && kind != MOE_FFN_RELU && kind != MOE_FFN_SWIGLU && kind != MOE_FFN_GELU)
     return MOE_ERR_INVALID_ARG;
   if (act_dt != MOE_F32 && act_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
@@ -279,7 +298,13 @@ int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode
     const int kmul = fp8 ? 16 : 8;
     if (d % kmul != 0 || (two && d_ff % kmul != 0)) return MOE_ERR_UNSUPPORTED;
   }
-  const void* ptrs[] = {x_rows, offsets, w1, w3, w2, s1, s3, s2, b1, b2, y_rows};
+  // training forward: the first product's fp32 pre-activations kept too
+  // (bf16 activations and weights, a two-layer kind, packed or shared rows)
+  const bool stash = h1 != nullptr;
+  if (stash && (act_dt != MOE_BF16 || w_dt != MOE_BF16 || !two || gather)) return MOE_ERR_INVALID_ARG;
+  if (stash && (kind == MOE_FFN_SWIGLU) != (h3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!stash && h3) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_rows, offsets, w1, w3, w2, s1, s3, s2, b1, b2, y_rows, h1, h3};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return MOE_ERR_INVALID_ARG;
   const size_t need = moe_ffn_workspace_size(kind, act_dt, max_rows, E, d, d_ff, d_out);
@@ -345,7 +370,13 @@ int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode
                    : kind == MOE_FFN_RELU ? EPI_RELU
                    : kind == MOE_FFN_GELU ? EPI_GELU
                                           : EPI_PLAIN;
-  st = launch_grouped_gemm(epi1, fp8, p1, max_rows, mtm, stream);
+  if (stash) {
+    p1.pre1 = h1;
+    p1.pre3 = h3;
+    st = launch_grouped_gemm_stash(epi1, p1, mtm, stream);
+  } else {
+    st = launch_grouped_gemm(epi1, fp8, p1, max_rows, mtm, stream);
+  }
   if (st != MOE_OK || !two) return st;
 
   GemmParams p2{};

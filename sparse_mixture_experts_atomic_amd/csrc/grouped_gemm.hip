@@ -790,7 +790,8 @@ template <int EPI, int BK, bool FP8, int XM = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr bool PRE = XM == 1 || XM == 2;
   constexpr bool WG = XM == 2;
-  constexpr int BWE = XM >= 3 ? XM - 2 : 0;   // 3, 4, 5: the SwiGLU, ReLU, GELU backward epilogue
+  constexpr int BWE = XM >= 3 && XM <= 5 ? XM - 2 : 0;   // 3, 4, 5: the SwiGLU, ReLU, GELU backward epilogue
+  constexpr bool STASH = XM == 6;             // the activation output and the fp32 pre-activations
   constexpr int BM = 256;
   constexpr int R = 2;                  // split parts are whole stage pairs
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
@@ -1226,8 +1227,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
     const int col0 = EPI == EPI_SWIGLU ? nt * HC + wn * 64 : nt * BN + wn * 128;
     // (the fp32 staging of PRE takes the 128 + 8 bf16 pitch whatever OC is)
-    wave_epilogue<EPI, FM, false, PRE, BWE>(acc, reinterpret_cast<uint16_t*>(ring) + wave * 128 * ((PRE ? 128 : OC) + 8),
-                                            p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
+    uint16_t* st = reinterpret_cast<uint16_t*>(ring) + wave * 128 * ((PRE || STASH ? 128 : OC) + 8);
+    if constexpr (STASH) {
+      // first the pre-activations (fp32), then the activation (bf16), each
+      // staged through the wavefront's block (the first ends with a fence)
+      wave_epilogue<EPI, FM, false, true>(acc, st, p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
+      wave_epilogue<EPI, FM, false, false>(acc, st, p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
+    } else {
+      wave_epilogue<EPI, FM, false, PRE, BWE>(acc, st, p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
+    }
   };
   if constexpr (!FP8) {
     if (unit < 0 && tc.rows_valid <= 64) {
@@ -1561,6 +1569,19 @@ int launch_grouped_gemm_pre(int epi, const GemmParams& p, int m_tiles_max, hipSt
   q.split_max = 1;
   if (epi == EPI_SWIGLU) return launch_dma_pre<EPI_SWIGLU, kDmaBK, false, 1>(q, m_tiles_max, stream);
   if (epi == EPI_PLAIN) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 1>(q, m_tiles_max, stream);
+  return MOE_ERR_UNSUPPORTED;
+}
+
+int launch_grouped_gemm_stash(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  const bool dma_ok = p.K % kDmaKMult == 0 && p.N % 8 == 0 && static_cast<size_t>(p.N) * p.K * 2 < (size_t(1) << 31) &&
+                      static_cast<size_t>(kGemmBM) * p.K * 2 < (size_t(1) << 31) && !p.gather && !p.s1 && p.C &&
+                      p.pre1 && (epi != EPI_SWIGLU || p.pre3);
+  if (!dma_ok) return MOE_ERR_UNSUPPORTED;
+  GemmParams q = p;
+  q.split_max = 1;
+  if (epi == EPI_SWIGLU) return launch_dma_pre<EPI_SWIGLU, kDmaBK, false, 6>(q, m_tiles_max, stream);
+  if (epi == EPI_RELU) return launch_dma_pre<EPI_RELU, kDmaBK, false, 6>(q, m_tiles_max, stream);
+  if (epi == EPI_GELU) return launch_dma_pre<EPI_GELU, kDmaBK, false, 6>(q, m_tiles_max, stream);
   return MOE_ERR_UNSUPPORTED;
 }
 

@@ -144,7 +144,7 @@ struct GemmParams {
   int n_cu;                  // compute units (one block of the DMA kernel each)
   int split_max;             // most K parts of a split tile (1: no split)
   const float* row_scale;    // fp8 activations: scale of each source row of A (or null)
-  float* pre1;               // pre-activation outputs (fp32 [*, N]; launch_grouped_gemm_pre only):
+  float* pre1;               // pre-activation outputs (fp32 [*, N]; launch_grouped_gemm_pre and _stash):
   float* pre3;               //   gate (+ bias) and, for SwiGLU, up
   // launch_grouped_gemm_wgrad only: segment e takes K columns [128 kseg[e],
   // 128 kseg[e+1]) of A (rows from 0, pitch lda) and of B (shared by all
@@ -188,6 +188,11 @@ int launch_grouped_gemm_wgrad(const GemmParams& p, int m_tiles_max, hipStream_t 
 // da = dY W2 with the activation's backward in the epilogue (bwd_epi: one of
 // BWD_EPI_SWIGLU, _RELU, _GELU) on the LDS-DMA kernel, B = W2 transposed to
 // [E, d_ff, d_out]; MOE_ERR_UNSUPPORTED for shapes it does not take.
+// The first product of a training forward: the activation to C as
+// launch_grouped_gemm writes it, and the fp32 pre-activations (+ bias) to
+// pre1 (SwiGLU: gate to pre1, up to pre3), [rows, N] each; MOE_ERR_UNSUPPORTED
+// for shapes the LDS-DMA kernel does not take.
+int launch_grouped_gemm_stash(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
 int launch_grouped_gemm_actbwd(int bwd_epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
 
 // Per-row e4m3 quantisation (quant.hip): scale[r] = max |x[r, :]| / 448 (1

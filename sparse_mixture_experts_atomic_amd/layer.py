@@ -59,6 +59,10 @@ class MoELayer:
         self.loss = torch.empty((1,), **f32)
         # training: the router keeps its fp32 logits for the backward pass
         self.logits = None
+        # training with the expert FFNs' pre-activations kept: buffers, and
+        # whether the last forward filled them (routed, shared)
+        self._keep = None
+        self._kept = None
         act = L.F32 if act_dtype == torch.float32 else L.BF16
         self.ws_router = self._ws(L.router_workspace_size(T, d, E, act), dev)
         self._router_ws = (self.ws_router, False)   # the workspace aux() reads (noisy or not)
@@ -121,6 +125,8 @@ class MoELayer:
 
     def experts(self, x_perm=None, offsets=None):
         w = self.w
+        if self._keep is not None:
+            self._kept["routed"] = False
         if self.fp8_act:
             L.expert_ffn_fp8(self.kind, self.xq, self.xs, self.perm_token, L.ROWS_PACKED, self.T * self.k,
                              self.offsets if offsets is None else offsets, self.E, self.d, self.d_ff, self.d_out,
@@ -133,20 +139,40 @@ class MoELayer:
                                   w["w1"], w.get("w3"), w.get("w2"), w.get("s1"), w.get("s3"), w.get("s2"),
                                   w.get("b1"), w.get("b2"), self.y_rows, self.ws_ffn)
             return
-        L.expert_ffn_grouped(self.kind, self.x_perm if x_perm is None else x_perm, self.T * self.k, L.ROWS_PACKED,
-                             self.offsets if offsets is None else offsets, self.E, self.d, self.d_ff, self.d_out,
-                             w["w1"], w.get("w3"), w.get("w2"), w.get("s1"), w.get("s3"), w.get("s2"),
+        xr = self.x_perm if x_perm is None else x_perm
+        offs = self.offsets if offsets is None else offsets
+        if self._keep is not None:
+            # training: the first product's fp32 pre-activations are kept for
+            # the backward pass where the library takes the shape
+            h1, h3 = self._keep["routed"]
+            self._kept["routed"] = L.expert_ffn_grouped_train(
+                self.kind, xr, self.T * self.k, L.ROWS_PACKED, offs, self.E, self.d, self.d_ff, self.d_out, w["w1"],
+                w.get("w3"), w.get("w2"), w.get("b1"), w.get("b2"), self.y_rows, h1, h3, self.ws_ffn)
+            if self._kept["routed"]:
+                return
+        L.expert_ffn_grouped(self.kind, xr, self.T * self.k, L.ROWS_PACKED, offs, self.E, self.d, self.d_ff,
+                             self.d_out, w["w1"], w.get("w3"), w.get("w2"), w.get("s1"), w.get("s3"), w.get("s2"),
                              w.get("b1"), w.get("b2"), self.y_rows, self.ws_ffn)
 
     def shared(self, x):
         if not self.n_shared:
             return
         w = self.w
+        if self._keep is not None:
+            self._kept["shared"] = False
         if self.fp8_act:
             L.expert_ffn_fp8(self.kind, self.xq, self.xs, None, L.ROWS_SHARED, self.n_shared * self.T, self.sh_offsets,
                              self.n_shared, self.d, self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"), w.get("sh_w2"),
                              w.get("sh_s1"), w.get("sh_s3"), w.get("sh_s2"), self.shared_y, self.ws_sh_f8)
             return
+        if self._keep is not None:
+            h1, h3 = self._keep["shared"]
+            self._kept["shared"] = L.expert_ffn_grouped_train(
+                self.kind, x, self.n_shared * self.T, L.ROWS_SHARED, self.sh_offsets, self.n_shared, self.d,
+                self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"), w.get("sh_w2"), w.get("sh_b1"), w.get("sh_b2"),
+                self.shared_y, h1, h3, self.ws_sh)
+            if self._kept["shared"]:
+                return
         L.expert_ffn_grouped(self.kind, x, self.n_shared * self.T, L.ROWS_SHARED, self.sh_offsets, self.n_shared,
                              self.d, self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"), w.get("sh_w2"),
                              w.get("sh_s1"), w.get("sh_s3"), w.get("sh_s2"), w.get("sh_b1"), w.get("sh_b2"),
@@ -166,9 +192,11 @@ class MoELayer:
                                self.loss, self.prob_colsum)
 
     # ---------------------------------------------------------------- training
-    def enable_backward(self):
+    def enable_backward(self, keep_pre=True):
         """Allocate what the backward pass needs (the forward then also keeps
-        the router logits); gradients land in self.grad after backward()."""
+        the router logits and, with keep_pre, the expert FFNs' fp32
+        pre-activations, so that the backward does not recompute the first
+        product); gradients land in self.grad after backward()."""
         if self.logits is not None:
             return
         dev = self.topk_idx.device
@@ -182,7 +210,20 @@ class MoELayer:
         self.dx_rows = torch.empty((max(A, 1), d), dtype=act, device=dev)
         self.dx = torch.empty((T, d), dtype=act, device=dev)
         self.ws_rbwd = self._ws(L.router_backward_workspace_size(T, d, E), dev)
-        self.ws_fbwd = self._ws(L.ffn_backward_workspace_size(self.kind, A, E, d, self.d_ff, self.d_out), dev)
+        keep = (keep_pre and self.kind != L.FFN_LINEAR and act == torch.bfloat16 and not self.fp8_act
+                and self.w["w1"].dtype == torch.bfloat16)
+        if keep:
+            def pre(rows):
+                h1 = torch.empty((max(rows, 1), self.d_ff), **f32)
+                return h1, (torch.empty_like(h1) if self.kind == L.FFN_SWIGLU else None)
+            self._keep = {"routed": pre(A), "shared": pre(self.n_shared * T) if self.n_shared else None}
+            self._kept = {"routed": False, "shared": False}
+            wsz = L.ffn_backward_kept_workspace_size
+        else:
+            wsz = L.ffn_backward_workspace_size
+        # the recomputing backward's larger workspace is made only if a
+        # forward could not keep the pre-activations
+        self.ws_fbwd = self._ws(wsz(self.kind, A, E, d, self.d_ff, self.d_out), dev)
         g = {"w_g": torch.empty((E, d), **f32), "b_g": torch.empty((E,), **f32)}
         for pre in ("", "sh_"):
             for n in ("w1", "w3", "w2", "b1", "b2"):
@@ -192,27 +233,54 @@ class MoELayer:
         self.grad = g
         if self.n_shared:
             self.dx_shared = torch.empty((self.n_shared, T, d), dtype=act, device=dev)
-            self.ws_sbwd = self._ws(L.ffn_backward_workspace_size(self.kind, self.n_shared * T, self.n_shared, d,
-                                                                  self.d_ff, self.d_out), dev)
+            self.ws_sbwd = self._ws(wsz(self.kind, self.n_shared * T, self.n_shared, d, self.d_ff, self.d_out), dev)
 
     def backward_combine(self, dy):
         L.combine_backward(dy, self.y_rows, self.dest_pos, self.topk_gate, self.dy_rows, self.dgate)
 
+    def _bwd_ws(self, name, rows, E):
+        """The workspace of the recomputing FFN backward (made on first use
+        when the layer was set up to keep the pre-activations)."""
+        ws = getattr(self, name)
+        need = L.ffn_backward_workspace_size(self.kind, rows, E, self.d, self.d_ff, self.d_out)
+        if ws.numel() < need:
+            ws = self._ws(need, ws.device)
+            setattr(self, name, ws)
+        return ws
+
     def backward_experts(self):
         w, g = self.w, self.grad
-        L.expert_ffn_grouped_backward(self.kind, self.x_perm, self.T * self.k, L.ROWS_PACKED, self.offsets, self.E,
+        A = self.T * self.k
+        if self._keep is not None and self._kept["routed"]:
+            h1, h3 = self._keep["routed"]
+            L.expert_ffn_grouped_backward_kept(self.kind, self.x_perm, A, L.ROWS_PACKED, self.offsets, self.E, self.d,
+                                               self.d_ff, self.d_out, w["w1"], w.get("w3"), w.get("w2"), w.get("b1"),
+                                               w.get("b2"), h1, h3, self.dy_rows, self.dx_rows, g["w1"], g.get("w3"),
+                                               g.get("w2"), g.get("b1"), g.get("b2"), self.ws_fbwd)
+            return
+        L.expert_ffn_grouped_backward(self.kind, self.x_perm, A, L.ROWS_PACKED, self.offsets, self.E,
                                       self.d, self.d_ff, self.d_out, w["w1"], w.get("w3"), w.get("w2"), w.get("b1"),
                                       w.get("b2"), self.dy_rows, self.dx_rows, g["w1"], g.get("w3"), g.get("w2"),
-                                      g.get("b1"), g.get("b2"), self.ws_fbwd)
+                                      g.get("b1"), g.get("b2"), self._bwd_ws("ws_fbwd", A, self.E))
 
     def backward_shared(self, x, dy):
         if not self.n_shared:
             return
         w, g = self.w, self.grad
-        L.expert_ffn_grouped_backward(self.kind, x, self.n_shared * self.T, L.ROWS_SHARED, self.sh_offsets,
+        R = self.n_shared * self.T
+        if self._keep is not None and self._kept["shared"]:
+            h1, h3 = self._keep["shared"]
+            L.expert_ffn_grouped_backward_kept(self.kind, x, R, L.ROWS_SHARED, self.sh_offsets, self.n_shared, self.d,
+                                               self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"), w.get("sh_w2"),
+                                               w.get("sh_b1"), w.get("sh_b2"), h1, h3, dy, self.dx_shared,
+                                               g["sh_w1"], g.get("sh_w3"), g.get("sh_w2"), g.get("sh_b1"),
+                                               g.get("sh_b2"), self.ws_sbwd)
+            return
+        L.expert_ffn_grouped_backward(self.kind, x, R, L.ROWS_SHARED, self.sh_offsets,
                                       self.n_shared, self.d, self.d_ff, self.d_out, w["sh_w1"], w.get("sh_w3"),
                                       w.get("sh_w2"), w.get("sh_b1"), w.get("sh_b2"), dy, self.dx_shared, g["sh_w1"],
-                                      g.get("sh_w3"), g.get("sh_w2"), g.get("sh_b1"), g.get("sh_b2"), self.ws_sbwd)
+                                      g.get("sh_w3"), g.get("sh_w2"), g.get("sh_b1"), g.get("sh_b2"),
+                                      self._bwd_ws("ws_sbwd", R, self.n_shared))
 
     def backward_router(self, x, daux=1.0):
         L.router_backward(x, self.logits, self.topk_idx, self.topk_gate, self.dgate, self.counts_routed, self.gate,

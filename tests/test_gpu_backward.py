@@ -76,13 +76,13 @@ def _sum_bound_err(got, ref, absterms):
 
 
 class BwdRun:
-    def __init__(self, cfg, seed=77, residual=False):
+    def __init__(self, cfg, seed=77, residual=False, keep_pre=True, arr=None):
         self.cfg = cfg
-        self.arr = W.generate(cfg)
+        self.arr = W.generate(cfg) if arr is None else arr
         self.C = L.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
         assert self.C == O.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.cap_round)
         self.layer = MoELayer(**layer_kwargs(cfg, self.arr, self.C, "cuda"))
-        self.layer.enable_backward()
+        self.layer.enable_backward(keep_pre=keep_pre)
         self.x = to_tensor(self.arr["x"], "cuda")
         self.x64 = O.to_f64(self.arr["x"], cfg.act_dtype)
         rng = np.random.default_rng(seed)
@@ -277,3 +277,62 @@ def test_backward_mixtral_full():
     r.check_experts(experts=[0, 3, 7])
     r.check_router()
     r.check_permute()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["mixtral_s", "deepseek_s", "switch_drop_s", "gelu_bias", "cap_hit_k4",
+                                  "empty_experts", "mixtral_full"])
+def test_kept_pre_activations_match_recompute(name):
+    """Training forward keeping the first product's fp32 pre-activations
+    (moe_expert_ffn_grouped_train) and the backward reading them
+    (moe_expert_ffn_grouped_backward_kept).  The backward's gradients are
+    the recomputing backward's, bit for bit, on the same rows (the kept and
+    the recomputed pre-activations are the same GEMM, unsplit).  The
+    forward's output: bit for bit where the plain forward does not split
+    tail tiles over K (the full Mixtral shape), else within the bf16
+    tolerance (the split sums in another order).  Shapes the kept path does
+    not take (d = 64) fall back to the recomputing path."""
+    cfg = W.MIXTRAL if name == "mixtral_full" else CASES[name]
+    say(f"[case] kept pre-activations {name}: T={cfg.T} d={cfg.d} E={cfg.E} {cfg.ffn}")
+    r = BwdRun(cfg, residual=name == "deepseek_s")
+    r.run()
+    ly = r.layer
+    flags = dict(ly._kept)
+    expect = cfg.d % 128 == 0
+    assert flags["routed"] == expect, flags
+    if cfg.n_shared:
+        assert flags["shared"] == expect, flags
+    w = ly.w
+    A = cfg.T * cfg.k
+    # the plain forward of the routed experts on the same rows
+    y_plain = torch.empty_like(ly.y_rows)
+    L.expert_ffn_grouped(ly.kind, ly.x_perm, A, L.ROWS_PACKED, ly.offsets, cfg.E, cfg.d, cfg.d_ff, cfg.d_out,
+                         w["w1"], w.get("w3"), w.get("w2"), None, None, None, w.get("b1"), w.get("b2"), y_plain,
+                         ly.ws_ffn)
+    # the recomputing backward on the same rows and output gradients
+    ws = torch.empty(L.ffn_backward_workspace_size(ly.kind, A, cfg.E, cfg.d, cfg.d_ff, cfg.d_out),
+                     dtype=torch.uint8, device="cuda")
+    names = [n for n in ("w1", "w3", "w2", "b1", "b2") if n in ly.grad]
+    g = {n: torch.full_like(ly.grad[n], -7.0) for n in names}
+    dx_rows = torch.full_like(ly.dx_rows, -7.0)
+    L.expert_ffn_grouped_backward(ly.kind, ly.x_perm, A, L.ROWS_PACKED, ly.offsets, cfg.E, cfg.d, cfg.d_ff,
+                                  cfg.d_out, w["w1"], w.get("w3"), w.get("w2"), w.get("b1"), w.get("b2"), ly.dy_rows,
+                                  dx_rows, g["w1"], g.get("w3"), g.get("w2"), g.get("b1"), g.get("b2"), ws)
+    torch.cuda.synchronize()
+    n_rows = r.A
+    for n in names:
+        assert torch.equal(_bits(ly.grad[n]), _bits(g[n])), n
+    assert torch.equal(_bits(ly.dx_rows[:n_rows]), _bits(dx_rows[:n_rows])), "dx_rows"
+    got, ref = ly.y_rows[:n_rows], y_plain[:n_rows]
+    if name == "mixtral_full":
+        assert torch.equal(_bits(got), _bits(ref)), "y_rows"
+    else:
+        err = rownorm_err(act_to_f64(got), act_to_f64(ref))
+        assert err <= BF16_TOL, err
+    differ = int((_bits(got) != _bits(ref)).sum())
+    say(f"  kept {flags}: gradients and dx_rows bit-identical to the recomputing backward; "
+        f"forward y_rows: {differ} of {got.numel()} elements differ from the plain forward")
