@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the training-step (forward + backward) leg")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-activation leg")
+    ap.add_argument("--no-gathered", action="store_true",
+                    help="skip the gathered-FFN leg (its GEMMs share kernel names with the layer's own)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration) and exit")
     args = ap.parse_args()
@@ -264,33 +266,35 @@ def main():
     # order for the profiles): whole steps of the same layer with the routed FFN
     # reading x through the dispatch permutation (no packed copy of x; the
     # same weight tensors, bit-identical output)
-    glayer = MoELayer(**lkw, gather_rows=True)
-    for _ in range(args.warmup):
+    gathered = None
+    glayer = None if args.no_gathered else MoELayer(**lkw, gather_rows=True)
+    for _ in range(args.warmup if glayer is not None else 0):
         glayer.forward(x)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        glayer.forward(x)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step_gather = start.elapsed_time(stop) / args.steps
-    gd, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gf = torch.cuda.Event(enable_timing=True)
-    g_disp, g_exp = [], []
-    for _ in range(args.steps):
-        glayer.router(x)
-        gd.record()
-        glayer.dispatch(x)
-        ge.record()
-        glayer.experts()
-        gf.record()
+    if glayer is not None:
         torch.cuda.synchronize()
-        g_disp.append(gd.elapsed_time(ge))
-        g_exp.append(ge.elapsed_time(gf))
-    gathered = {"ms_per_step": ms_step_gather, "value": cfg.T / (ms_step_gather * 1e-3),
-                "dispatch_ms": float(np.median(g_disp)), "experts_ms": float(np.median(g_exp)),
-                "note": "routed FFN reads x through perm_token (moe_expert_ffn_gathered); dispatch copies no rows"}
-    del glayer
+        start.record()
+        for _ in range(args.steps):
+            glayer.forward(x)
+        stop.record()
+        torch.cuda.synchronize()
+        ms_step_gather = start.elapsed_time(stop) / args.steps
+        gd, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gf = torch.cuda.Event(enable_timing=True)
+        g_disp, g_exp = [], []
+        for _ in range(args.steps):
+            glayer.router(x)
+            gd.record()
+            glayer.dispatch(x)
+            ge.record()
+            glayer.experts()
+            gf.record()
+            torch.cuda.synchronize()
+            g_disp.append(gd.elapsed_time(ge))
+            g_exp.append(ge.elapsed_time(gf))
+        gathered = {"ms_per_step": ms_step_gather, "value": cfg.T / (ms_step_gather * 1e-3),
+                    "dispatch_ms": float(np.median(g_disp)), "experts_ms": float(np.median(g_exp)),
+                    "note": "routed FFN reads x through perm_token (moe_expert_ffn_gathered); dispatch copies no rows"}
+        del glayer
 
     # timed region 5 (last): training steps, forward + backward of a layer
     # instance that keeps the router logits; dy is a fixed seeded draw.  The
