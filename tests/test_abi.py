@@ -215,3 +215,66 @@ def test_aux_from_router_validation_before_launch():
     need_n = L.router_noisy_workspace_size(4096, 4096, 8, L.BF16)
     assert need_n > need
     assert call(noisy=1, wsb=need) == L.ERR_WORKSPACE
+
+
+def test_noisy_router_philox_and_draws_validation_before_launch():
+    lib = L.lib()
+    fake = 1 << 20
+    f = lib.moe_router_topk_noisy_philox
+
+    def call(x=fake, dt=L.BF16, wg=fake, wn=fake, bn=None, eps=1e-2, T=8, d=16, E=4, k=2, mode=0, ws=fake,
+             wsb=1 << 20):
+        return f(x, dt, wg, None, wn, bn, 7, 3, eps, T, d, E, k, mode, fake, fake, None, None, ws, wsb, None)
+
+    assert call(k=5) == L.ERR_INVALID_ARG
+    assert call(wn=None) == L.ERR_INVALID_ARG
+    assert call(wn=fake + 4) == L.ERR_INVALID_ARG
+    assert call(bn=fake + 4) == L.ERR_INVALID_ARG
+    assert call(eps=float("nan")) == L.ERR_INVALID_ARG
+    assert call(eps=-1.0) == L.ERR_INVALID_ARG
+    assert call(d=12) == L.ERR_INVALID_ARG
+    assert call(ws=None, wsb=0) == L.ERR_WORKSPACE
+    assert call(wsb=L.router_noisy_workspace_size(8, 16, 4, L.BF16) - 16) == L.ERR_WORKSPACE
+    assert call(E=512) == L.ERR_UNSUPPORTED
+    g = lib.moe_gate_noise_philox
+    assert g(1, 2, (1 << 62) + 1, fake, None) == L.ERR_INVALID_ARG
+    assert g(1, 2, 5, None, None) == L.ERR_INVALID_ARG
+    assert g(1, 2, 0, None, None) == L.OK            # nothing to draw, nothing launched
+
+
+def test_training_ffn_validation_before_launch():
+    lib = L.lib()
+    f = 1 << 20
+    ws = lib.moe_ffn_workspace_size(L.FFN_SWIGLU, L.BF16, 64, 4, 128, 128, 64)
+
+    def fwd(kind=L.FFN_SWIGLU, act=L.BF16, w_dt=L.BF16, w3=f, h1=f, h3=f, b1=None, rows=64, wsb=ws):
+        return lib.moe_expert_ffn_grouped_train(kind, f, act, rows, 0, f, 4, 128, 128, 64, f, w3, f, w_dt, b1, None,
+                                                f, h1, h3, f, wsb, None)
+    assert fwd(kind=L.FFN_LINEAR) == L.ERR_INVALID_ARG        # nothing to keep
+    assert fwd(h1=None) == L.ERR_INVALID_ARG
+    assert fwd(h3=None) == L.ERR_INVALID_ARG                  # SwiGLU keeps both products
+    assert fwd(kind=L.FFN_RELU, w3=None) == L.ERR_INVALID_ARG  # ReLU keeps one (h3 given)
+    assert fwd(act=L.F32, w_dt=L.F32) == L.ERR_INVALID_ARG    # bf16 only
+    assert fwd(h1=f + 4) == L.ERR_INVALID_ARG
+    assert fwd(wsb=16) == L.ERR_WORKSPACE
+    assert fwd(rows=0, h1=None, h3=None) == L.OK              # no rows: nothing kept, nothing launched
+
+    full = lib.moe_ffn_backward_workspace_size(L.FFN_SWIGLU, 64, 4, 128, 128, 64)
+    kept = lib.moe_ffn_backward_kept_workspace_size(L.FFN_SWIGLU, 64, 4, 128, 128, 64)
+    assert full - kept >= 2 * 64 * 128 * 4                     # the two recomputed fp32 buffers
+    assert (lib.moe_ffn_backward_kept_workspace_size(L.FFN_LINEAR, 64, 4, 128, 0, 64)
+            == lib.moe_ffn_backward_workspace_size(L.FFN_LINEAR, 64, 4, 128, 0, 64))
+
+    def bwd(kind=L.FFN_SWIGLU, w3=f, h1=f, h3=f, wsb=kept, dw3=f):
+        return lib.moe_expert_ffn_grouped_backward_kept(kind, f, L.BF16, 64, 0, f, 4, 128, 128, 64, f, w3, f, L.BF16,
+                                                        None, None, h1, h3, f, f, f, dw3, f, None, None, f, wsb, None)
+    assert bwd(kind=L.FFN_LINEAR) == L.ERR_INVALID_ARG
+    assert bwd(h1=None) == L.ERR_INVALID_ARG
+    assert bwd(h3=None) == L.ERR_INVALID_ARG
+    assert bwd(kind=L.FFN_RELU, w3=None, dw3=None) == L.ERR_INVALID_ARG   # h3 given without SwiGLU
+    assert bwd(h3=f + 4) == L.ERR_INVALID_ARG
+    assert bwd(wsb=kept - 16) == L.ERR_WORKSPACE
+    # the recomputing backward needs the larger workspace
+    rec = lib.moe_expert_ffn_grouped_backward(L.FFN_SWIGLU, f, L.BF16, 64, 0, f, 4, 128, 128, 64, f, f, f, L.BF16,
+                                              None, None, f, f, f, f, f, None, None, f, kept, None)
+    assert rec == L.ERR_WORKSPACE
