@@ -71,11 +71,34 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
   }
 }
 
-// Standard normal draw i of the stream (seed, offset): counter block i / 4
-// (counter words: block low, block high, offset low, offset high; key: seed
-// low, seed high), the pair of output words (i mod 4) / 2 as u1, u2 =
-// (word + 1/2) 2^-32, and the Box-Muller value sqrt(-2 ln u1) times cos
-// (even i) or sin (odd i) of 2 pi u2.  In fp64, rounded once to fp32.
+// Box-Muller pair from two output words: u1, u2 = (word + 1/2) 2^-32 and
+// sqrt(-2 ln u1) times cos (even draw) and sin (odd draw) of 2 pi u2, in
+// fp64, each rounded once to fp32
+__device__ __forceinline__ void box_muller_pair(uint32_t wa, uint32_t wb, float& even, float& odd) {
+  const double u1 = (static_cast<double>(wa) + 0.5) * 0x1p-32;
+  const double u2 = (static_cast<double>(wb) + 0.5) * 0x1p-32;
+  const double r = sqrt(-2.0 * log(u1));
+  double sn, cs;
+  sincospi(2.0 * u2, &sn, &cs);
+  even = static_cast<float>(r * cs);
+  odd = static_cast<float>(r * sn);
+}
+
+// The four draws 4 j .. 4 j + 3 of the stream (seed, offset): counter block
+// j (counter words: j low, j high, offset low, offset high; key: seed low,
+// seed high); draws 4 j, 4 j + 1 from words 0, 1 and 4 j + 2, 4 j + 3 from
+// words 2, 3.
+__device__ __forceinline__ void philox_normal4(unsigned long long seed, unsigned long long offset,
+                                               unsigned long long j, float (&v)[4]) {
+  uint32_t c0 = static_cast<uint32_t>(j), c1 = static_cast<uint32_t>(j >> 32);
+  uint32_t c2 = static_cast<uint32_t>(offset), c3 = static_cast<uint32_t>(offset >> 32);
+  philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  box_muller_pair(c0, c1, v[0], v[1]);
+  box_muller_pair(c2, c3, v[2], v[3]);
+}
+
+// Standard normal draw i of the stream: draw i mod 4 of block i / 4 (one
+// Box-Muller pair is computed)
 __device__ __forceinline__ float philox_normal(unsigned long long seed, unsigned long long offset,
                                                unsigned long long i) {
   const unsigned long long j = i >> 2;
@@ -83,12 +106,9 @@ __device__ __forceinline__ float philox_normal(unsigned long long seed, unsigned
   uint32_t c2 = static_cast<uint32_t>(offset), c3 = static_cast<uint32_t>(offset >> 32);
   philox4x32_10(c0, c1, c2, c3, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
   const bool second = (i >> 1) & 1;
-  const double u1 = (static_cast<double>(second ? c2 : c0) + 0.5) * 0x1p-32;
-  const double u2 = (static_cast<double>(second ? c3 : c1) + 0.5) * 0x1p-32;
-  const double r = sqrt(-2.0 * log(u1));
-  double sn, cs;
-  sincospi(2.0 * u2, &sn, &cs);
-  return static_cast<float>((i & 1) ? r * sn : r * cs);
+  float even, odd;
+  box_muller_pair(second ? c2 : c0, second ? c3 : c1, even, odd);
+  return (i & 1) ? odd : even;
 }
 
 // the noisy gate's draw for flat index t E + e
@@ -832,6 +852,7 @@ __global__ __launch_bounds__(kFnThreads) void router_finish_kernel(RouterArgs a,
   // launch_finish picks PER with PER * kFnThreads >= kFnTok * E
   __shared__ float lg[kFnTok * kRtMaxE];
   __shared__ float wcol[kFnWaves * kRtMaxE];
+  __shared__ float drs[NOISY ? kFnTok * kRtMaxE : 1];   // the block's draws when drawn here
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -864,8 +885,22 @@ __global__ __launch_bounds__(kFnThreads) void router_finish_kernel(RouterArgs a,
 #pragma unroll
       for (int u = 0; u < PER; ++u) dr[u] = a.noise[static_cast<size_t>(t0) * a.E + jj[u]];
     } else {
+      // the block's draws [t0 E, t0 E + n_ent), a counter block (four
+      // draws, two Box-Muller pairs) per thread, through LDS
+      const unsigned long long base = static_cast<unsigned long long>(t0) * a.E;
+      const unsigned long long jb = base >> 2, je = (base + n_ent + 3) >> 2;
+      for (unsigned long long j = jb + tid; j < je; j += kFnThreads) {
+        float v[4];
+        philox_normal4(a.seed, a.offset, j, v);
 #pragma unroll
-      for (int u = 0; u < PER; ++u) dr[u] = philox_normal(a.seed, a.offset, static_cast<size_t>(t0) * a.E + jj[u]);
+        for (int q = 0; q < 4; ++q) {
+          const unsigned long long i = 4 * j + q;
+          if (i >= base && i < base + n_ent) drs[i - base] = v[q];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) dr[u] = drs[jj[u]];
     }
     if (a.b_n) {
 #pragma unroll
@@ -1222,13 +1257,19 @@ int scratch_on_current_device(void** out) {
 namespace moe {
 namespace {
 
-// out[i] = standard normal draw start + i of the stream (seed, offset), a
-// grid-stride loop
+// out[i] = standard normal draw i of the stream (seed, offset): a
+// grid-stride loop over counter blocks, four draws each
 __global__ __launch_bounds__(256) void gate_noise_kernel(unsigned long long seed, unsigned long long offset, size_t n,
                                                          float* __restrict__ out) {
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    out[i] = philox_normal(seed, offset, i);
+  const size_t nb = (n + 3) / 4;
+  for (size_t j = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < nb;
+       j += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    float v[4];
+    philox_normal4(seed, offset, j, v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (4 * j + q < n) out[4 * j + q] = v[q];
+  }
 }
 
 }  // namespace
@@ -1242,7 +1283,7 @@ int moe_gate_noise_philox(uint64_t seed, uint64_t offset, size_t n, float* out, 
   if (n > (size_t(1) << 62)) return MOE_ERR_INVALID_ARG;
   if (n == 0) return MOE_OK;
   if (!out) return MOE_ERR_INVALID_ARG;
-  const size_t blocks = std::min<size_t>((n + 255) / 256, 8 * 256);
+  const size_t blocks = std::min<size_t>(((n + 3) / 4 + 255) / 256, 8 * 256);
   hipLaunchKernelGGL(gate_noise_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                      static_cast<unsigned long long>(seed), static_cast<unsigned long long>(offset), n, out);
   return check_launch();
