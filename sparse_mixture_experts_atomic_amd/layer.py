@@ -199,6 +199,10 @@ class MoELayer:
         product); gradients land in self.grad after backward()."""
         if self.logits is not None:
             return
+        if self.gather_rows:
+            # the backward reads the packed rows the dispatch copied
+            raise ValueError("the backward pass needs the packed rows: build the layer with gather_rows=False "
+                             "and bf16 (not e4m3) expert weights")
         dev = self.topk_idx.device
         T, d, E, k, A = self.T, self.d, self.E, self.k, self.T * self.k
         f32 = dict(dtype=torch.float32, device=dev)
