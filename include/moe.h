@@ -14,9 +14,12 @@
  *   (routed experts, then shared experts) -> moe_combine -> moe_aux_loss.
  * Variants: moe_router_topk_noisy or moe_router_topk_noisy_philox in place
  * of moe_router_topk (noisy gating in training mode, with the caller's
- * normal draws or with draws from a counter-based generator), and moe_dispatch_permute without the row copy followed
- * by moe_expert_ffn_gathered in place of moe_expert_ffn_grouped for the
- * routed experts (the FFN reads x through the permutation).
+ * normal draws or with draws from a counter-based generator);
+ * moe_dispatch_permute without the row copy followed by
+ * moe_expert_ffn_gathered in place of moe_expert_ffn_grouped for the routed
+ * experts (the FFN reads x through the permutation); and, for training,
+ * moe_expert_ffn_grouped_train in place of moe_expert_ffn_grouped (the
+ * first product's pre-activations kept for the backward calls below).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE memory owned by the caller.  The library
