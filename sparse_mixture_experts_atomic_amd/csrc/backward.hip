@@ -574,7 +574,7 @@ __global__ void iota_kernel(int32_t* out, int E, int M) {
 // in each row) and activation a [max_rows, d_ff], the transposed first-layer
 // weights [E, d, Kt] and the forward GEMM's split-tail partial sums
 struct FfnBwdLayout {
-  size_t ts128, ts256, h1, h3, dh, a, wt, partial, kp, xt, dyt, at, dht, wofs_o, wofs_1, tsw_o, tsw_1, total;
+  size_t ts128, ts256, h1, h3, dh, a, wt, wt_bytes, partial, kp, xt, dyt, at, dht, wofs_o, wofs_1, tsw_o, tsw_1, total;
 };
 
 FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int d_out, bool stashed = false) {
@@ -595,10 +595,16 @@ FfnBwdLayout ffn_bwd_layout(int kind, int max_rows, int E, int d, int d_ff, int 
   L.h3 = kind == MOE_FFN_SWIGLU && !stashed ? take(ff * 4) : 0;
   L.dh = two ? take(static_cast<size_t>(max_rows) * kt * 2) : 0;
   L.a = two ? take(ff * 2) : 0;
-  // transposed weights: the first layer's [E, d, kt] for dX, before it the
-  // second layer's [E, d_ff, d_out] for da
-  L.wt = take(static_cast<size_t>(E) * std::max(static_cast<size_t>(d) * kt,
-                                                two ? static_cast<size_t>(d_ff) * static_cast<size_t>(d_out) : 0) * 2);
+  // transposed weights (the first layer's [E, d, kt] for dX, before it the
+  // second layer's [E, d_ff, d_out] for da), only for shapes whose products
+  // cannot read the weights as stored
+  const int n1 = two ? d_ff : d_out;
+  const bool tb = grouped_gemm_tb_shape_ok(static_cast<int>(kt), d, n1) &&
+                  (!two || grouped_gemm_tb_shape_ok(d_out, d_ff, d_out));
+  L.wt = tb ? 0
+            : take(static_cast<size_t>(E) * std::max(static_cast<size_t>(d) * kt,
+                                                    two ? static_cast<size_t>(d_ff) * static_cast<size_t>(d_out) : 0) * 2);
+  L.wt_bytes = tb ? 0 : 1;
   L.partial = take(static_cast<size_t>(current_cu_count()) * 256 * 256 * 4);
   // weight gradients: activations transposed per segment to [features, kp],
   // kp >= max_rows + 128 E bounds the sum of the segments padded to 128 rows
@@ -668,7 +674,7 @@ int ffn_backward_run(int kind, const void* x_rows, int act_dt, int max_rows, int
   uint16_t* dh1 = two ? reinterpret_cast<uint16_t*>(ws + lay.dh) : nullptr;
   uint16_t* dh3 = kind == MOE_FFN_SWIGLU ? dh1 + n1 : nullptr;
   uint16_t* act = two ? reinterpret_cast<uint16_t*>(ws + lay.a) : nullptr;
-  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + lay.wt);
+  uint16_t* wt = lay.wt_bytes ? reinterpret_cast<uint16_t*>(ws + lay.wt) : nullptr;   // (the fallback's)
   const int shared = row_mode == MOE_ROWS_SHARED ? 1 : 0;
   const uint16_t* X = static_cast<const uint16_t*>(x_rows);
   const uint16_t* DY = static_cast<const uint16_t*>(dy_rows);
@@ -736,15 +742,10 @@ int ffn_backward_run(int kind, const void* x_rows, int act_dt, int max_rows, int
   if (two) {
     // 2. da = dY W2 (K = d_out), with the activation's backward in the
     //    epilogue: dh1 (dh3) and the activation a.  On the forward's LDS-DMA
-    //    kernel over W2 transposed to [E, d_ff, d_out], else on the backward
+    //    kernel reading W2's rows as stored through transposing LDS reads;
+    //    else over W2 transposed to [E, d_ff, d_out]; else on the backward
     //    kernel
     const int epi = kind == MOE_FFN_SWIGLU ? BWD_EPI_SWIGLU : kind == MOE_FFN_RELU ? BWD_EPI_RELU : BWD_EPI_GELU;
-    const dim3 tg((d_ff + 63) / 64, (d_out + 63) / 64, E);
-    hipLaunchKernelGGL(transpose_w_kernel, tg, dim3(256), 0, stream, static_cast<const uint16_t*>(w2),
-                       static_cast<const uint16_t*>(nullptr),
-                       d_out, d_out, d_ff, wt);
-    st = check_launch();
-    if (st != MOE_OK) return st;
     GemmParams a{};
     a.A = DY;
     a.a_shared = shared;
@@ -762,7 +763,18 @@ int ffn_backward_run(int kind, const void* x_rows, int act_dt, int max_rows, int
     a.o2 = dh3;
     a.o3 = act;
     a.ldo = kt;
-    st = launch_grouped_gemm_actbwd(epi, a, mt256, stream);
+    a.B1 = w2;
+    a.tb_k1 = d_out;
+    st = launch_grouped_gemm_actbwd_tb(epi, a, mt256, stream);
+    if (st == MOE_ERR_UNSUPPORTED && wt) {
+      const dim3 tg((d_ff + 63) / 64, (d_out + 63) / 64, E);
+      hipLaunchKernelGGL(transpose_w_kernel, tg, dim3(256), 0, stream, static_cast<const uint16_t*>(w2),
+                         static_cast<const uint16_t*>(nullptr), d_out, d_out, d_ff, wt);
+      st = check_launch();
+      if (st != MOE_OK) return st;
+      a.B1 = wt;
+      st = launch_grouped_gemm_actbwd(epi, a, mt256, stream);
+    }
     if (st != MOE_ERR_UNSUPPORTED && st != MOE_OK) return st;
   }
   if (two && st == MOE_ERR_UNSUPPORTED) {
@@ -791,28 +803,36 @@ int ffn_backward_run(int kind, const void* x_rows, int act_dt, int max_rows, int
     if (st != MOE_OK) return st;
   }
   // 3. dX = dh W13 over K = kt (dh1 W1 + dh3 W3 for SwiGLU; linear: dY W1):
-  //    the first layer's weights transposed to [E, d, kt], then the forward's
-  //    grouped GEMM (both operands K-contiguous)
+  //    the forward's grouped GEMM reading the first layer's weights as stored
+  //    (K rows: W1's, then W3's) through transposing LDS reads; else over the
+  //    weights transposed to [E, d, kt] (both operands K-contiguous)
   {
-    const dim3 tg((d + 63) / 64, (kt + 63) / 64, E);
-    hipLaunchKernelGGL(transpose_w_kernel, tg, dim3(256), 0, stream, static_cast<const uint16_t*>(w1),
-                       static_cast<const uint16_t*>(w3), n1, kt, d, wt);
-    st = check_launch();
-    if (st != MOE_OK) return st;
     GemmParams g{};
     g.A = two ? dh1 : DY;
     g.a_shared = two ? 0 : shared;
     g.offsets = offsets;
     g.ts = ts256;
     g.E = E;
-    g.B1 = wt;
     g.C = static_cast<uint16_t*>(dx_rows);
     g.N = d;
     g.K = kt;
     g.partial = reinterpret_cast<float*>(ws + lay.partial);
     g.n_cu = current_cu_count();
     g.split_max = kGemmSplitMax;
-    st = launch_grouped_gemm(EPI_PLAIN, false, g, max_rows, mt256, stream);
+    g.B1 = w1;
+    g.B3 = w3;
+    g.tb_k1 = n1;
+    st = launch_grouped_gemm_tb(g, mt256, stream);
+    if (st == MOE_ERR_UNSUPPORTED && wt) {
+      const dim3 tg((d + 63) / 64, (kt + 63) / 64, E);
+      hipLaunchKernelGGL(transpose_w_kernel, tg, dim3(256), 0, stream, static_cast<const uint16_t*>(w1),
+                         static_cast<const uint16_t*>(w3), n1, kt, d, wt);
+      st = check_launch();
+      if (st != MOE_OK) return st;
+      g.B1 = wt;
+      g.B3 = nullptr;
+      st = launch_grouped_gemm(EPI_PLAIN, false, g, max_rows, mt256, stream);
+    }
     if (st != MOE_OK) return st;
   }
   // 4. weight gradients, K = the segment's rows: dW2 = dY^T a; dW1 = dh1^T X

@@ -439,6 +439,11 @@ __device__ __forceinline__ int dma_swz(int r, int c) {
   return r * CH + (c ^ ((r >> SH) & (CH - 1)));
 }
 
+// Chunk swizzle of a transposed-B image (64 K rows of 32 16-byte chunks):
+// the four K rows a half-wavefront's transposing read takes (k % 4 = 0..3)
+// land 64 bytes apart, so they cover 256 distinct bytes
+__device__ __forceinline__ int tb_swz(int k) { return 4 * (k & 3); }
+
 // Split tail.  With V tiles and n_cu CUs (one block each), the last round
 // holds rem = V % n_cu tiles and leaves the other CUs idle.  When that round
 // is at most half full, its tiles are split along K into S parts (S <= n_cu /
@@ -788,10 +793,17 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 // shared by the segments, fp32 output through the PRE epilogue
 template <int EPI, int BK, bool FP8, int XM = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParams p) {
-  constexpr bool PRE = XM == 1 || XM == 2;
-  constexpr bool WG = XM == 2;
-  constexpr int BWE = XM >= 3 && XM <= 5 ? XM - 2 : 0;   // 3, 4, 5: the SwiGLU, ReLU, GELU backward epilogue
-  constexpr bool STASH = XM == 6;             // the activation output and the fp32 pre-activations
+  // XM 7 and up: mode XM - 7 with B read from rows of K (TB): B[n][k] is
+  // element (k, n) of a [K, N] matrix (a weight used transposed), each stage
+  // a 64 x 256 image of K rows, read into MFMA operands by transposing LDS
+  // reads.  Plain (7) and the activation backward (10-12) only.
+  constexpr bool TB = XM >= 7;
+  constexpr int XB = TB ? XM - 7 : XM;
+  constexpr bool PRE = XB == 1 || XB == 2;
+  constexpr bool WG = XB == 2;
+  constexpr int BWE = XB >= 3 && XB <= 5 ? XB - 2 : 0;   // 3, 4, 5: the SwiGLU, ReLU, GELU backward epilogue
+  constexpr bool STASH = XB == 6;             // the activation output and the fp32 pre-activations
+  static_assert(!TB || (EPI == EPI_PLAIN && !FP8 && (XB == 0 || BWE != 0)), "transposed B: plain B rows only");
   constexpr int BM = 256;
   constexpr int R = 2;                  // split parts are whole stage pairs
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
@@ -862,9 +874,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     const long lda = WG ? p.lda : K;
     const char* a_sb = uniform_ptr(reinterpret_cast<const char*>(
         gat ? p.A : p.A + static_cast<size_t>(p.a_shared ? row0 - seg0 : row0) * lda + kb));
-    uint32_t a_vo[LDA];
+    // (transposed B: no gather; the offsets are formed at each issue from the
+    // lane's first row, which keeps seven registers free for the transposing
+    // reads' addresses)
+    uint32_t a_vo[TB ? 1 : LDA];
 #pragma unroll
-    for (int i = 0; i < LDA; ++i) {
+    for (int i = 0; i < (TB ? 1 : LDA); ++i) {
       const int r = min(i * RPI + tid / CH, rows_valid - 1);
       const int src = gat ? min(max(p.gather[row0 + r], 0), p.a_rows - 1) : r;   // clamped: never outside A
       a_vo[i] = static_cast<uint32_t>((src * lda + cq * 8) * 2);
@@ -872,8 +887,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     const int cqb = (tid & (CHB - 1)) ^ ((tid >> 4) & (CHB - 1));
     const char* b_sb[LDB];
     uint32_t b_vo[LDB];
+    if constexpr (TB) {
+      // slot i * 256 + tid of a stage's image: K row i * 8 + tid / 32 (of 64),
+      // stored chunk tid % 32 holding the row's global chunk (tid % 32) ^
+      // tb_swz(row) of the n-tile's 256 columns (clamped into the matrix: the
+      // columns past N feed discarded outputs)
+      // (K row i * 8 + tid / 32 has the swizzle term of row tid / 32: one
+      // lane offset serves every i, the row step goes into the uniform base)
+      const int k = tid >> 5;
+      const int n = min(nt * BN + 8 * ((tid & 31) ^ tb_swz(k)), N - 8);
+      b_vo[0] = static_cast<uint32_t>((k * N + n) * 2);
+      b_sb[0] = nullptr;
+    }
 #pragma unroll
-    for (int i = 0; i < LDB; ++i) {
+    for (int i = 0; i < (TB ? 0 : LDB); ++i) {
       const int r = i * RPIB + tid / CHB;
       int n;
       const void* base = p.B1;
@@ -901,14 +928,51 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     // one DMA instruction: instruction q of operand A or B of stage st into
     // half-slot h
     auto issue_a = [&](int st, int h, int q) __attribute__((always_inline)) {
-      dma16(a_sb + (ks0 + st) * BK * 2, a_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+      if constexpr (TB) {
+        const uint32_t vo = static_cast<uint32_t>((min(q * RPI + tid / CH, rows_valid - 1) * lda + cq * 8) * 2);
+        dma16(a_sb + (ks0 + st) * BK * 2, vo, lds_addr(ring + h * HALF + q * 256) + wave_lds);
+      } else {
+        dma16(a_sb + (ks0 + st) * BK * 2, a_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+      }
     };
+    // transposed B: K row kg of expert e is at tb_lo + kg N 2 below tb_k1
+    // (B1) and at tb_hi + kg N 2 from there on (B3; the origin shifted back
+    // by tb_k1 rows), so a stage's base is one select and one multiply-add
+    const uintptr_t tb_lo = TB ? reinterpret_cast<uintptr_t>(p.B1) + static_cast<uintptr_t>(e) * p.tb_k1 * N * 2 : 0;
+    const uintptr_t tb_hi = TB ? reinterpret_cast<uintptr_t>(p.B3) +
+                                     (static_cast<uintptr_t>(e) * (K - p.tb_k1) - p.tb_k1) * N * 2
+                               : 0;
     auto issue_b = [&](int st, int h, int q) __attribute__((always_inline)) {
-      dma16(b_sb[q] + (ks0 + st) * BK * EB, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+      if constexpr (TB) {
+        const int kg = (ks0 + st) * BK;
+        const uintptr_t base = (kg < p.tb_k1 ? tb_lo : tb_hi) + static_cast<uintptr_t>(kg + 8 * q) * N * 2;
+        dma16(reinterpret_cast<const char*>(base), b_vo[0], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+      } else {
+        dma16(b_sb[q] + (ks0 + st) * BK * EB, b_vo[q], lds_addr(ring + h * HALF + q * 256) + wave_lds);
+      }
     };
+    // transposed B: the 16-lane groups of a transposing read hand lane i
+    // element i % 4 of the 8 bytes that lane 4 q + i / 4 of the group
+    // addressed (q = 0..3).  Lane (fr, fc) needs K rows 16 ks + 8 fc + 0..7
+    // of column wn WN + 32 r + fr, so lane j of a group addresses K row
+    // 16 ks + 8 fc + 4 h + j / 4, columns 4 (j % 4) + 0..3 of the group's 16
+    // (read h = 0, 1).  Byte offsets within a stage's image for k-step 0:
+    // With the swizzle on chunk bits 2-3 (fragment r's bits), fragment r
+    // sits at 64 (r ^ (k % 4)) bytes from the lane's fragment-0 chunk; read
+    // h adds 4 K rows (2 KB), k-step ks 16 (8 KB).
+    const int tb_q = (lane >> 2) & 3;                      // the lane's K row % 4
+    const int tb_base = (8 * fc + tb_q) * 512 + (((wn * WN + (fr & 16)) >> 3) << 4) + (lane & 2) * 8 + (lane & 1) * 8;
     auto read_one = [&](const uint4* SA, const uint4* SB, int ks, int r, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN])
         __attribute__((always_inline)) {
-      if (r < FN) {
+      if (r < FN && TB) {
+        // two transposing reads (h = 0, 1) at the lane's fixed offsets; the
+        // k-step adds 16 K rows (8 KB)
+        const char* sb = reinterpret_cast<const char*>(SB) + tb_base + ((r ^ tb_q) << 6) + ks * (16 * 512);
+        typedef short v4s_t __attribute__((ext_vector_type(4)));
+        const v4s_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(sb));
+        const v4s_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(sb + 4 * 512));
+        fb[r] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else if (r < FN) {
         uint4 v = SB[dma_swz<CH>(wn * WN + r * 32 + fr, 2 * ks + fc)];
         fb[r] = *reinterpret_cast<bf16x8_t*>(&v);
       } else {
@@ -1482,7 +1546,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
 
 template <int EPI, int BK, bool FP8, int XM>
 int launch_dma_pre(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
-  constexpr bool PRE = XM >= 1;          // (no split tail for any of the extra modes)
+  constexpr bool PRE = XM >= 1 && XM != 7;   // (no split tail for the extra modes but the transposed-B plain one)
   constexpr int HC = EPI == EPI_SWIGLU ? 128 : 256;
   const long n_tiles = (p.N + HC - 1) / HC;
   long blocks = n_tiles * m_tiles_max;
@@ -1596,6 +1660,30 @@ int launch_grouped_gemm_actbwd(int bwd_epi, const GemmParams& p, int m_tiles_max
   if (bwd_epi == BWD_EPI_SWIGLU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 3>(q, m_tiles_max, stream);
   if (bwd_epi == BWD_EPI_RELU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 4>(q, m_tiles_max, stream);
   if (bwd_epi == BWD_EPI_GELU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 5>(q, m_tiles_max, stream);
+  return MOE_ERR_UNSUPPORTED;
+}
+
+namespace {
+bool tb_ok(const GemmParams& p) {
+  static_assert(kDmaKMult == 128 && kDmaBK == 64 && kGemmBM == 256, "the shape check's constants");
+  return grouped_gemm_tb_shape_ok(p.K, p.N, p.tb_k1) && (p.tb_k1 == p.K || p.B3) && !p.gather && !p.s1 && !p.bias;
+}
+}  // namespace
+
+int launch_grouped_gemm_tb(const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  if (!tb_ok(p)) return MOE_ERR_UNSUPPORTED;
+  if (p.split_max > 1 && !p.partial) return MOE_ERR_UNSUPPORTED;
+  return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 7>(p, m_tiles_max, stream);
+}
+
+int launch_grouped_gemm_actbwd_tb(int bwd_epi, const GemmParams& p, int m_tiles_max, hipStream_t stream) {
+  if (!tb_ok(p) || p.ldo % 8 != 0 || !p.hin1 || !p.o1 || !p.o3 || (bwd_epi == BWD_EPI_SWIGLU && (!p.hin3 || !p.o2)))
+    return MOE_ERR_UNSUPPORTED;
+  GemmParams q = p;
+  q.split_max = 1;
+  if (bwd_epi == BWD_EPI_SWIGLU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 10>(q, m_tiles_max, stream);
+  if (bwd_epi == BWD_EPI_RELU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 11>(q, m_tiles_max, stream);
+  if (bwd_epi == BWD_EPI_GELU) return launch_dma_pre<EPI_PLAIN, kDmaBK, false, 12>(q, m_tiles_max, stream);
   return MOE_ERR_UNSUPPORTED;
 }
 

@@ -144,6 +144,10 @@ struct GemmParams {
   int n_cu;                  // compute units (one block of the DMA kernel each)
   int split_max;             // most K parts of a split tile (1: no split)
   const float* row_scale;    // fp8 activations: scale of each source row of A (or null)
+  // launch_grouped_gemm_tb and launch_grouped_gemm_actbwd_tb: B[n][k] is
+  // element (k, n) of the K x N matrix of expert e, rows k < tb_k1 in B1
+  // ([E, tb_k1, N]) and the rest in B3 ([E, K - tb_k1, N])
+  int tb_k1;
   float* pre1;               // pre-activation outputs (fp32 [*, N]; launch_grouped_gemm_pre and _stash):
   float* pre3;               //   gate (+ bias) and, for SwiGLU, up
   // launch_grouped_gemm_wgrad only: segment e takes K columns [128 kseg[e],
@@ -194,6 +198,17 @@ int launch_grouped_gemm_wgrad(const GemmParams& p, int m_tiles_max, hipStream_t 
 // for shapes the LDS-DMA kernel does not take.
 int launch_grouped_gemm_stash(int epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
 int launch_grouped_gemm_actbwd(int bwd_epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
+// The plain and the activation-backward products with B read from rows of
+// K (the weights as stored, used transposed; see tb_k1); MOE_ERR_UNSUPPORTED
+// for shapes the LDS-DMA kernel does not take.
+int launch_grouped_gemm_tb(const GemmParams& p, int m_tiles_max, hipStream_t stream);
+// Whether the transposed-B launches take a K x N product whose first k1 K
+// rows come from B1 (the shape part of their checks)
+inline bool grouped_gemm_tb_shape_ok(int K, int N, int k1) {
+  return K > 0 && K % 128 == 0 && N >= 8 && N % 8 == 0 && k1 > 0 && k1 % 64 == 0 && k1 <= K &&
+         static_cast<size_t>(256) * K * 2 < (size_t(1) << 31) && static_cast<size_t>(64) * N * 2 < (size_t(1) << 31);
+}
+int launch_grouped_gemm_actbwd_tb(int bwd_epi, const GemmParams& p, int m_tiles_max, hipStream_t stream);
 
 // Per-row e4m3 quantisation (quant.hip): scale[r] = max |x[r, :]| / 448 (1
 // for a zero row), q = e4m3(x / scale); rows_dev (device, or null) bounds the
