@@ -489,7 +489,7 @@ __device__ __forceinline__ SplitPlan split_plan(int V, int KT, int R, int n_cu, 
 // other wavefront uses.
 // RS: fp8 activations; rsl[r] (LDS) is the scale of the wavefront's row r,
 // applied with the column scale before the activation.
-template <int EPI, int FM, bool RS = false, bool PRE = false, int BWE = 0>
+template <int EPI, int FM, bool RS = false, bool PRE = false, int BWE = 0, bool NT = false>
 __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint16_t* st, const GemmParams& p, int e,
                                               int row0, int rows_valid, int col0, const float* rsl = nullptr) {
   constexpr int OC = EPI == EPI_SWIGLU ? 64 : 128;
@@ -607,7 +607,15 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
         const int pc = (c % (OC / 4)) * 4;
         if (rb + r < rows_valid && col0 + pc < N) {
           const float4 v = *reinterpret_cast<const float4*>(stf + r * PF + pc);
-          *reinterpret_cast<float4*>(dst + static_cast<size_t>(row0 + rb + r) * N + col0 + pc) = v;
+          float* o = dst + static_cast<size_t>(row0 + rb + r) * N + col0 + pc;
+          if constexpr (NT) {
+            // weight gradients: written once, read by no later kernel of the
+            // pass; streamed past the L2 that holds the operands
+            typedef float f4v_t __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(__builtin_bit_cast(f4v_t, v), reinterpret_cast<f4v_t*>(o));
+          } else {
+            *reinterpret_cast<float4*>(o) = v;
+          }
         }
       }
       // the next pass overwrites the block: every lane's reads come first
@@ -1298,7 +1306,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       wave_epilogue<EPI, FM, false, true>(acc, st, p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
       wave_epilogue<EPI, FM, false, false>(acc, st, p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
     } else {
-      wave_epilogue<EPI, FM, false, PRE, BWE>(acc, st, p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
+      wave_epilogue<EPI, FM, false, PRE, BWE, WG>(acc, st, p, e, row0 + wm * WM, rows_valid - wm * WM, col0);
     }
   };
   if constexpr (!FP8) {
