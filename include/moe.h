@@ -556,7 +556,8 @@ int moe_expert_ffn_grouped_backward_kept(int kind, const void* x_rows, int act_d
  * slices in fp64, in order).  The input gradient dz W_g is added by
  * moe_permute_backward.
  *   dz    [T, E] fp32 out;  dw_g [E, d] fp32 out;  db_g [E] fp32 out or NULL
- * E <= 256 (else MOE_ERR_UNSUPPORTED).  T == 0 writes zero dw_g and db_g.
+ * E <= 256 and T <= 65535 x 128 (else MOE_ERR_UNSUPPORTED).  T == 0 writes zero dw_g
+ * and db_g.
  */
 size_t moe_router_backward_workspace_size(int T, int d, int E);
 int moe_router_backward(const void* x, int x_dt, const float* logits, const int32_t* topk_idx,

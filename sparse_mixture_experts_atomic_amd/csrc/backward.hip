@@ -402,6 +402,7 @@ int moe_router_backward(const void* x, int x_dt, const float* logits, const int3
     return MOE_ERR_WORKSPACE;
   const int nb = (T + 15) / 16;
   const int ns = (T + kRwSlice - 1) / kRwSlice;
+  if (ns > 65535) return MOE_ERR_UNSUPPORTED;   // token slices of the weight gradient are grid rows
   float* colpart = static_cast<float*>(workspace);
   float* wpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           align_up(static_cast<size_t>(nb > 0 ? nb : 1) * E * sizeof(float), kWsAlign));
