@@ -278,3 +278,23 @@ def test_training_ffn_validation_before_launch():
     rec = lib.moe_expert_ffn_grouped_backward(L.FFN_SWIGLU, f, L.BF16, 64, 0, f, 4, 128, 128, 64, f, f, f, L.BF16,
                                               None, None, f, f, f, f, f, None, None, f, kept, None)
     assert rec == L.ERR_WORKSPACE
+
+
+def test_router_backward_validation_before_launch():
+    lib = L.lib()
+    f = 1 << 20    # never dereferenced: validation fails first
+
+    def call(T=64, d=16, E=4, k=2, mode=L.GATE_RENORM, x=f, ws=f, wsb=None):
+        if wsb is None:
+            wsb = lib.moe_router_backward_workspace_size(T, d, E)
+        return lib.moe_router_backward(x, L.BF16, f, f, f, f, f, T, d, E, k, mode, 0.01, 1.0, f, f, None, ws, wsb,
+                                       None)
+    assert call(k=5) == L.ERR_INVALID_ARG                 # k > E
+    assert call(mode=7) == L.ERR_INVALID_ARG
+    assert call(x=None) == L.ERR_INVALID_ARG
+    assert call(x=f + 4) == L.ERR_INVALID_ARG
+    assert call(E=257, k=2) == L.ERR_UNSUPPORTED
+    assert call(ws=None) == L.ERR_WORKSPACE
+    assert call(wsb=16) == L.ERR_WORKSPACE
+    # token slices of 128 beyond the grid's 65535 rows
+    assert call(T=65536 * 128) == L.ERR_UNSUPPORTED
