@@ -221,8 +221,14 @@ int moe_expert_ffn_fp8(int kind, const void* xq, const float* x_scale, int n_src
   uint8_t* Hq = two ? reinterpret_cast<uint8_t*>(ws + align_up(ff * 2, kWsAlign)) : nullptr;
   float* sh = two ? reinterpret_cast<float*>(ws + align_up(ff * 2, kWsAlign) + align_up(ff, kWsAlign)) : nullptr;
 
-  int st = launch_tile_map(offsets, E, kGemmBM, ts, stream);
-  if (st != MOE_OK) return st;
+  // the m-tile prefix: formed by the first GEMM launch itself for a few
+  // segments, else by a launch of its own
+  const bool ts_in_gemm = E <= kGemmTsBuildMaxE;
+  int st = MOE_OK;
+  if (!ts_in_gemm) {
+    st = launch_tile_map(offsets, E, kGemmBM, ts, stream);
+    if (st != MOE_OK) return st;
+  }
   const int mtm = m_tiles_max(max_rows, E);
   GemmParams p1{};
   p1.A = static_cast<const uint16_t*>(xq);
@@ -231,6 +237,7 @@ int moe_expert_ffn_fp8(int kind, const void* xq, const float* x_scale, int n_src
   p1.a_rows = n_src;
   p1.offsets = offsets;
   p1.ts = ts;
+  p1.ts_build = ts_in_gemm ? ts : nullptr;
   p1.E = E;
   p1.B1 = w1;
   p1.B3 = w3;
@@ -343,8 +350,14 @@ int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode
                                  Y, max_rows, stream);
   }
 
-  int st = launch_tile_map(offsets, E, kGemmBM, ts, stream);
-  if (st != MOE_OK) return st;
+  // the m-tile prefix: formed by the first GEMM launch itself for a few
+  // segments, else by a launch of its own
+  const bool ts_in_gemm = E <= kGemmTsBuildMaxE;
+  int st = MOE_OK;
+  if (!ts_in_gemm) {
+    st = launch_tile_map(offsets, E, kGemmBM, ts, stream);
+    if (st != MOE_OK) return st;
+  }
   const int mtm = m_tiles_max(max_rows, E);
 
   GemmParams p1{};
@@ -354,6 +367,7 @@ int ffn_run(int kind, const void* x_rows, int act_dt, int max_rows, int row_mode
   p1.a_rows = n_src;
   p1.offsets = offsets;
   p1.ts = ts;
+  p1.ts_build = ts_in_gemm ? ts : nullptr;
   p1.E = E;
   p1.B1 = w1;
   p1.B3 = w3;

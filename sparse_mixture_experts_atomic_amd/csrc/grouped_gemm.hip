@@ -73,6 +73,37 @@ __device__ __forceinline__ int find_segment(const int32_t* ts, int E, int m) {
   return lo;
 }
 
+// The m-tile prefix of the segments (tiles of kGemmBM rows) for this block:
+// read from p.ts, or, when p.ts_build is set (E <= kGemmTsBuildMaxE), formed
+// from the offsets by the first wavefront (a lane per segment, a wavefront
+// scan) into lts (E + 1 ints of LDS) and also stored by block 0 to
+// p.ts_build for the launches that follow.  Every thread of the block calls
+// it (it ends with a block barrier when it builds).
+__device__ __forceinline__ const int32_t* block_tile_prefix(const GemmParams& p, int32_t* lts) {
+  if (!p.ts_build) return p.ts;
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    int v = 0;
+    if (l < p.E) {
+      const int len = p.offsets[l + 1] - p.offsets[l];
+      v = len > 0 ? (len + kGemmBM - 1) / kGemmBM : 0;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (l >= o) v += u;
+    }
+    if (l < p.E) lts[l + 1] = v;
+    if (l == 0) lts[0] = 0;
+    if (blockIdx.x == 0) {
+      if (l < p.E) p.ts_build[l + 1] = v;
+      if (l == 0) p.ts_build[0] = 0;
+    }
+  }
+  __syncthreads();
+  return lts;
+}
+
 // Register-staged kernel for shapes the DMA kernel does not take (K not a
 // multiple of 128): block tile BM x BN (weight rows), 4 wavefronts in a 2x2
 // grid, each owning a (BM/2) x (BN/2) accumulator tile; global -> registers
@@ -685,19 +716,32 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
 struct TileCoord {
   int e, nt, row0, rows_valid, seg0;
 };
-__device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, int L, int m_total, int n_tiles, int BM) {
+__device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, const int32_t* ts, int L, int m_total,
+                                                int n_tiles, int BM) {
   const int grp = L / (m_total * kNGroup);
   const int gs = min(kNGroup, n_tiles - grp * kNGroup);
   const int Lr = L - grp * m_total * kNGroup;
   TileCoord t;
-  t.e = find_segment(p.ts, p.E, Lr / gs);
-  const int me = p.ts[t.e + 1] - p.ts[t.e];
-  const int r = Lr - p.ts[t.e] * gs;
-  const int mt_g = p.ts[t.e] + r % me;
+  t.e = find_segment(ts, p.E, Lr / gs);
+  const int me = ts[t.e + 1] - ts[t.e];
+  const int r = Lr - ts[t.e] * gs;
+  const int mt_g = ts[t.e] + r % me;
   t.nt = grp * kNGroup + r / me;
   t.seg0 = p.offsets[t.e];
-  t.row0 = t.seg0 + (mt_g - p.ts[t.e]) * BM;
+  t.row0 = t.seg0 + (mt_g - ts[t.e]) * BM;
   t.rows_valid = min(BM, p.offsets[t.e + 1] - t.row0);
+  return t;
+}
+
+// The coordinates are the same in every lane (they depend on the block and
+// the prefix only): moved to scalar registers, so that the addresses formed
+// from them stay scalar whether the prefix was read from LDS or global memory.
+__device__ __forceinline__ TileCoord uniform_tile(TileCoord t) {
+  t.e = __builtin_amdgcn_readfirstlane(t.e);
+  t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+  t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+  t.rows_valid = __builtin_amdgcn_readfirstlane(t.rows_valid);
+  t.seg0 = __builtin_amdgcn_readfirstlane(t.seg0);
   return t;
 }
 
@@ -718,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
   const int r = blockIdx.x >> 2;
   const int w = blockIdx.x & 3;
   if (r >= sp.rem) return;
-  const TileCoord t = tile_coord(p, sp.full + r, m_total, n_tiles, 256);
+  const TileCoord t = tile_coord(p, p.ts, sp.full + r, m_total, n_tiles, 256);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int fi = tid >> 6;
@@ -820,7 +864,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
   __shared__ uint4 ring[5 * 256 * (kDmaBK / 8)];
 
   const int n_tiles = (p.N + HC - 1) / HC;
-  const int m_total = p.ts[p.E];
+  // the m-tile prefix (formed here: in the last half-slot of the ring, which
+  // no DMA fills before the barrier after the tile coordinates)
+  const int32_t* ts = block_tile_prefix(p, reinterpret_cast<int32_t*>(ring + 4 * 256 * (kDmaBK / 8)));
+  const int m_total = __builtin_amdgcn_readfirstlane(ts[p.E]);
   const int V = m_total * n_tiles;
   const int KT = p.K / BK;              // even
   const SplitPlan sp = split_plan(V, KT, R, p.n_cu, p.split_max);
@@ -836,7 +883,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     L = sp.full + unit / sp.S;
   }
   const int ks0 = unit < 0 ? 0 : (unit % sp.S) * sp.chunk;   // first stage of this block
-  const TileCoord tc = tile_coord(p, L, m_total, n_tiles, BM);
+  const TileCoord tc = uniform_tile(tile_coord(p, ts, L, m_total, n_tiles, BM));
+  if (p.ts_build) __syncthreads();      // every lane has read the prefix before the ring fills
   // weight gradients: the segment's own K range (a multiple of 128, may be 0)
   // (kseg counts units of 128 columns)
   const int kb = WG ? p.kseg[tc.e] * kDmaKMult : 0;
@@ -1366,14 +1414,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
   __shared__ uint4 ring[5 * HALF];           // 160 KB
 
   const int n_tiles = (p.N + HC - 1) / HC;
-  const int m_total = p.ts[p.E];
+  // the m-tile prefix (formed here: in the last half-slot of the ring, which
+  // no DMA fills before the barrier after the tile coordinates)
+  const int32_t* ts = block_tile_prefix(p, reinterpret_cast<int32_t*>(ring + 4 * HALF));
+  const int m_total = __builtin_amdgcn_readfirstlane(ts[p.E]);
   const int V = m_total * n_tiles;
   const int per = (V + kXcds - 1) / kXcds;
   const int b = blockIdx.x;
   if (b / kXcds >= per) return;
   const int L = (b % kXcds) * per + b / kXcds;   // blocks of one XCD take a contiguous range
   if (L >= V) return;
-  const TileCoord tc = tile_coord(p, L, m_total, n_tiles, 256);
+  const TileCoord tc = uniform_tile(tile_coord(p, ts, L, m_total, n_tiles, 256));
+  if (p.ts_build) __syncthreads();      // every lane has read the prefix before the ring fills
   const int e = tc.e, nt = tc.nt, row0 = tc.row0, rows_valid = tc.rows_valid, seg0 = tc.seg0;
   const int K = p.K, N = p.N;
   const int KT = K / kF8BK;
@@ -1727,6 +1779,14 @@ int launch_grouped_gemm(int epi, bool fp8, const GemmParams& p, int max_rows, in
     if (epi == EPI_RELU) return launch_dma<EPI_RELU, kDmaBK, false>(p, m_tiles_max, stream);
     if (epi == EPI_GELU) return launch_dma<EPI_GELU, kDmaBK, false>(p, m_tiles_max, stream);
     return launch_dma<EPI_PLAIN, kDmaBK, false>(p, m_tiles_max, stream);
+  }
+  if (p.ts_build) {
+    // the register-staged kernel reads a prefix built before it
+    const int st = launch_tile_map(p.offsets, p.E, kGemmBM, p.ts_build, stream);
+    if (st != MOE_OK) return st;
+    GemmParams q = p;
+    q.ts_build = nullptr;
+    return launch_epi<kGemmBM, 128, 1>(epi, fp8, q, m_tiles_max, stream);
   }
   return launch_epi<kGemmBM, 128, 1>(epi, fp8, p, m_tiles_max, stream);
 }

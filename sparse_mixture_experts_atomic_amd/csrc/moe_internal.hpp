@@ -131,6 +131,10 @@ struct GemmParams {
   int a_rows;                // rows of A when gathering (bounds the DMA offsets)
   const int32_t* offsets;    // [E+1] segment bounds
   const int32_t* ts;         // [E+1] m-tile prefix (tiles of kGemmBM rows)
+  // E <= 64 only: the first launch of a call forms the prefix from offsets
+  // in each block, and block 0 leaves it here (= ts) for the launches after
+  // it (null: ts is already built)
+  int32_t* ts_build;
   int E;
   const void* B1;            // [E, N, K] bf16 or e4m3 codes
   const void* B3;            // SwiGLU up projection [E, N, K]
@@ -165,6 +169,10 @@ struct GemmParams {
   uint16_t* o3;
   long ldo;
 };
+
+// Most segments for which a grouped GEMM launch forms the m-tile prefix itself
+// (one lane per segment) instead of a separate tile-map launch before it.
+constexpr int kGemmTsBuildMaxE = 64;
 
 // Bytes of the split-tail partial buffer for n_cu compute units.
 inline size_t gemm_partial_bytes(int n_cu) { return static_cast<size_t>(n_cu > 0 ? n_cu : 0) * 256 * 256 * sizeof(float); }
