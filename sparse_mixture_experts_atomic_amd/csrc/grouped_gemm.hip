@@ -713,9 +713,16 @@ __device__ __forceinline__ void wave_epilogue(const f32x16_t (&acc)[FM][4], uint
 // Within a group of gs n-tiles the order is segment, then n-tile, then the
 // segment's m-tiles, so the m-tiles that share a weight tile are neighbours
 // in L and run at the same time on one XCD whatever the segment lengths.
+// MC > 0: a segment's m-tiles are taken in chunks of MC (segment, chunk,
+// n-tile, m-tile of the chunk), so that a round of 32 tiles covers a few
+// m-tiles by several n-tiles even when a segment has dozens of m-tiles (the
+// weight gradients: 56 m-tiles of 256 output rows per expert at d_ff =
+// 14336, where m fastest put 32 m-tiles of one n-tile in a round: 33
+// operand streams for 32 tiles instead of 12).
 struct TileCoord {
   int e, nt, row0, rows_valid, seg0;
 };
+template <int MC = 0>
 __device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, const int32_t* ts, int L, int m_total,
                                                 int n_tiles, int BM) {
   const int grp = L / (m_total * kNGroup);
@@ -724,9 +731,16 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmParams& p, const int32
   TileCoord t;
   t.e = find_segment(ts, p.E, Lr / gs);
   const int me = ts[t.e + 1] - ts[t.e];
-  const int r = Lr - ts[t.e] * gs;
-  const int mt_g = ts[t.e] + r % me;
-  t.nt = grp * kNGroup + r / me;
+  int r = Lr - ts[t.e] * gs;
+  int m0 = 0, cs = me;
+  if constexpr (MC > 0) {
+    const int c = r / (MC * gs);
+    m0 = c * MC;
+    cs = min(MC, me - m0);
+    r -= c * MC * gs;
+  }
+  const int mt_g = ts[t.e] + m0 + r % cs;
+  t.nt = grp * kNGroup + r / cs;
   t.seg0 = p.offsets[t.e];
   t.row0 = t.seg0 + (mt_g - ts[t.e]) * BM;
   t.rows_valid = min(BM, p.offsets[t.e + 1] - t.row0);
@@ -883,7 +897,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
     L = sp.full + unit / sp.S;
   }
   const int ks0 = unit < 0 ? 0 : (unit % sp.S) * sp.chunk;   // first stage of this block
-  const TileCoord tc = uniform_tile(tile_coord(p, ts, L, m_total, n_tiles, BM));
+  const TileCoord tc = uniform_tile(tile_coord<WG ? 4 : 0>(p, ts, L, m_total, n_tiles, BM));
   if (p.ts_build) __syncthreads();      // every lane has read the prefix before the ring fills
   // weight gradients: the segment's own K range (a multiple of 128, may be 0)
   // (kseg counts units of 128 columns)
