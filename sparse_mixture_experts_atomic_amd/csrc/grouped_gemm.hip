@@ -1082,8 +1082,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(GemmParam
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    // MFMA q of a k-step: fragment row i = q / FN, columns in snake order
+    // (ascending in even rows, descending in odd ones), so that each MFMA
+    // shares an operand with the one before it (A along a row, B where two
+    // rows meet).  Each accumulator still takes its k-steps in order, so the
+    // results are bit for bit those of any other order; the operands that do
+    // not change between MFMAs cost less power, and at the power limit that
+    // is time (the Mixtral-shaped FFN 0.5% faster).
     auto mma_one = [&](int q, const bf16x8_t (&fa)[FM], const bf16x8_t (&fb)[FN]) __attribute__((always_inline)) {
-      acc[q / FN][q % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / FN], fb[q % FN], acc[q / FN][q % FN], 0, 0, 0);
+      const int i = q / FN;
+      const int j = (i & 1) ? FN - 1 - q % FN : q % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
 
     bf16x8_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
@@ -1503,8 +1512,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_f8_kernel(GemmParams
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   // a wavefront whose rows all lie past the segment's end skips its MFMAs
   const bool wave_rows = wm * 128 < rows_valid;
+  // columns in snake order, as in the bf16 kernel
   auto mma = [&](const i32x8_t (&f)[8], int q) __attribute__((always_inline)) {
-    const int i = q >> 2, j = q & 3;
+    const int i = q >> 2, j = (i & 1) ? 3 - (q & 3) : q & 3;
     if (wave_rows)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[i], f[4 + j], acc[i][j], 0, 0, 0, 127, 0, 127);
   };
